@@ -1,0 +1,273 @@
+/*
+ * lit.h - C ABI of the lightning-indexer decode step for MI355X (gfx950).
+ *
+ * One decode step of a Compressed Sparse Attention (CSA) layer, as the pages
+ * below describe it, split into the calls a caller strings together:
+ *
+ *   lit_idx_score        score every compressed entry with the 128-dim index keys
+ *   lit_topk_select      keep the k best entries (lower index wins ties)
+ *   lit_sparse_attn_decode  MQA attention over the kept rows plus the SWA window
+ *   lit_golden_topk      dense "golden" attention and its top-k (measurement)
+ *   lit_golden_topp_vote top-p 0.6 per layer, then a cross-layer vote (labels)
+ *   lit_recall           set overlap of two selections
+ *   lit_lsa_gate         sigmoid chunk gate of FlashMemory/LSA (candidate set)
+ *
+ * Pages cited (title, then the part of the page):
+ *   [ARCH]  ai-muninn.com, "284B 塞得進 128GB、長 context 還跑得動:DeepSeek-V4-Flash
+ *           打的是 KV cache,不是參數量" (series Part 6, the V4-Flash architecture post).
+ *           Sections "(A) 壓縮你存的" (storage, layer table), "(B) 只讀你需要的"
+ *           (lightning indexer), "為什麼你沒辦法靠量化 KV 再省記憶體" (KV precision).
+ *   [FMEN]  ai-muninn.com, "FlashMemory can't improve DeepSeek-V4-Flash's own lightning
+ *           indexer - I retrained it on my exact Q2 and it still lost" (series Part 7,
+ *           English). Sections "The setup", "Act 1", "Act 3".
+ *   [LSA]   zhichai.net, "FlashMemory-DeepSeek-V4 深度解读：用预言家替代记忆海绵".
+ *           Sections 2.2 (the gate), 3.2 (labels), 4.1 (gate layers), and the
+ *           gated-score equation quoted in the second reply.
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a DEVICE pointer unless its comment says "host".
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Arguments are validated on the host before anything is enqueued. On a
+ *     validation failure the call returns a non-zero lit_status, enqueues
+ *     nothing, and lit_last_error() describes the failure. The library never
+ *     exits or aborts the process.
+ *   - A failed kernel launch returns LIT_ERR_LAUNCH. Faults inside a kernel
+ *     surface at the caller's next synchronisation of `stream`.
+ *   - The caller owns every buffer. The library allocates no device memory;
+ *     scratch space comes from a caller-provided workspace whose size is given
+ *     by the matching *_workspace_bytes() query. Workspace contents need no
+ *     initialisation and are not meaningful after a call.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Calls that overlap on one stream are ordered; calls on different streams
+ *     that share an output or a workspace race.
+ *   - Indices are int32 (N < 2^31). Dense arrays are C-contiguous, in the
+ *     shapes given, with no padding between rows.
+ */
+#ifndef LIT_H
+#define LIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIT_ABI_VERSION 1
+
+/* Width of an index key ([ARCH] (B): each compressed entry has its own 128-dim key). */
+#define LIT_IDX_DIM 128
+/* Width of a compressed latent row ([ARCH] (A): attn_comp_kv rows are 512 wide). */
+#define LIT_KV_DIM 512
+/* FP8 rows ([ARCH] KV precision): the first 448 dims are E4M3 in groups of 64,
+ * the last 64 (RoPE) dims are BF16. */
+#define LIT_KV_FP8_DIMS 448
+#define LIT_KV_ROPE_DIMS 64
+#define LIT_KV_FP8_GROUP 64
+#define LIT_KV_SCALE_STRIDE 8 /* bytes per row of E8M0 scales: 7 used, 1 pad */
+/* Entries per chunk of the key-norm side output of lit_idx_score. */
+#define LIT_KNORM_CHUNK 256
+/* Limits. */
+#define LIT_MAX_IDX_HEADS 64
+#define LIT_MAX_Q_HEADS 64
+#define LIT_MAX_WINDOW 8192
+
+typedef enum {
+  LIT_OK = 0,
+  LIT_ERR_NULL = 1,      /* a required pointer is NULL */
+  LIT_ERR_SHAPE = 2,     /* a size is out of range or sizes disagree */
+  LIT_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  LIT_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination */
+  LIT_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+  LIT_ERR_LAUNCH = 6     /* the HIP runtime refused a launch or query */
+} lit_status;
+
+typedef enum {
+  LIT_F32 = 0,
+  LIT_BF16 = 1,
+  /* [ARCH] KV precision: dims 0..447 are OCP E4M3FN bytes, one E8M0 power-of-two
+   * scale byte per 64-dim group (value 2^(byte-127)); dims 448..511 are BF16. */
+  LIT_FP8E4M3_G64_ROPE_BF16 = 2
+} lit_dtype;
+
+/* Inputs of the lightning indexer ([ARCH] (B); score form from [LSA] reply
+ * equation without the sigmoid, "native ReLU-MQA"). Host struct, read during
+ * the call only.
+ *   q : [B][H][128] index queries, dtype `dtype` (LIT_F32 or LIT_BF16), 16-B aligned
+ *   w : [B][H] fp32 head weights
+ *   k : [B][N][128] index keys (index_comp_kv), same dtype as q, 16-B aligned */
+typedef struct {
+  const void* q;
+  const float* w;
+  const void* k;
+  lit_dtype dtype;
+  int32_t H; /* 1..64 */
+} lit_idx_in;
+
+/* Compressed latent KV (attn_comp_kv, [ARCH] (A)); used as both K and V by the
+ * MQA attention. Host struct, read during the call only.
+ *   LIT_F32 / LIT_BF16: data = [B][N][512], 16-B aligned; rope, scale unused.
+ *   LIT_FP8E4M3_G64_ROPE_BF16: data = [B][N][448] E4M3 bytes (16-B aligned),
+ *     rope = [B][N][64] BF16 (16-B aligned), scale = [B][N][8] E8M0 bytes (byte 7 unused). */
+typedef struct {
+  lit_dtype dtype;
+  int32_t n_rows; /* N */
+  const void* data;
+  const void* rope;
+  const uint8_t* scale;
+} lit_kv;
+
+/* Inputs of one FlashMemory/LSA gate layer ([LSA] 2.2, 4.1; projections named in
+ * [FMEN] "Act 2": wq_a, wq_b, weights_proj). Host struct.
+ *   h      : [B][d_model] fp32 hidden state at this layer
+ *   wq_a   : [rank][d_model] BF16   (u = wq_a . h)
+ *   wq_b   : [H*128][rank]  BF16    (q = wq_b . u, read as [H][128])
+ *   w_proj : [H][d_model]   BF16    (w = w_proj . h, signed head weights)
+ *   k      : [B][N][128]    BF16    frozen index keys of this layer, 16-B aligned */
+typedef struct {
+  const float* h;
+  const void* wq_a;
+  const void* wq_b;
+  const void* w_proj;
+  const void* k;
+} lit_gate_layer;
+
+int lit_abi_version(void);
+/* Thread-local text describing the last failure on the calling thread (host string). */
+const char* lit_last_error(void);
+
+/* ---- a1: indexer scores ------------------------------------------------------
+ * [ARCH] (B): a light indexer scores every compressed entry with its own 128-dim
+ * key. For each sequence b and entry n:
+ *     scores[b][n] = sum_h w[b][h] * max(0, sum_d q[b][h][d] * k[b][n][d])
+ * computed with fp32 accumulation (bf16 products are exact in fp32).
+ * allowed : [B][N] u8 or NULL. Where allowed[b][n] == 0 the score is -inf
+ *           (the candidate set restricted by the gate, [FMEN] "The setup").
+ * scores  : [B][N] fp32 output.
+ * kmax    : [B][ceil(N/LIT_KNORM_CHUNK)] fp32 output or NULL: for each chunk of
+ *           LIT_KNORM_CHUNK consecutive entries, an upper bound of the largest
+ *           Euclidean norm of a key in it. lit_topk_select needs it for exact
+ *           selection. */
+lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
+                         float* scores, float* kmax, void* stream);
+
+/* ---- a2: top-k selection -----------------------------------------------------
+ * [ARCH] (B): keep the n_indexer_top_k (512; 1024 for the Pro variant) best
+ * entries and turn them into a comp_allowed mask and a list of row ids.
+ * Order: score descending, then index ascending (the lower index wins a tie).
+ * Entries whose score is -inf or NaN are never selected. count[b] =
+ * min(k, number of selectable entries).
+ * exact == NULL : the order is that of the fp32 `scores` as given.
+ * exact != NULL : the order is that of the exact scores, i.e. the definition of
+ *   lit_idx_score evaluated in fp64 in canonical order (d ascending within a head,
+ *   then h ascending, each w*relu product rounded before it is added). `exact`
+ *   must be the same inputs that produced `scores`, and `kmax` its side output;
+ *   entries whose fp32 score lies within a proven error bound of the k-th score
+ *   are rescored in fp64 so the selection equals the fp64 one bit for bit.
+ * ids   : [B][k] int32 output, selected indices ascending, tail filled with -1.
+ * count : [B] int32 output.
+ * mask  : [B][N] u8 output (1 = selected) or NULL.
+ * Workspace: lit_topk_workspace_bytes(B, N, k) bytes. */
+size_t lit_topk_workspace_bytes(int32_t B, int32_t N, int32_t k);
+lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k,
+                           const lit_idx_in* exact, const float* kmax,
+                           int32_t* ids, int32_t* count, uint8_t* mask,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- a3/a4/a5: sparse MQA attention decode ------------------------------------
+ * [ARCH] (B): attention reads only the selected compressed rows plus the
+ * sliding window of the last `window` entries; [ARCH] (A): rows are the 512-wide
+ * attn_comp_kv, shared by all query heads as key and value (MQA); HCA layers
+ * read every row (ids == NULL). For each sequence b and head h:
+ *     R      = { ids[b][0..count[b]) } U { N-window .. N-1 }   (each row once)
+ *     x_r    = scale * (q[b][h] . kv[b][r])
+ *     out[b][h] = sum_{r in R} softmax(x)_r * kv[b][r]
+ *     lse[b][h] = log(sum_{r in R} exp(x_r))            (natural log)
+ * q      : [B][Hq][512], dtype q_dtype (LIT_F32 with LIT_F32 kv, else LIT_BF16)
+ * kv     : rows, see lit_kv. FP8 rows are dequantised exactly (E4M3 value times
+ *          2^(scale-127)) before use ([ARCH] KV precision).
+ * ids    : [B][k_cap] ascending ids (tail -1) with count[b] valid, or NULL for
+ *          every row (then count and window are ignored).
+ * window : 0..LIT_MAX_WINDOW, clamped to N.
+ * out    : [B][Hq][512] fp32 output; lse: [B][Hq] fp32 output or NULL.
+ * An empty R (count 0 and window 0) gives out = 0 and lse = -inf.
+ * Workspace: lit_attn_workspace_bytes(B, Hq, N) bytes. */
+size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N);
+lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,
+                                  int32_t B, const int32_t* ids, const int32_t* count,
+                                  int32_t k_cap, int32_t window, float scale,
+                                  float* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* ---- a6: dense golden top-k ---------------------------------------------------
+ * [FMEN] "Act 3": golden = what the model attends to under an unmasked softmax
+ * over all chunks. In fp64, for each sequence b:
+ *     P[h][n] = softmax_n(scale * (q[b][h] . kv[b][n]))     over all N rows
+ *     pbar[n] = (sum_h P[h][n]) / Hq                          (head average)
+ *     G       = top-k of pbar, pbar descending then index ascending.
+ * ids   : [B][k] ascending (tail -1); count: [B]; mask: [B][N] u8 or NULL;
+ * pbar  : [B][N] fp64 output or NULL.
+ * Workspace: lit_golden_workspace_bytes(B, Hq, N, k) bytes. */
+size_t lit_golden_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t k);
+lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,
+                           int32_t B, float scale, int32_t k,
+                           int32_t* ids, int32_t* count, uint8_t* mask, double* pbar,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ---- a9: top-p per layer, then a cross-layer vote -----------------------------
+ * [LSA] 3.2: per layer, turn the scores into probabilities with a softmax, keep
+ * the smallest set whose cumulative probability reaches top_p (0.6), then mark
+ * an entry golden when at least min_votes (3) of the L layers kept it.
+ * For every layer l and sequence b (fp64):
+ *     p    = x[l][b]            if is_logits == 0 (x already holds probabilities)
+ *          = softmax_n(x[l][b]) if is_logits != 0
+ *     order entries by p descending, index ascending; T = the shortest prefix
+ *     whose running sum (added in that order) is >= top_p.
+ *     votes[b][n] = number of layers whose T holds n;  gold = votes >= min_votes.
+ * x     : [L][B][N] fp64
+ * gold  : [B][N] u8 output; gold_count: [B] int32 output;
+ * votes : [B][N] int32 output or NULL.
+ * Workspace: lit_topp_workspace_bytes(L, B, N) bytes. */
+size_t lit_topp_workspace_bytes(int32_t L, int32_t B, int32_t N);
+lit_status lit_golden_topp_vote(const double* x, int32_t is_logits, int32_t L, int32_t B,
+                                int32_t N, double top_p, int32_t min_votes,
+                                uint8_t* gold, int32_t* gold_count, int32_t* votes,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---- exact indexer scores (label pipeline helper) ------------------------------
+ * The lit_idx_score definition evaluated in fp64 in canonical order for every
+ * entry (the order lit_topk_select's exact mode matches). Slow; for labels.
+ * scores64 : [B][N] fp64 output (-inf where allowed[b][n] == 0). */
+lit_status lit_idx_score_exact(const lit_idx_in* in, const uint8_t* allowed, int32_t B,
+                               int32_t N, double* scores64, void* stream);
+
+/* ---- a7: recall -----------------------------------------------------------------
+ * [FMEN] "Act 1", "Act 3": overlap of two selections over the same entries.
+ * inter[b] = #{n : a[b][n] != 0 and m[b][n] != 0}; count_a, count_b the set
+ * sizes (any of the three outputs may be NULL). Recall = inter / |golden|. */
+lit_status lit_recall(const uint8_t* a, const uint8_t* m, int32_t B, int32_t N,
+                      int32_t* inter, int32_t* count_a, int32_t* count_b, void* stream);
+
+/* ---- a8: FlashMemory / LSA sigmoid chunk gate ------------------------------------
+ * [LSA] 2.2: every tau = 64 decode steps a memory indexer scores each compressed
+ * chunk with a sigmoid and keeps those at or above the threshold; [LSA] 4.1: the
+ * indexers sit at layers 10, 12 and 20 and their kept sets are OR-ed; the
+ * score form is the second reply's gated equation. For each layer l, sequence b:
+ *     u = wq_a . h ;  q = wq_b . u  (as [H][128]) ;  w = w_proj . h     (fp64)
+ *     z[n] = sum_h w[h] * max(0, q[h] . k[b][n])
+ *     keep[n] = sigmoid(z[n]) >= threshold  <=>  z[n] >= log(threshold/(1-threshold))
+ * gate[b][n] = OR over layers of keep; gate_count[b] = number kept.
+ * The decision is exact: the fp64 value of z in canonical order (h, then d
+ * ascending; each product rounded before it is added) decides it.
+ * layers : host array of n_layers (1..8) structs; threshold in (0,1).
+ * Workspace: lit_gate_workspace_bytes(n_layers, B, H, rank, N) bytes. */
+size_t lit_gate_workspace_bytes(int32_t n_layers, int32_t B, int32_t H, int32_t rank, int32_t N);
+lit_status lit_lsa_gate(const lit_gate_layer* layers, int32_t n_layers, int32_t B, int32_t N,
+                        int32_t H, int32_t d_model, int32_t rank, double threshold,
+                        uint8_t* gate, int32_t* gate_count, void* ws, size_t ws_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIT_H */

@@ -1,0 +1,41 @@
+// capi.hip - library-wide entry points and the host-side error plumbing.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "lit_common.h"
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+namespace lit {
+
+lit_status fail(lit_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_last_error[0] = 0; }
+
+lit_status launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LIT_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return LIT_OK;
+}
+
+lit_status allow_lds(const void* kernel, size_t bytes, const char* what) {
+  if (bytes <= 65536) return LIT_OK;
+  hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess)
+    return fail(LIT_ERR_LAUNCH, "%s: cannot reserve %zu bytes of LDS: %s", what, bytes, hipGetErrorString(e));
+  return LIT_OK;
+}
+
+}  // namespace lit
+
+extern "C" int lit_abi_version(void) { return LIT_ABI_VERSION; }
+
+extern "C" const char* lit_last_error(void) { return g_last_error; }

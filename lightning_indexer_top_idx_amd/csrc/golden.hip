@@ -1,0 +1,393 @@
+// golden.hip - a6: dense "golden" attention top-k; a9: top-p per layer + vote.
+//
+// a6, ai-muninn.com, "FlashMemory can't improve DeepSeek-V4-Flash's own lightning indexer",
+// section "Act 3": the ground truth a selector is scored against is the dense
+// attention, an unmasked softmax over every chunk; its top-k is the golden set.
+// The head-averaged form (average the per-head probabilities) is how the tiny
+// workload states it. Everything is fp64: the logits are canonical sums (exact
+// products, d ascending), so they are bit-identical to a sequential CPU sum; the
+// softmax denominators are parallel tree sums.
+//
+// a9, zhichai.net, "FlashMemory-DeepSeek-V4 深度解读", section 3.2: labels come from a
+// softmax of each layer's indexer logits, a top-p cut at p = 0.6 (the smallest
+// set of entries whose cumulative probability reaches p), and a vote that keeps
+// entries chosen by at least 3 of the 21 CSA layers. The running sum is added
+// sequentially in sorted order (probability descending, index ascending), so the
+// cut matches a sequential CPU walk.
+#include <algorithm>
+#include <math.h>
+
+#include "lit_common.h"
+#include "select.h"
+
+namespace lit {
+namespace {
+
+constexpr int GT = 16;      // rows and heads per logits tile
+constexpr int HALF = 256;   // dims staged per pass
+constexpr int LSTR = HALF + 1;
+
+__device__ __forceinline__ float kv_elem_f32(int dtype, const void* data, const uint16_t* rope, const uint8_t* scale,
+                                             size_t row, int d) {
+  if (dtype == LIT_F32) return ((const float*)data)[row * LIT_KV_DIM + d];
+  if (dtype == LIT_BF16) return bf16_to_f32(((const uint16_t*)data)[row * LIT_KV_DIM + d]);
+  if (d >= LIT_KV_FP8_DIMS) return bf16_to_f32(rope[row * LIT_KV_ROPE_DIMS + d - LIT_KV_FP8_DIMS]);
+  const uint32_t byte = ((const uint8_t*)data)[row * LIT_KV_FP8_DIMS + d];
+  const uint32_t sb = scale[row * LIT_KV_SCALE_STRIDE + d / LIT_KV_FP8_GROUP];
+  const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
+  float v;
+  if (e == 15u && m == 7u)
+    v = __uint_as_float(0x7fc00000u);
+  else if (e == 0u)
+    v = (float)m * 0x1p-9f;
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  v = __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
+  const float sc = sb == 255u ? __uint_as_float(0x7fc00000u) : (sb == 0u ? 0x1p-127f : __uint_as_float(sb << 23));
+  return v * sc;
+}
+
+__device__ __forceinline__ float q_elem_f32(int dtype, const void* q, size_t off) {
+  return dtype == LIT_F32 ? ((const float*)q)[off] : bf16_to_f32(((const uint16_t*)q)[off]);
+}
+
+// X[b][h][n] = scale * sum_d q[b][h][d] kv[b][n][d], fp64, d ascending.
+__global__ __launch_bounds__(256) void golden_logits_kernel(const void* q, int q_dtype, int Hq, int kv_dtype,
+                                                            const void* data, const uint16_t* rope,
+                                                            const uint8_t* scale, int N, double sc,
+                                                            double* __restrict__ X) {
+  __shared__ float qs[GT][LSTR];
+  __shared__ float ks[GT][LSTR];
+  const int b = blockIdx.z, h0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int tid = threadIdx.x, r = tid >> 4, hh = tid & 15;
+  double acc = 0.0;
+  for (int half = 0; half < 2; half++) {
+    const int d0 = half * HALF;
+    for (int u = tid; u < GT * HALF; u += 256) {
+      const int rr = u / HALF, d = u % HALF;
+      const int h = h0 + rr, n = n0 + rr;
+      qs[rr][d] = h < Hq ? q_elem_f32(q_dtype, q, ((size_t)b * Hq + h) * LIT_KV_DIM + d0 + d) : 0.f;
+      ks[rr][d] = n < N ? kv_elem_f32(kv_dtype, data, rope, scale, (size_t)b * N + n, d0 + d) : 0.f;
+    }
+    __syncthreads();
+    for (int d = 0; d < HALF; d++) acc = fma((double)qs[hh][d], (double)ks[r][d], acc);
+    __syncthreads();
+  }
+  const int h = h0 + hh, n = n0 + r;
+  if (h < Hq && n < N) X[((size_t)b * Hq + h) * N + n] = sc * acc;
+}
+
+// Per (b, h): max and sum of exp(x - max) over n.
+__global__ __launch_bounds__(1024) void golden_stats_kernel(const double* __restrict__ X, int N,
+                                                            double* __restrict__ stats) {
+  __shared__ double red[16];
+  const double* x = X + (size_t)blockIdx.x * N;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  double m = -INFINITY;
+  for (int n = tid; n < N; n += 1024) m = fmax(m, x[n]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  m = red[0];
+  for (int i = 1; i < 16; i++) m = fmax(m, red[i]);
+  __syncthreads();
+  double z = 0.0;
+  for (int n = tid; n < N; n += 1024) z += exp(x[n] - m);
+  z = wave_sum_f64(z);
+  if (lane == 0) red[wid] = z;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int i = 0; i < 16; i++) t += red[i];
+    stats[2 * blockIdx.x] = m;
+    stats[2 * blockIdx.x + 1] = t;
+  }
+}
+
+// pbar[b][n] = (sum_h exp(X - m_h) / Z_h) / Hq, h ascending.
+__global__ __launch_bounds__(256) void golden_pbar_kernel(const double* __restrict__ X, const double* __restrict__ stats,
+                                                          int Hq, int N, double* __restrict__ pbar) {
+  const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  double acc = 0.0;
+  for (int h = 0; h < Hq; h++) {
+    const size_t bh = (size_t)b * Hq + h;
+    acc += exp(X[bh * N + n] - stats[2 * bh]) / stats[2 * bh + 1];
+  }
+  pbar[(size_t)b * N + n] = acc / (double)Hq;
+}
+
+// Top-k of one sequence's fp64 values (value desc, index asc).
+__global__ __launch_bounds__(1024) void topk_f64_kernel(const double* __restrict__ v, int N, int k, uint8_t* sel_ws,
+                                                        int32_t* ids, int32_t* count, uint8_t* mask) {
+  __shared__ SelectScratch sc;
+  const int b = blockIdx.x;
+  const double* vb = v + (size_t)b * N;
+  uint8_t* sel = sel_ws + (size_t)b * N;
+  auto key = [&](int i) -> uint64_t { return score_key64(vb[i]); };
+  int nsel = 0;
+  for (int i = threadIdx.x; i < N; i += blockDim.x) nsel += key(i) != 0ull;
+  int total;
+  block_excl_scan(nsel, sc.scan, &total);
+  if (total <= k) {
+    const int seg = (N + blockDim.x - 1) / blockDim.x;
+    const int a = min(N, (int)threadIdx.x * seg), e = min(N, a + seg);
+    for (int i = a; i < e; i++) sel[i] = key(i) != 0ull;
+  } else {
+    int r_eq;
+    const uint64_t T = radix_select<uint64_t>(key, N, k, &sc, &r_eq);
+    mark_top<uint64_t>(key, N, T, r_eq, sel, &sc);
+  }
+  emit_selection(sel, N, k, ids + (size_t)b * k, count + b, mask ? mask + (size_t)b * N : nullptr, &sc);
+}
+
+// ---- top-p + vote --------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, size_t n, int32_t v) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
+}
+
+// One workgroup per (layer, sequence): probabilities, sort, sequential cut, votes.
+__global__ __launch_bounds__(1024) void topp_kernel(const double* __restrict__ x, int is_logits, int B, int N,
+                                                    int Np2, double top_p, double* __restrict__ prob_ws,
+                                                    uint64_t* __restrict__ key_ws, int32_t* __restrict__ idx_ws,
+                                                    int32_t* __restrict__ votes) {
+  __shared__ double red[16];
+  __shared__ double dshare[2];
+  __shared__ double pchunk[1024];
+  __shared__ int ishare[2];
+  const int lb = blockIdx.x, b = lb % B;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const double* xr = x + (size_t)lb * N;
+  double* pr = prob_ws + (size_t)lb * N;
+  uint64_t* kr = key_ws + (size_t)lb * Np2;
+  int32_t* ir = idx_ws + (size_t)lb * Np2;
+  // probabilities
+  if (is_logits) {
+    double m = -INFINITY;
+    for (int n = tid; n < N; n += 1024) m = fmax(m, xr[n]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    if (tid == 0) {
+      double mm = red[0];
+      for (int i = 1; i < 16; i++) mm = fmax(mm, red[i]);
+      dshare[0] = mm;
+    }
+    __syncthreads();
+    m = dshare[0];
+    for (int n = tid; n < N; n += 1024) pr[n] = exp(xr[n] - m);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {  // Z in index order, as a sequential CPU sum would add it
+      double z = 0.0;
+      for (int n = 0; n < N; n++) z += pr[n];
+      dshare[1] = z;
+    }
+    __syncthreads();
+    const double z = dshare[1];
+    for (int n = tid; n < N; n += 1024) pr[n] = pr[n] / z;
+  } else {
+    for (int n = tid; n < N; n += 1024) pr[n] = xr[n];
+  }
+  __threadfence();
+  __syncthreads();
+  // sort ascending by (inverted key, index) == probability descending, index ascending
+  for (int i = tid; i < Np2; i += 1024) {
+    if (i < N) {
+      kr[i] = ~score_key64(pr[i]);
+      ir[i] = i;
+    } else {
+      kr[i] = ~0ull;
+      ir[i] = 0x7fffffff;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  for (int k2 = 2; k2 <= Np2; k2 <<= 1) {
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < Np2; i += 1024) {
+        const int p = i ^ j;
+        if (p > i) {
+          const uint64_t ka = kr[i], kb = kr[p];
+          const int ia = ir[i], ib = ir[p];
+          const bool a_gt_b = (ka > kb) || (ka == kb && ia > ib);
+          const bool up = (i & k2) == 0;
+          if (a_gt_b == up) {
+            kr[i] = kb;
+            kr[p] = ka;
+            ir[i] = ib;
+            ir[p] = ia;
+          }
+        }
+      }
+      __threadfence();
+      __syncthreads();
+    }
+  }
+  // sequential cut: running sum in sorted order until it reaches top_p
+  if (tid == 0) {
+    ishare[0] = N;
+    dshare[0] = 0.0;
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < N; c0 += 1024) {
+    if (c0 + tid < N) pchunk[tid] = pr[ir[c0 + tid]];
+    __syncthreads();
+    if (tid == 0 && ishare[0] == N) {
+      double run = dshare[0];
+      const int len = min(1024, N - c0);
+      for (int i = 0; i < len; i++) {
+        run += pchunk[i];
+        if (run >= top_p) {
+          ishare[0] = c0 + i + 1;
+          break;
+        }
+      }
+      dshare[0] = run;
+    }
+    __syncthreads();
+    if (ishare[0] != N) break;
+  }
+  const int cut = ishare[0];
+  int32_t* vb = votes + (size_t)b * N;
+  for (int i = tid; i < cut; i += 1024) atomicAdd(&vb[ir[i]], 1);
+}
+
+__global__ __launch_bounds__(256) void vote_kernel(const int32_t* __restrict__ votes, int N, int min_votes,
+                                                   uint8_t* __restrict__ gold, int32_t* __restrict__ gold_count,
+                                                   int32_t* __restrict__ votes_out) {
+  __shared__ int red[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int c = 0;
+  for (int n = tid; n < N; n += 256) {
+    const int v = votes[(size_t)b * N + n];
+    const uint8_t gsel = v >= min_votes;
+    gold[(size_t)b * N + n] = gsel;
+    c += gsel;
+    if (votes_out) votes_out[(size_t)b * N + n] = v;
+  }
+  c = wave_sum(c);
+  if ((tid & 63) == 0) red[tid >> 6] = c;
+  __syncthreads();
+  if (tid == 0) gold_count[b] = red[0] + red[1] + red[2] + red[3];
+}
+
+struct GoldenWs {
+  double* X;
+  double* stats;
+  double* pbar;
+  uint8_t* sel;
+  size_t bytes;
+};
+
+GoldenWs golden_ws(void* base, int B, int Hq, int N) {
+  GoldenWs w;
+  uint8_t* p = (uint8_t*)base;
+  size_t off = 0;
+  w.X = (double*)(p + off);
+  off += round_up((size_t)B * Hq * N * sizeof(double), 256);
+  w.stats = (double*)(p + off);
+  off += round_up((size_t)B * Hq * 2 * sizeof(double), 256);
+  w.pbar = (double*)(p + off);
+  off += round_up((size_t)B * N * sizeof(double), 256);
+  w.sel = p + off;
+  off += round_up((size_t)B * N, 256);
+  w.bytes = off;
+  return w;
+}
+
+int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+}  // namespace
+}  // namespace lit
+
+using namespace lit;
+
+extern "C" size_t lit_golden_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t k) {
+  (void)k;
+  if (B < 1 || Hq < 1 || N < 1) return 0;
+  return golden_ws(nullptr, B, Hq, N).bytes;
+}
+
+extern "C" lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv, int32_t B,
+                                      float scale, int32_t k, int32_t* ids, int32_t* count, uint8_t* mask,
+                                      double* pbar, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  const char* who = "lit_golden_topk";
+  if (!q || !kv || !kv->data || !ids || !count) return fail(LIT_ERR_NULL, "%s: q, kv, ids and count are required", who);
+  if (B < 1 || Hq < 1 || Hq > LIT_MAX_Q_HEADS || kv->n_rows < 1 || k < 1)
+    return fail(LIT_ERR_SHAPE, "%s: B=%d Hq=%d N=%d k=%d", who, B, Hq, kv->n_rows, k);
+  if (kv->dtype == LIT_F32 ? q_dtype != LIT_F32 : q_dtype != LIT_BF16)
+    return fail(LIT_ERR_DTYPE, "%s: query dtype %d does not match rows dtype %d", who, (int)q_dtype, (int)kv->dtype);
+  if (kv->dtype != LIT_F32 && kv->dtype != LIT_BF16 && kv->dtype != LIT_FP8E4M3_G64_ROPE_BF16)
+    return fail(LIT_ERR_DTYPE, "%s: kv dtype %d unsupported", who, (int)kv->dtype);
+  if (kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 && (!kv->rope || !kv->scale))
+    return fail(LIT_ERR_NULL, "%s: FP8 rows need rope and scale arrays", who);
+  const int N = kv->n_rows;
+  GoldenWs W = golden_ws(ws, B, Hq, N);
+  if (!ws || ws_bytes < W.bytes)
+    return fail(LIT_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", who, ws_bytes, W.bytes);
+  if (!aligned(ws, 256) || (pbar && !aligned(pbar, 8)))
+    return fail(LIT_ERR_ALIGN, "%s: workspace must be 256-byte aligned, pbar 8-byte aligned", who);
+  hipStream_t st = (hipStream_t)stream;
+  double* pb = pbar ? pbar : W.pbar;
+  dim3 g1((unsigned)cdiv(N, GT), (unsigned)cdiv(Hq, GT), (unsigned)B);
+  golden_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, Hq, (int)kv->dtype, kv->data, (const uint16_t*)kv->rope,
+                                           kv->scale, N, (double)scale, W.X);
+  LIT_CHECK_LAUNCH(who);
+  golden_stats_kernel<<<dim3((unsigned)(B * Hq)), 1024, 0, st>>>(W.X, N, W.stats);
+  LIT_CHECK_LAUNCH(who);
+  golden_pbar_kernel<<<dim3((unsigned)cdiv(N, 256), (unsigned)B), 256, 0, st>>>(W.X, W.stats, Hq, N, pb);
+  LIT_CHECK_LAUNCH(who);
+  topk_f64_kernel<<<dim3((unsigned)B), 1024, 0, st>>>(pb, N, k, W.sel, ids, count, mask);
+  LIT_CHECK_LAUNCH(who);
+  return LIT_OK;
+}
+
+extern "C" size_t lit_topp_workspace_bytes(int32_t L, int32_t B, int32_t N) {
+  if (L < 1 || B < 1 || N < 1) return 0;
+  const size_t rows = (size_t)L * B;
+  const size_t np2 = (size_t)next_pow2(N);
+  return round_up(rows * N * sizeof(double), 256) + round_up(rows * np2 * sizeof(uint64_t), 256) +
+         round_up(rows * np2 * sizeof(int32_t), 256) + round_up((size_t)B * N * sizeof(int32_t), 256);
+}
+
+extern "C" lit_status lit_golden_topp_vote(const double* x, int32_t is_logits, int32_t L, int32_t B, int32_t N,
+                                           double top_p, int32_t min_votes, uint8_t* gold, int32_t* gold_count,
+                                           int32_t* votes, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  const char* who = "lit_golden_topp_vote";
+  if (!x || !gold || !gold_count) return fail(LIT_ERR_NULL, "%s: x, gold and gold_count are required", who);
+  if (L < 1 || B < 1 || N < 1 || N > (1 << 24)) return fail(LIT_ERR_SHAPE, "%s: L=%d B=%d N=%d", who, L, B, N);
+  if (!(top_p > 0.0 && top_p <= 1.0)) return fail(LIT_ERR_SHAPE, "%s: top_p=%g outside (0,1]", who, top_p);
+  const size_t need = lit_topp_workspace_bytes(L, B, N);
+  if (!ws || ws_bytes < need)
+    return fail(LIT_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", who, ws_bytes, need);
+  if (!aligned(ws, 256) || !aligned(x, 8)) return fail(LIT_ERR_ALIGN, "%s: misaligned x or workspace", who);
+  const size_t rows = (size_t)L * B;
+  const int np2 = next_pow2(N);
+  uint8_t* p = (uint8_t*)ws;
+  double* prob = (double*)p;
+  p += round_up(rows * N * sizeof(double), 256);
+  uint64_t* keys = (uint64_t*)p;
+  p += round_up(rows * np2 * sizeof(uint64_t), 256);
+  int32_t* idx = (int32_t*)p;
+  p += round_up(rows * np2 * sizeof(int32_t), 256);
+  int32_t* vacc = (int32_t*)p;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t nv = (size_t)B * N;
+  fill_i32_kernel<<<dim3((unsigned)std::min<size_t>(cdiv(nv, 256), 4096)), 256, 0, st>>>(vacc, nv, 0);
+  LIT_CHECK_LAUNCH(who);
+  topp_kernel<<<dim3((unsigned)rows), 1024, 0, st>>>(x, is_logits, B, N, np2, top_p, prob, keys, idx, vacc);
+  LIT_CHECK_LAUNCH(who);
+  vote_kernel<<<dim3((unsigned)B), 256, 0, st>>>(vacc, N, min_votes, gold, gold_count, votes);
+  LIT_CHECK_LAUNCH(who);
+  return LIT_OK;
+}

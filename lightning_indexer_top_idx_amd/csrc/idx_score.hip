@@ -1,0 +1,374 @@
+// idx_score.hip - a1: lightning-indexer scores on MFMA (gfx950).
+//
+// [ARCH] ai-muninn.com, "284B 塞得進 128GB、長 context 還跑得動:DeepSeek-V4-Flash 打的是
+// KV cache,不是參數量", section "(B) 只讀你需要的": a light indexer scores every
+// compressed entry with its own 128-dim key (index_comp_kv). The score form is the
+// "native ReLU-MQA" named with the gated equation of zhichai.net, "FlashMemory-DeepSeek-V4
+// 深度解读" (second reply), without the sigmoid:
+//     s[n] = sum_h w[h] * max(0, q[h] . k[n])
+//
+// Shape of the work: per sequence a [H x 128] x [128 x N] product, reduced over h
+// with the weights. At 64 heads that is 64 flop per key byte, far below the MFMA
+// ridge (~312 flop/B), so the kernel is HBM-bound on the key stream; MFMA keeps
+// the arithmetic off the VALU (fp32 VALU alone would be ~3x slower than HBM).
+//
+// Mapping (v_mfma_f32_16x16x32_bf16, wave64): A = 16 heads x 32 dims of q (staged
+// in LDS once per workgroup, already in operand order), B = 32 dims x 16 entries
+// of keys loaded straight from HBM into registers (lane l holds entry l%16 and 8
+// consecutive dims), C = 16 heads x 16 entries. The dims are assigned to the 128
+// K positions so that each lane's four 16-byte key loads cover one contiguous
+// 64-byte piece per K-step; A uses the same assignment, so the dot products are
+// unchanged. A wave handles 64 entries per step (4 column groups), a workgroup
+// handles S chunks of 256 entries; the key-norm side output is one value per
+// 256-entry chunk.
+#include <math.h>
+
+#include "exact.h"
+#include "lit_common.h"
+
+namespace lit {
+namespace {
+
+constexpr int CHUNK = LIT_KNORM_CHUNK;  // 256 entries: 4 waves x 64
+static_assert(CHUNK == 256, "kernel tiling assumes 256-entry chunks");
+
+// Per-lane weights of the heads this lane's accumulators hold.
+template <int MT>
+__device__ __forceinline__ void load_lane_weights(const float* wlds, float (&wr)[MT][4]) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) wr[mt][i] = wlds[16 * mt + 4 * g + i];
+}
+
+// Epilogue shared by both dtypes: weighted ReLU over the lane's heads, summed
+// across the four 16-lane groups (which hold the other heads of the same entry).
+template <int MT>
+__device__ __forceinline__ float weighted_relu(const f32x4 (&acc)[MT], const float (&wr)[MT][4]) {
+  float p = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) p = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), p);
+  p += __shfl_xor(p, 16);
+  p += __shfl_xor(p, 32);
+  return p;
+}
+
+__device__ __forceinline__ float sumsq_bf16x8(u32x4 v) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
+    s = fmaf(a, a, s);
+    s = fmaf(b, b, s);
+  }
+  return s;
+}
+
+template <int MT, int S>
+__global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
+                                                             const float* __restrict__ w,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint8_t* __restrict__ allowed, int H,
+                                                             int N, int nchunks, float* __restrict__ scores,
+                                                             float* __restrict__ kmax) {
+  __shared__ u32x4 qlds[MT * 4 * 64];
+  __shared__ float wlds[64];
+  __shared__ float nmax[4][S];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+
+  // Stage q as MFMA A operands: operand (mt, j) lane (hh + 16*gg) holds head
+  // 16*mt + hh, dims 8*gg + 32*j .. +7.
+  const uint16_t* qb = q + (size_t)b * H * LIT_IDX_DIM;
+  for (int idx = tid; idx < MT * 16 * 16; idx += 256) {
+    const int h = idx >> 4, d8 = idx & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (h < H) v = *(const u32x4*)(qb + h * LIT_IDX_DIM + d8 * 8);
+    const int mt = h >> 4, hh = h & 15, gg = d8 & 3, j = d8 >> 2;
+    qlds[(mt * 4 + j) * 64 + hh + 16 * gg] = v;
+  }
+  if (tid < 64) wlds[tid] = tid < H ? w[(size_t)b * H + tid] : 0.f;
+  __syncthreads();
+  float wr[MT][4];
+  load_lane_weights<MT>(wlds, wr);
+
+  const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
+  const uint8_t* ab = allowed ? allowed + (size_t)b * N : nullptr;
+  float* sb = scores + (size_t)b * N;
+  const int wg_base = blockIdx.x * (S * CHUNK);
+
+#pragma unroll 1
+  for (int s = 0; s < S; s++) {
+    const int base = wg_base + s * CHUNK + wid * 64;
+    u32x4 kr[4][4];
+#pragma unroll
+    for (int G = 0; G < 4; G++) {
+      const int e = base + 16 * G + c;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e < N) v = *(const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 8 * g + 32 * j);
+        kr[G][j] = v;
+      }
+    }
+    f32x4 acc[4][MT];
+#pragma unroll
+    for (int G = 0; G < 4; G++)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[G][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, qlds[(mt * 4 + j) * 64 + lane]);
+#pragma unroll
+        for (int G = 0; G < 4; G++)
+          acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kr[G][j]),
+                                                               acc[G][mt], 0, 0, 0);
+      }
+    float my_score = 0.f, my_n2 = 0.f;
+#pragma unroll
+    for (int G = 0; G < 4; G++) {
+      const float p = weighted_relu<MT>(acc[G], wr);
+      float n2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; j++) n2 += sumsq_bf16x8(kr[G][j]);
+      n2 += __shfl_xor(n2, 16);
+      n2 += __shfl_xor(n2, 32);
+      if (G == g) {
+        my_score = p;
+        my_n2 = n2;
+      }
+    }
+    // lane = 16*g + c holds entry base + lane
+    const int e = base + lane;
+    if (e < N) {
+      float v = my_score;
+      if (ab && ab[e] == 0) v = -INFINITY;
+      sb[e] = v;
+    }
+    const float m = wave_max(my_n2);
+    if (lane == 0) nmax[wid][s] = m;
+  }
+  __syncthreads();
+  if (kmax && tid < S) {
+    const int chunk = blockIdx.x * S + tid;
+    if (chunk < nchunks) {
+      const float m = fmaxf(fmaxf(nmax[0][tid], nmax[1][tid]), fmaxf(nmax[2][tid], nmax[3][tid]));
+      // outward: sqrt and the fp32 sum of squares are each within a few ulp
+      kmax[(size_t)b * nchunks + chunk] = sqrtf(m) * (1.0f + 0x1p-18f);
+    }
+  }
+}
+
+// FP32 inputs: v_mfma_f32_16x16x4_f32, lane l holds A[l%16][l/16] and
+// B[l/16][l%16]; K-step j pairs lane group g with dim 32*g + j.
+template <int MT>
+__global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restrict__ q,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ k,
+                                                            const uint8_t* __restrict__ allowed, int H,
+                                                            int N, int nchunks, float* __restrict__ scores,
+                                                            float* __restrict__ kmax) {
+  __shared__ float qlds[MT * 32 * 64];
+  __shared__ float wlds[64];
+  __shared__ float nmax[4];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const float* qb = q + (size_t)b * H * LIT_IDX_DIM;
+  for (int idx = tid; idx < MT * 16 * LIT_IDX_DIM; idx += 256) {
+    const int h = idx >> 7, d = idx & 127;
+    const float v = h < H ? qb[h * LIT_IDX_DIM + d] : 0.f;
+    const int mt = h >> 4, hh = h & 15, gg = d >> 5, j = d & 31;
+    qlds[(mt * 32 + j) * 64 + hh + 16 * gg] = v;
+  }
+  if (tid < 64) wlds[tid] = tid < H ? w[(size_t)b * H + tid] : 0.f;
+  __syncthreads();
+  float wr[MT][4];
+  load_lane_weights<MT>(wlds, wr);
+
+  const float* kb = k + (size_t)b * N * LIT_IDX_DIM;
+  const uint8_t* ab = allowed ? allowed + (size_t)b * N : nullptr;
+  float* sb = scores + (size_t)b * N;
+  const int base = blockIdx.x * CHUNK + wid * 64;
+  float my_score = 0.f, my_n2 = 0.f;
+#pragma unroll 1
+  for (int G = 0; G < 4; G++) {
+    const int e = base + 16 * G + c;
+    float kr[32];
+#pragma unroll
+    for (int v4 = 0; v4 < 8; v4++) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (e < N) v = *(const f32x4*)(kb + (size_t)e * LIT_IDX_DIM + 32 * g + 4 * v4);
+#pragma unroll
+      for (int i = 0; i < 4; i++) kr[4 * v4 + i] = v[i];
+    }
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int j = 0; j < 32; j++)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qlds[(mt * 32 + j) * 64 + lane], kr[j], acc[mt], 0, 0, 0);
+    const float p = weighted_relu<MT>(acc, wr);
+    float n2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) n2 = fmaf(kr[j], kr[j], n2);
+    n2 += __shfl_xor(n2, 16);
+    n2 += __shfl_xor(n2, 32);
+    if (G == g) {
+      my_score = p;
+      my_n2 = n2;
+    }
+  }
+  const int e = base + lane;
+  if (e < N) {
+    float v = my_score;
+    if (ab && ab[e] == 0) v = -INFINITY;
+    sb[e] = v;
+  }
+  const float m = wave_max(my_n2);
+  if (lane == 0) nmax[wid] = m;
+  __syncthreads();
+  if (kmax && tid == 0 && (int)blockIdx.x < nchunks) {
+    const float mm = fmaxf(fmaxf(nmax[0], nmax[1]), fmaxf(nmax[2], nmax[3]));
+    kmax[(size_t)b * nchunks + blockIdx.x] = sqrtf(mm) * (1.0f + 0x1p-18f);
+  }
+}
+
+// Canonical fp64 scores of every entry: one wave per entry (slow; for labels).
+__global__ __launch_bounds__(256) void idx_score_exact_kernel(const void* __restrict__ q,
+                                                              const float* __restrict__ w,
+                                                              const void* __restrict__ k,
+                                                              const uint8_t* __restrict__ allowed, int dtype,
+                                                              int H, int N, double* __restrict__ out) {
+  __shared__ float qT[LIT_IDX_DIM * 64];
+  __shared__ float krow[4][LIT_IDX_DIM];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int idx = tid; idx < LIT_IDX_DIM * 64; idx += 256) {
+    const int d = idx >> 6, h = idx & 63;
+    float v = 0.f;
+    if (h < H) {
+      const size_t off = ((size_t)b * H + h) * LIT_IDX_DIM + d;
+      v = dtype == LIT_F32 ? ((const float*)q)[off] : bf16_to_f32(((const uint16_t*)q)[off]);
+    }
+    qT[idx] = v;
+  }
+  __syncthreads();
+  const float w_h = lane < H ? w[(size_t)b * H + lane] : 0.f;
+  const int waves = gridDim.x * 4;
+  for (int n = blockIdx.x * 4 + wid; n < N; n += waves) {
+    const size_t row = ((size_t)b * N + n) * LIT_IDX_DIM;
+    for (int d = lane; d < LIT_IDX_DIM; d += 64)
+      krow[wid][d] = dtype == LIT_F32 ? ((const float*)k)[row + d] : bf16_to_f32(((const uint16_t*)k)[row + d]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    double s = exact_score_wave(qT, krow[wid], w_h, H);
+    if (allowed && allowed[(size_t)b * N + n] == 0) s = -INFINITY;
+    if (lane == 0) out[(size_t)b * N + n] = s;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+lit_status check_idx_in(const lit_idx_in* in, int32_t B, int32_t N, const char* who) {
+  if (!in) return fail(LIT_ERR_NULL, "%s: inputs struct is NULL", who);
+  if (!in->q || !in->w || !in->k) return fail(LIT_ERR_NULL, "%s: q, w and k must be non-NULL", who);
+  if (B < 1 || N < 1) return fail(LIT_ERR_SHAPE, "%s: B=%d and N=%d must be >= 1", who, B, N);
+  if (in->H < 1 || in->H > LIT_MAX_IDX_HEADS)
+    return fail(LIT_ERR_SHAPE, "%s: H=%d outside 1..%d", who, in->H, LIT_MAX_IDX_HEADS);
+  if (in->dtype != LIT_F32 && in->dtype != LIT_BF16)
+    return fail(LIT_ERR_DTYPE, "%s: index q/k dtype %d unsupported (F32 or BF16)", who, (int)in->dtype);
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->w, 4))
+    return fail(LIT_ERR_ALIGN, "%s: q and k must be 16-byte aligned, w 4-byte aligned", who);
+  return LIT_OK;
+}
+
+}  // namespace
+
+lit_status check_idx_inputs(const lit_idx_in* in, int32_t B, int32_t N, const char* who) {
+  return check_idx_in(in, B, N, who);
+}
+
+}  // namespace lit
+
+using namespace lit;
+
+template <int MT>
+static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed, int N,
+                        int nchunks, float* scores, float* kmax) {
+  const uint16_t* q = (const uint16_t*)in->q;
+  const uint16_t* k = (const uint16_t*)in->k;
+  if (S == 4)
+    idx_score_bf16_kernel<MT, 4><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, kmax);
+  else if (S == 2)
+    idx_score_bf16_kernel<MT, 2><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, kmax);
+  else
+    idx_score_bf16_kernel<MT, 1><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, kmax);
+}
+
+template <int MT>
+static void launch_f32(dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed, int N,
+                       int nchunks, float* scores, float* kmax) {
+  idx_score_f32_kernel<MT><<<grid, 256, 0, st>>>((const float*)in->q, in->w, (const float*)in->k, allowed, in->H,
+                                                 N, nchunks, scores, kmax);
+}
+
+extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
+                                    float* scores, float* kmax, void* stream) {
+  clear_error();
+  lit_status st = check_idx_in(in, B, N, "lit_idx_score");
+  if (st != LIT_OK) return st;
+  if (!scores) return fail(LIT_ERR_NULL, "lit_idx_score: scores is NULL");
+  if (!aligned(scores, 4) || (kmax && !aligned(kmax, 4)))
+    return fail(LIT_ERR_ALIGN, "lit_idx_score: scores/kmax must be 4-byte aligned");
+  const int nchunks = (int)cdiv(N, CHUNK);
+  const int MT = (in->H + 15) / 16;
+  hipStream_t hs = (hipStream_t)stream;
+  if (in->dtype == LIT_BF16) {
+    // More chunks per workgroup when there is plenty of work: amortises the q staging.
+    const int64_t total = (int64_t)B * nchunks;
+    const int S = total >= 4096 ? 4 : (total >= 2048 ? 2 : 1);
+    dim3 grid((unsigned)cdiv(nchunks, S), (unsigned)B);
+    switch (MT) {
+      case 1: launch_bf16<1>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      case 2: launch_bf16<2>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      case 3: launch_bf16<3>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      default: launch_bf16<4>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+    }
+  } else {
+    dim3 grid((unsigned)nchunks, (unsigned)B);
+    switch (MT) {
+      case 1: launch_f32<1>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      case 2: launch_f32<2>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      case 3: launch_f32<3>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      default: launch_f32<4>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+    }
+  }
+  LIT_CHECK_LAUNCH("lit_idx_score");
+  return LIT_OK;
+}
+
+extern "C" lit_status lit_idx_score_exact(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
+                                          double* scores64, void* stream) {
+  clear_error();
+  lit_status st = check_idx_in(in, B, N, "lit_idx_score_exact");
+  if (st != LIT_OK) return st;
+  if (!scores64) return fail(LIT_ERR_NULL, "lit_idx_score_exact: scores64 is NULL");
+  if (!aligned(scores64, 8)) return fail(LIT_ERR_ALIGN, "lit_idx_score_exact: scores64 must be 8-byte aligned");
+  const int per_b = (int)std::min<int64_t>(cdiv(N, 4), 1024);
+  dim3 grid((unsigned)per_b, (unsigned)B);
+  idx_score_exact_kernel<<<grid, 256, 0, (hipStream_t)stream>>>(in->q, in->w, in->k, allowed, (int)in->dtype,
+                                                                in->H, N, scores64);
+  LIT_CHECK_LAUNCH("lit_idx_score_exact");
+  return LIT_OK;
+}

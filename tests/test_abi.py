@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every symbol include/lit.h declares, and
+rejects bad arguments on the host (no GPU needed: validation enqueues nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lightning_indexer_top_idx_amd as lit
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lit.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lit_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(lit.LIB_PATH):
+        pytest.fail("liblit.so is not built (python -m lightning_indexer_top_idx_amd.build)")
+    return lit.load()
+
+
+def test_every_declared_symbol_is_exported(L):
+    syms = declared_symbols()
+    assert len(syms) >= 15
+    for s in syms:
+        assert hasattr(L, s), f"{s} missing from liblit.so"
+    assert sorted(lit.EXPORTS) == syms
+
+
+def test_abi_version(L):
+    assert L.lit_abi_version() == 1
+
+
+def _idx(q=0x1000, w=0x2000, k=0x3000, dtype=1, H=64):
+    return lit.IdxIn(q, w, k, dtype, H)
+
+
+def test_idx_score_validation(L):
+    sc = ctypes.c_void_p(0x4000)
+    assert L.lit_idx_score(None, None, 1, 16, sc, None, None) == 1  # NULL inputs
+    assert "NULL" in lit.last_error()
+    d = _idx(H=0)
+    assert L.lit_idx_score(ctypes.byref(d), None, 1, 16, sc, None, None) == 2
+    d = _idx(H=65)
+    assert L.lit_idx_score(ctypes.byref(d), None, 1, 16, sc, None, None) == 2
+    d = _idx(dtype=2)  # FP8 index keys are not a supported index dtype
+    assert L.lit_idx_score(ctypes.byref(d), None, 1, 16, sc, None, None) == 4
+    d = _idx(k=0x3008)  # keys must be 16-byte aligned
+    assert L.lit_idx_score(ctypes.byref(d), None, 1, 16, sc, None, None) == 3
+    d = _idx()
+    assert L.lit_idx_score(ctypes.byref(d), None, 0, 16, sc, None, None) == 2
+    assert L.lit_idx_score(ctypes.byref(d), None, 1, 16, None, None, None) == 1
+
+
+def test_topk_validation(L):
+    p = ctypes.c_void_p
+    need = L.lit_topk_workspace_bytes(2, 1000, 64)
+    assert need >= 2 * 1000 * 13
+    assert L.lit_topk_select(None, 2, 1000, 64, None, None, p(0x1000), p(0x2000), None, p(0x3000), need, None) == 1
+    assert L.lit_topk_select(p(0x4000), 2, 1000, 0, None, None, p(0x1000), p(0x2000), None, p(0x3000), need, None) == 2
+    assert L.lit_topk_select(p(0x4000), 2, 1000, 64, None, None, p(0x1000), p(0x2000), None, p(0x3000), need - 1,
+                             None) == 5
+    assert L.lit_topk_select(p(0x4000), 2, 1000, 64, None, None, p(0x1000), p(0x2000), None, None, need, None) == 5
+    d = _idx()
+    # exact mode without the kmax side output
+    assert L.lit_topk_select(p(0x4000), 2, 1000, 64, ctypes.byref(d), None, p(0x1000), p(0x2000), None, p(0x3000),
+                             need, None) == 1
+    assert "kmax" in lit.last_error()
+
+
+def test_attention_validation(L):
+    p = ctypes.c_void_p
+    kv = lit.KVDesc(1, 1000, 0x1000, None, None)
+    assert L.lit_sparse_attn_decode(None, 1, 64, ctypes.byref(kv), 1, None, None, 0, 0, 0.04, p(0x2000), None, None,
+                                    0, None) == 1
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 65, ctypes.byref(kv), 1, None, None, 0, 0, 0.04, p(0x2000), None,
+                                    None, 0, None) == 2
+    # f16-like dtype that is not supported: the call refuses instead of exiting
+    kvbad = lit.KVDesc(7, 1000, 0x1000, None, None)
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kvbad), 1, None, None, 0, 0, 0.04, p(0x2000),
+                                    None, None, 0, None) == 4
+    # bf16 rows with fp32 queries
+    assert L.lit_sparse_attn_decode(p(0x3000), 0, 64, ctypes.byref(kv), 1, None, None, 0, 0, 0.04, p(0x2000), None,
+                                    None, 0, None) == 4
+    # FP8 rows without scale / rope
+    kv8 = lit.KVDesc(2, 1000, 0x1000, None, None)
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv8), 1, None, None, 0, 0, 0.04, p(0x2000), None,
+                                    None, 0, None) == 1
+    # window out of range
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv), 1, p(0x5000), p(0x6000), 512, 9000, 0.04,
+                                    p(0x2000), None, None, 0, None) == 2
+    # misaligned rows
+    kvm = lit.KVDesc(1, 1000, 0x1004, None, None)
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kvm), 1, None, None, 0, 0, 0.04, p(0x2000), None,
+                                    None, 0, None) == 3
+    # many sequences split the rows: the workspace is required
+    assert L.lit_attn_workspace_bytes(4, 64, 125000) > 256
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04, p(0x2000), None,
+                                    None, 0, None) == 5
+
+
+def test_other_entry_points_validation(L):
+    p = ctypes.c_void_p
+    assert L.lit_recall(None, p(0x1000), 1, 10, None, None, None, None) == 1
+    assert L.lit_recall(p(0x1000), p(0x1000), 0, 10, None, None, None, None) == 2
+    kv = lit.KVDesc(1, 100, 0x1000, None, None)
+    assert L.lit_golden_topk(p(0x2000), 1, 64, ctypes.byref(kv), 1, 0.04, 0, p(0x3000), p(0x4000), None, None,
+                             p(0x5000), 1 << 30, None) == 2
+    assert L.lit_golden_topp_vote(p(0x1000), 0, 21, 1, 100, 1.5, 3, p(0x2000), p(0x3000), None, p(0x4000), 1 << 30,
+                                  None) == 2
+    assert L.lit_golden_topp_vote(p(0x1000), 0, 21, 1, 100, 0.6, 3, p(0x2000), p(0x3000), None, p(0x4000), 16,
+                                  None) == 5
+    layers = (lit.GateLayerDesc * 1)(lit.GateLayerDesc(0x1000, 0x2000, 0x3000, 0x4000, 0x5000))
+    assert L.lit_lsa_gate(layers, 1, 1, 100, 64, 4096, 2048, 1.0, p(0x6000), p(0x7000), p(0x8000), 1 << 30,
+                          None) == 2
+    assert L.lit_lsa_gate(layers, 9, 1, 100, 64, 4096, 2048, 0.5, p(0x6000), p(0x7000), p(0x8000), 1 << 30,
+                          None) == 2
+    bad = (lit.GateLayerDesc * 1)(lit.GateLayerDesc(0x1000, 0, 0x3000, 0x4000, 0x5000))
+    assert L.lit_lsa_gate(bad, 1, 1, 100, 64, 4096, 2048, 0.5, p(0x6000), p(0x7000), p(0x8000), 1 << 30, None) == 1
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+
+    saved = lit._lib
+    try:
+        lit._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            lit.load(str(tmp_path / "missing.so"))
+    finally:
+        lit._lib = saved
