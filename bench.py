@@ -1,0 +1,331 @@
+"""Benchmark of the lightning-indexer decode step on one MI355X.
+
+A step is one decode step of the whole hot path over one batch: for each of
+the 21 CSA layers, in sequence, the indexer scores (a1), the exact top-512
+(a2) and the sparse MQA attention over the selected rows plus the 128-row
+window (a3), for 32 sequences at 64K context (16384 compressed entries each).
+One query = one sequence x one layer x one decode step; value = queries/s.
+
+Inputs are synthetic (seeded, generated on the GPU) and resident in HBM before
+the timed region. The step is captured once in a HIP graph (checked against
+the eager result) and replayed. Besides the headline line the JSON carries:
+  roofline     : the dominant kernel (indexer scores) - algorithmic bytes per
+                 launch / its average launch time, measured with HIP events on
+                 the stream it runs on, against the 8 TB/s HBM peak;
+  cpu_baseline : the CPU oracle on a bounded sample of the same queries;
+  others       : the 64K batch-1 latency and the 500K batch-4 step.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode queries/sec (indexer+top-512+sparse attn) at 64K/500K ctx; % HBM roofline"
+
+
+def algo_bytes_per_query(N, H, k, window, Hq, kv_row_bytes=1024):
+    """Algorithmic HBM bytes of one query of the path (score + select + attend)."""
+    keys = N * 128 * 2
+    rows = min(N, k + window) * kv_row_bytes
+    small = H * 128 * 2 + H * 4 + Hq * 512 * 2 + Hq * 512 * 4 + k * 4
+    return keys + rows + small
+
+
+def idx_score_bytes_per_query(N, H):
+    """Algorithmic bytes of one query of the indexer-score kernel: the keys, the
+    queries and weights, the fp32 scores written and the key-norm chunk maxima."""
+    return N * 128 * 2 + H * 128 * 2 + H * 4 + N * 4 + (-(-N // 256)) * 4
+
+
+class Path:
+    """Preallocated buffers of one layer of B sequences and the three C calls."""
+
+    def __init__(self, lit, L, k, window, scale, dev):
+        import torch
+
+        self.lit, self.L = lit, L
+        self.B, self.N = L.idx.k_idx.shape[0], L.idx.k_idx.shape[1]
+        self.H, self.Hq = L.idx.q_idx.shape[1], L.q.shape[1]
+        self.k, self.window, self.scale = k, window, scale
+        B, N = self.B, self.N
+        self.scores = torch.empty(B, N, dtype=torch.float32, device=dev)
+        self.kmax = torch.empty(B, -(-N // 256), dtype=torch.float32, device=dev)
+        self.ids = torch.empty(B, k, dtype=torch.int32, device=dev)
+        self.count = torch.empty(B, dtype=torch.int32, device=dev)
+        self.out = torch.empty(B, self.Hq, 512, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(B, self.Hq, dtype=torch.float32, device=dev)
+        C = lit.load()
+        self.ws_topk = torch.empty(C.lit_topk_workspace_bytes(B, N, k), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(C.lit_attn_workspace_bytes(B, self.Hq, N), dtype=torch.uint8, device=dev)
+        self.idx_desc = lit.idx_in(L.idx.q_idx, L.idx.w, L.idx.k_idx)
+        self.kv_desc = lit.kv_desc(L.kv)
+        self.C = C
+
+    def score(self, stream):
+        st = self.C.lit_idx_score(ctypes.byref(self.idx_desc), None, self.B, self.N, self.scores.data_ptr(),
+                                  self.kmax.data_ptr(), stream)
+        assert st == 0, self.lit.last_error()
+
+    def select(self, stream):
+        st = self.C.lit_topk_select(self.scores.data_ptr(), self.B, self.N, self.k, ctypes.byref(self.idx_desc),
+                                    self.kmax.data_ptr(), self.ids.data_ptr(), self.count.data_ptr(), None,
+                                    self.ws_topk.data_ptr(), self.ws_topk.numel(), stream)
+        assert st == 0, self.lit.last_error()
+
+    def attend(self, stream):
+        st = self.C.lit_sparse_attn_decode(self.L.q.data_ptr(), self.lit.LIT_BF16, self.Hq, ctypes.byref(self.kv_desc),
+                                           self.B, self.ids.data_ptr(), self.count.data_ptr(), self.k, self.window,
+                                           self.scale, self.out.data_ptr(), self.lse.data_ptr(),
+                                           self.ws_attn.data_ptr(), self.ws_attn.numel(), stream)
+        assert st == 0, self.lit.last_error()
+
+    def run(self, stream):
+        self.score(stream)
+        self.select(stream)
+        self.attend(stream)
+
+
+def capture(fn):
+    """Captures fn(stream) into a graph; returns the graph."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(torch.cuda.current_stream().cuda_stream)  # warm (attributes, code objects)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps):
+    import torch
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3  # seconds
+
+
+def stored_traffic(kernel_src, workload):
+    """Per-launch HBM bytes of the indexer-score kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"idx_score_{workload}_counters.json")
+    src = os.path.join(ROOT, "lightning_indexer_top_idx_amd", "csrc", kernel_src)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != h:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(layers, wl, k, window, scale, budget_s, max_queries, threads, gpu_paths):
+    """The oracle, as it stands, on a bounded sample of the same queries."""
+    import numpy as np
+    import oracle
+
+    oracle.build()
+    jobs, keys = [], []
+    n_layers, B = len(layers), layers[0].idx.k_idx.shape[0]
+    picks = [(l, (7 * l + 3) % B) for l in range(n_layers)][:max_queries]
+    for l, b in picks:
+        L = layers[l]
+        jobs.append(dict(q_idx=oracle.np_of(L.idx.q_idx[b]), w=oracle.np_of(L.idx.w[b]).copy(),
+                         k_idx=oracle.np_of(L.idx.k_idx[b]), k=k, q=oracle.np_of(L.q[b]), kv_dtype=oracle.BF16,
+                         data=oracle.np_of(L.kv.data[b]), window=window, scale_f=scale))
+        keys.append((l, b))
+    # parity of the timed path on the sample (ids bit-exact, outputs within 2e-2)
+    t0 = time.perf_counter()
+    res = oracle.decode_queries(jobs, threads=threads)
+    done, elapsed = len(jobs), time.perf_counter() - t0
+    while elapsed < budget_s:
+        t1 = time.perf_counter()
+        oracle.decode_queries(jobs, threads=threads)
+        done += len(jobs)
+        elapsed += time.perf_counter() - t1
+    ids_ok, worst = True, 0.0
+    for (l, b), (c, rids, rout, _) in zip(keys, res):
+        P = gpu_paths[l]
+        ids_ok &= bool(np.array_equal(P.ids[b].cpu().numpy(), rids))
+        o = P.out[b].double().cpu().numpy()
+        worst = max(worst, float((np.abs(o - rout).max(-1) / np.abs(rout).max(-1)).max()))
+    return {"value": done / elapsed, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(jobs)} distinct queries of the timed workload (one sequence per layer), "
+                      f"score+exact top-{k}+attention in fp64 C, {done} query runs in {elapsed:.1f} s",
+            "parity_on_sample": {"ids_bit_exact": ids_ok, "attn_max_rel_err": worst}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not supported "
+                                   "(the path shards by sequence with no communication; see the design notes)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lightning_indexer_top_idx_amd as lit
+    from lightning_indexer_top_idx_amd import workloads as W
+
+    lit.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.CTX64K_B
+    scale = 1.0 / math.sqrt(512)
+    print(f"[bench] generating {wl.name}: {wl.layers} layers x {wl.B} sequences x N={wl.N}", file=sys.stderr,
+          flush=True)
+    layers = [W.layer_inputs(wl, l, dev) for l in range(wl.layers)]
+    paths = [Path(lit, L, wl.k, wl.window, scale, dev) for L in layers]
+    torch.cuda.synchronize()
+
+    def step(stream):
+        for P in paths:
+            P.run(stream)
+
+    # eager reference, then the captured step; every replay must match it
+    step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref_ids = [P.ids.clone() for P in paths]
+    ref_out = [P.out.clone() for P in paths]
+    g = capture(step)
+    for _ in range(2):
+        for P in paths:
+            P.ids.fill_(-7)
+            P.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for P, ri, ro in zip(paths, ref_ids, ref_out):
+            assert torch.equal(P.ids, ri) and torch.equal(P.out, ro), "graph replay differs from the eager step"
+    print("[bench] graph replay matches the eager step", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    secs = time_graph(g, args.steps)
+    wall = time.perf_counter() - t0
+    q_per_step = wl.B * wl.layers
+    value = q_per_step * args.steps / secs
+    ms_per_step = secs / args.steps * 1e3
+    per_query = algo_bytes_per_query(wl.N, wl.H, wl.k, wl.window, wl.Hq)
+    print(f"[bench] {ms_per_step:.3f} ms/step, {value:.0f} queries/s", file=sys.stderr, flush=True)
+
+    # dominant kernel: the indexer scores, 21 launches back to back in one graph
+    gs = capture(lambda s: [P.score(s) for P in paths])
+    reps = 10
+    sec_s = time_graph(gs, reps)
+    launch_s = sec_s / (reps * len(paths))
+    score_bytes = idx_score_bytes_per_query(wl.N, wl.H) * wl.B
+    achieved = score_bytes / launch_s / 1e9
+    traffic = stored_traffic("idx_score.hip", wl.name)
+    roofline = {"bound": "hbm", "kernel": "idx_score (indexer scores, MFMA bf16)", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "avg_launch_us": round(launch_s * 1e6, 2),
+                "algorithmic_bytes_per_launch": score_bytes}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ctx64k_b: 32 sequences x 21 CSA layers run in sequence, 64K context "
+                               "(N=16384 compressed entries), 64x128 index heads, exact top-512 + SWA 128, "
+                               "64-head MQA over 512-wide bf16 rows",
+                   "global_batch": wl.B, "seq_len": 65536, "layers": wl.layers, "parallelism": "none (1 GPU)"},
+        "path_roofline": {"algorithmic_bytes_per_query": per_query,
+                          "achieved_GBs": round(per_query * value / 1e9, 1),
+                          "frac": round(per_query * value / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        print(f"[bench] CPU oracle on {threads} threads", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(layers, wl, wl.k, wl.window, scale, args.cpu_seconds, wl.layers,
+                                           threads, paths)
+
+    if not args.no_others:
+        out["others"] = others(lit, W, dev, scale)
+
+    del g, gs
+    print(json.dumps(out))
+
+
+def others(lit, W, dev, scale):
+    """Secondary figures: 64K batch-1 latency and the 500K batch-4 step."""
+    import torch
+
+    res = {}
+    # 64K, batch 1: 32 independent layers rotated so the data exceeds the 256 MB cache
+    wl = W.CTX64K
+    n_rot = 32
+    layers = [W.layer_inputs(wl, 100 + l, dev) for l in range(n_rot)]
+    paths = [Path(lit, L, wl.k, wl.window, scale, dev) for L in layers]
+    g = capture(lambda s: [P.run(s) for P in paths])
+    g.replay()
+    sec = time_graph(g, 5)
+    per_q = sec / (5 * n_rot)
+    res["ctx64k_b1"] = {"us_per_query": round(per_q * 1e6, 2), "queries_per_s": round(1 / per_q, 1),
+                        "note": "batch 1, one query per step; 32 distinct layers replayed back to back in a graph"}
+    del g, paths, layers
+    torch.cuda.empty_cache()
+    # 500K, batch 4: one CSA layer (N=125000) + one HCA layer (3907 rows read densely)
+    wl = W.CTX500K
+    L = W.layer_inputs(wl, 0, dev)
+    P = Path(lit, L, wl.k, wl.window, scale, dev)
+    hq, hkv = W.hca_inputs(wl, dev)
+    hout = torch.empty(wl.B, wl.Hq, 512, dtype=torch.float32, device=dev)
+    C = lit.load()
+    hws = torch.empty(C.lit_attn_workspace_bytes(wl.B, wl.Hq, wl.hca_N), dtype=torch.uint8, device=dev)
+    hdesc = lit.kv_desc(hkv)
+
+    def hca(s):
+        st = C.lit_sparse_attn_decode(hq.data_ptr(), lit.LIT_BF16, wl.Hq, ctypes.byref(hdesc), wl.B, None, None, 0, 0,
+                                      scale, hout.data_ptr(), None, hws.data_ptr(), hws.numel(), s)
+        assert st == 0, lit.last_error()
+
+    gc = capture(lambda s: P.run(s))
+    gh = capture(hca)
+    csa_s = time_graph(gc, 20) / 20
+    hca_s = time_graph(gh, 20) / 20
+    per_query = algo_bytes_per_query(wl.N, wl.H, wl.k, wl.window, wl.Hq)
+    res["ctx500k_b4"] = {"csa_step_us": round(csa_s * 1e6, 2), "queries_per_s": round(wl.B / csa_s, 1),
+                         "hbm_frac": round(per_query * wl.B / csa_s / 1e9 / HBM_PEAK_GBS, 4),
+                         "hca_layer_us": round(hca_s * 1e6, 2),
+                         "hca_hbm_frac": round(wl.B * wl.hca_N * 1024 / hca_s / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+if __name__ == "__main__":
+    main()

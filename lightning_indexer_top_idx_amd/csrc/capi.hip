@@ -2,6 +2,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+#include <vector>
+
 #include "lit_common.h"
 
 namespace {
@@ -28,9 +31,23 @@ lit_status launch_status(const char* what) {
 
 lit_status allow_lds(const void* kernel, size_t bytes, const char* what) {
   if (bytes <= 65536) return LIT_OK;
+  // Once per (kernel, device, size): keeps the attribute call out of captured graphs' hot path.
+  struct Entry {
+    const void* k;
+    int dev;
+    size_t bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LIT_ERR_LAUNCH, "%s: no current HIP device", what);
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : done)
+    if (e.k == kernel && e.dev == dev && e.bytes >= bytes) return LIT_OK;
   hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess)
     return fail(LIT_ERR_LAUNCH, "%s: cannot reserve %zu bytes of LDS: %s", what, bytes, hipGetErrorString(e));
+  done.push_back({kernel, dev, bytes});
   return LIT_OK;
 }
 
