@@ -60,7 +60,7 @@ class Path:
         self.k, self.window, self.scale = k, window, scale
         B, N = self.B, self.N
         self.scores = torch.empty(B, N, dtype=torch.float32, device=dev)
-        self.kmax = torch.empty(B, -(-N // 256), dtype=torch.float32, device=dev)
+        self.hints = torch.empty(B, lit.hints_len(N), dtype=torch.float32, device=dev)
         self.ids = torch.empty(B, k, dtype=torch.int32, device=dev)
         self.count = torch.empty(B, dtype=torch.int32, device=dev)
         self.out = torch.empty(B, self.Hq, 512, dtype=torch.float32, device=dev)
@@ -74,12 +74,12 @@ class Path:
 
     def score(self, stream):
         st = self.C.lit_idx_score(ctypes.byref(self.idx_desc), None, self.B, self.N, self.scores.data_ptr(),
-                                  self.kmax.data_ptr(), stream)
+                                  self.hints.data_ptr(), stream)
         assert st == 0, self.lit.last_error()
 
     def select(self, stream):
         st = self.C.lit_topk_select(self.scores.data_ptr(), self.B, self.N, self.k, ctypes.byref(self.idx_desc),
-                                    self.kmax.data_ptr(), self.ids.data_ptr(), self.count.data_ptr(), None,
+                                    self.hints.data_ptr(), self.ids.data_ptr(), self.count.data_ptr(), None,
                                     self.ws_topk.data_ptr(), self.ws_topk.numel(), stream)
         assert st == 0, self.lit.last_error()
 

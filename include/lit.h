@@ -65,8 +65,10 @@ extern "C" {
 #define LIT_KV_ROPE_DIMS 64
 #define LIT_KV_FP8_GROUP 64
 #define LIT_KV_SCALE_STRIDE 8 /* bytes per row of E8M0 scales: 7 used, 1 pad */
-/* Entries per chunk of the key-norm side output of lit_idx_score. */
+/* Entries per chunk of the key-norm part of lit_idx_score's hints. */
 #define LIT_KNORM_CHUNK 256
+/* Entries per group of the score-maximum part of lit_idx_score's hints. */
+#define LIT_HINT_GROUP 16
 /* Limits. */
 #define LIT_MAX_IDX_HEADS 64
 #define LIT_MAX_Q_HEADS 64
@@ -144,12 +146,15 @@ const char* lit_last_error(void);
  * allowed : [B][N] u8 or NULL. Where allowed[b][n] == 0 the score is -inf
  *           (the candidate set restricted by the gate, [FMEN] "The setup").
  * scores  : [B][N] fp32 output.
- * kmax    : [B][ceil(N/LIT_KNORM_CHUNK)] fp32 output or NULL: for each chunk of
- *           LIT_KNORM_CHUNK consecutive entries, an upper bound of the largest
- *           Euclidean norm of a key in it. lit_topk_select needs it for exact
- *           selection. */
+ * hints   : [B][lit_idx_hints_len(N)] fp32 output or NULL; the side output
+ *           lit_topk_select reads. hints[b][c] for c < ceil(N/LIT_KNORM_CHUNK)
+ *           is an upper bound of the largest Euclidean key norm among entries
+ *           c*LIT_KNORM_CHUNK ... +LIT_KNORM_CHUNK-1; hints[b][ceil(N/LIT_KNORM_CHUNK) + j]
+ *           is the largest of the scores written for entries LIT_HINT_GROUP*j ...
+ *           +LIT_HINT_GROUP-1 (-inf when none is allowed). */
+int32_t lit_idx_hints_len(int32_t N);
 lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
-                         float* scores, float* kmax, void* stream);
+                         float* scores, float* hints, void* stream);
 
 /* ---- a2: top-k selection -----------------------------------------------------
  * [ARCH] (B): keep the n_indexer_top_k (512; 1024 for the Pro variant) best
@@ -161,16 +166,21 @@ lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B
  * exact != NULL : the order is that of the exact scores, i.e. the definition of
  *   lit_idx_score evaluated in fp64 in canonical order (d ascending within a head,
  *   then h ascending, each w*relu product rounded before it is added). `exact`
- *   must be the same inputs that produced `scores`, and `kmax` its side output;
+ *   must be the same inputs that produced `scores`, and `hints` its side output;
  *   entries whose fp32 score lies within a proven error bound of the k-th score
  *   are rescored in fp64 so the selection equals the fp64 one bit for bit.
+ * hints : the side output of lit_idx_score for these scores, or NULL (then
+ *   every score is scanned, which is slower; exact mode requires hints).
+ *   With hints the call reads only the groups of entries that can reach the
+ *   top k (a lower bound on the k-th score comes from the group maxima).
  * ids   : [B][k] int32 output, selected indices ascending, tail filled with -1.
- * count : [B] int32 output.
+ * count : [B] int32 output (-1 would signal that the proven rounding bound was
+ *         violated; the call then selects nothing rather than guess).
  * mask  : [B][N] u8 output (1 = selected) or NULL.
  * Workspace: lit_topk_workspace_bytes(B, N, k) bytes. */
 size_t lit_topk_workspace_bytes(int32_t B, int32_t N, int32_t k);
 lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k,
-                           const lit_idx_in* exact, const float* kmax,
+                           const lit_idx_in* exact, const float* hints,
                            int32_t* ids, int32_t* count, uint8_t* mask,
                            void* ws, size_t ws_bytes, void* stream);
 

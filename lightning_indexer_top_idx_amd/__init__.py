@@ -31,7 +31,7 @@ _STATUS = {0: "LIT_OK", 1: "LIT_ERR_NULL", 2: "LIT_ERR_SHAPE", 3: "LIT_ERR_ALIGN
            5: "LIT_ERR_WORKSPACE", 6: "LIT_ERR_LAUNCH"}
 
 EXPORTS = [
-    "lit_abi_version", "lit_last_error", "lit_idx_score", "lit_topk_workspace_bytes", "lit_topk_select",
+    "lit_abi_version", "lit_last_error", "lit_idx_hints_len", "lit_idx_score", "lit_topk_workspace_bytes", "lit_topk_select",
     "lit_attn_workspace_bytes", "lit_sparse_attn_decode", "lit_golden_workspace_bytes", "lit_golden_topk",
     "lit_topp_workspace_bytes", "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall",
     "lit_gate_workspace_bytes", "lit_lsa_gate",
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH):
     vp, i32, sz, f32, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_double
     L.lit_abi_version.restype = ctypes.c_int
     L.lit_last_error.restype = ctypes.c_char_p
+    L.lit_idx_hints_len.argtypes = [i32]
+    L.lit_idx_hints_len.restype = i32
     L.lit_idx_score.argtypes = [ctypes.POINTER(IdxIn), vp, i32, i32, vp, vp, vp]
     L.lit_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.lit_topk_workspace_bytes.restype = sz
@@ -169,24 +171,30 @@ def kv_desc(kv) -> KVDesc:
 # the calls
 
 
-def idx_score(q_idx, w, k_idx, allowed=None, want_kmax: bool = True, out=None):
-    """a1: scores [B,N] fp32 (+ kmax [B,ceil(N/256)] key-norm chunk maxima)."""
+def hints_len(N: int) -> int:
+    return load().lit_idx_hints_len(N)
+
+
+def idx_score(q_idx, w, k_idx, allowed=None, want_hints: bool = True, out=None):
+    """a1: scores [B,N] fp32 and the selection hints [B, hints_len(N)] (key-norm
+    chunk bounds, then per-16-entry score maxima)."""
     torch = _torch()
     B, N = k_idx.shape[0], k_idx.shape[1]
     _need_cuda(allowed)
     scores = out if out is not None else torch.empty(B, N, dtype=torch.float32, device=k_idx.device)
-    kmax = torch.empty(B, -(-N // KNORM_CHUNK), dtype=torch.float32, device=k_idx.device) if want_kmax else None
+    hints = torch.empty(B, hints_len(N), dtype=torch.float32, device=k_idx.device) if want_hints else None
     desc = idx_in(q_idx, w, k_idx)
-    _check(load().lit_idx_score(ctypes.byref(desc), _ptr(allowed), B, N, scores.data_ptr(), _ptr(kmax),
+    _check(load().lit_idx_score(ctypes.byref(desc), _ptr(allowed), B, N, scores.data_ptr(), _ptr(hints),
                                 _stream(k_idx)))
-    return scores, kmax
+    return scores, hints
 
 
-def topk_select(scores, k: int, exact=None, kmax=None, want_mask: bool = True, ws=None):
+def topk_select(scores, k: int, exact=None, hints=None, want_mask: bool = True, ws=None):
     """a2: ids [B,k] ascending (tail -1), count [B], mask [B,N] u8.
-    exact: (q_idx, w, k_idx) that produced the scores -> fp64-exact selection."""
+    exact: (q_idx, w, k_idx) that produced the scores -> fp64-exact selection;
+    hints: the second output of idx_score for these scores."""
     torch = _torch()
-    _need_cuda(scores, kmax)
+    _need_cuda(scores, hints)
     B, N = scores.shape
     dev = scores.device
     ids = torch.empty(B, k, dtype=torch.int32, device=dev)
@@ -198,7 +206,7 @@ def topk_select(scores, k: int, exact=None, kmax=None, want_mask: bool = True, w
         ws = workspace(need, dev)
     desc = idx_in(*exact) if exact is not None else None
     _check(L.lit_topk_select(scores.data_ptr(), B, N, k, ctypes.byref(desc) if desc is not None else None,
-                             _ptr(kmax), ids.data_ptr(), count.data_ptr(), _ptr(mask), ws.data_ptr(), ws.numel(),
+                             _ptr(hints), ids.data_ptr(), count.data_ptr(), _ptr(mask), ws.data_ptr(), ws.numel(),
                              _stream(scores)))
     return ids, count, mask
 

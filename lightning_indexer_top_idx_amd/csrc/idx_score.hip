@@ -67,19 +67,56 @@ __device__ __forceinline__ float sumsq_bf16x8(u32x4 v) {
   return s;
 }
 
+// Loads the keys of 64 entries (4 column groups of 16) as B operands.
+__device__ __forceinline__ void load_keys_bf16(const uint16_t* kb, int base, int N, int g, int c,
+                                               u32x4 (&kr)[4][4]) {
+#pragma unroll
+  for (int G = 0; G < 4; G++) {
+    const int e = base + 16 * G + c;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (e < N) v = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 8 * g + 32 * j));
+      kr[G][j] = v;
+    }
+  }
+}
+
+// Scores of the lane's entry (lane = 16 g + c holds entry base + lane): the
+// allowed mask applied, the score stored, and the group maximum returned in
+// every lane of the 16-lane group (entries at or past N count as -inf).
+__device__ __forceinline__ float store_score(float v, int e, int N, const uint8_t* ab, float* sb) {
+  if (e < N) {
+    if (ab && ab[e] == 0) v = -INFINITY;
+    sb[e] = v;
+  } else {
+    v = -INFINITY;
+  }
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
 template <int MT, int S>
 __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ w,
                                                              const uint16_t* __restrict__ k,
                                                              const uint8_t* __restrict__ allowed, int H,
                                                              int N, int nchunks, float* __restrict__ scores,
-                                                             float* __restrict__ kmax) {
+                                                             float* __restrict__ hints, int hints_len) {
   __shared__ u32x4 qlds[MT * 4 * 64];
   __shared__ float wlds[64];
   __shared__ float nmax[4][S];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
+  const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
+  const int wg_base = blockIdx.x * (S * CHUNK);
+  // the first step's keys are in flight while q is staged
+  u32x4 kr[4][4];
+  load_keys_bf16(kb, wg_base + wid * 64, N, g, c, kr);
 
   // Stage q as MFMA A operands: operand (mt, j) lane (hh + 16*gg) holds head
   // 16*mt + hh, dims 8*gg + 32*j .. +7.
@@ -96,25 +133,14 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
   float wr[MT][4];
   load_lane_weights<MT>(wlds, wr);
 
-  const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
   const uint8_t* ab = allowed ? allowed + (size_t)b * N : nullptr;
   float* sb = scores + (size_t)b * N;
-  const int wg_base = blockIdx.x * (S * CHUNK);
+  float* gm = hints ? hints + (size_t)b * hints_len + nchunks : nullptr;
 
 #pragma unroll 1
   for (int s = 0; s < S; s++) {
     const int base = wg_base + s * CHUNK + wid * 64;
-    u32x4 kr[4][4];
-#pragma unroll
-    for (int G = 0; G < 4; G++) {
-      const int e = base + 16 * G + c;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (e < N) v = *(const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 8 * g + 32 * j);
-        kr[G][j] = v;
-      }
-    }
+    if (s > 0) load_keys_bf16(kb, base, N, g, c, kr);
     f32x4 acc[4][MT];
 #pragma unroll
     for (int G = 0; G < 4; G++)
@@ -146,21 +172,18 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
     }
     // lane = 16*g + c holds entry base + lane
     const int e = base + lane;
-    if (e < N) {
-      float v = my_score;
-      if (ab && ab[e] == 0) v = -INFINITY;
-      sb[e] = v;
-    }
+    const float gmax = store_score(my_score, e, N, ab, sb);
+    if (gm && c == 0 && base + 16 * g < N) gm[(base + 16 * g) / 16] = gmax;
     const float m = wave_max(my_n2);
     if (lane == 0) nmax[wid][s] = m;
   }
   __syncthreads();
-  if (kmax && tid < S) {
+  if (hints && tid < S) {
     const int chunk = blockIdx.x * S + tid;
     if (chunk < nchunks) {
       const float m = fmaxf(fmaxf(nmax[0][tid], nmax[1][tid]), fmaxf(nmax[2][tid], nmax[3][tid]));
       // outward: sqrt and the fp32 sum of squares are each within a few ulp
-      kmax[(size_t)b * nchunks + chunk] = sqrtf(m) * (1.0f + 0x1p-18f);
+      hints[(size_t)b * hints_len + chunk] = sqrtf(m) * (1.0f + 0x1p-18f);
     }
   }
 }
@@ -173,7 +196,7 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
                                                             const float* __restrict__ k,
                                                             const uint8_t* __restrict__ allowed, int H,
                                                             int N, int nchunks, float* __restrict__ scores,
-                                                            float* __restrict__ kmax) {
+                                                            float* __restrict__ hints, int hints_len) {
   __shared__ float qlds[MT * 32 * 64];
   __shared__ float wlds[64];
   __shared__ float nmax[4];
@@ -228,17 +251,14 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
     }
   }
   const int e = base + lane;
-  if (e < N) {
-    float v = my_score;
-    if (ab && ab[e] == 0) v = -INFINITY;
-    sb[e] = v;
-  }
+  const float gmax = store_score(my_score, e, N, ab, sb);
+  if (hints && c == 0 && base + 16 * g < N) hints[(size_t)b * hints_len + nchunks + (base + 16 * g) / 16] = gmax;
   const float m = wave_max(my_n2);
   if (lane == 0) nmax[wid] = m;
   __syncthreads();
-  if (kmax && tid == 0 && (int)blockIdx.x < nchunks) {
+  if (hints && tid == 0 && (int)blockIdx.x < nchunks) {
     const float mm = fmaxf(fmaxf(nmax[0], nmax[1]), fmaxf(nmax[2], nmax[3]));
-    kmax[(size_t)b * nchunks + blockIdx.x] = sqrtf(mm) * (1.0f + 0x1p-18f);
+    hints[(size_t)b * hints_len + blockIdx.x] = sqrtf(mm) * (1.0f + 0x1p-18f);
   }
 }
 
@@ -305,33 +325,39 @@ using namespace lit;
 
 template <int MT>
 static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed, int N,
-                        int nchunks, float* scores, float* kmax) {
+                        int nchunks, float* scores, float* hints, int hl) {
   const uint16_t* q = (const uint16_t*)in->q;
   const uint16_t* k = (const uint16_t*)in->k;
   if (S == 4)
-    idx_score_bf16_kernel<MT, 4><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, kmax);
+    idx_score_bf16_kernel<MT, 4><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
   else if (S == 2)
-    idx_score_bf16_kernel<MT, 2><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, kmax);
+    idx_score_bf16_kernel<MT, 2><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
   else
-    idx_score_bf16_kernel<MT, 1><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, kmax);
+    idx_score_bf16_kernel<MT, 1><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
 }
 
 template <int MT>
 static void launch_f32(dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed, int N,
-                       int nchunks, float* scores, float* kmax) {
+                       int nchunks, float* scores, float* hints, int hl) {
   idx_score_f32_kernel<MT><<<grid, 256, 0, st>>>((const float*)in->q, in->w, (const float*)in->k, allowed, in->H,
-                                                 N, nchunks, scores, kmax);
+                                                 N, nchunks, scores, hints, hl);
+}
+
+extern "C" int32_t lit_idx_hints_len(int32_t N) {
+  if (N < 1) return 0;
+  return (int32_t)(cdiv(N, LIT_KNORM_CHUNK) + cdiv(N, LIT_HINT_GROUP));
 }
 
 extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
-                                    float* scores, float* kmax, void* stream) {
+                                    float* scores, float* hints, void* stream) {
   clear_error();
   lit_status st = check_idx_in(in, B, N, "lit_idx_score");
   if (st != LIT_OK) return st;
   if (!scores) return fail(LIT_ERR_NULL, "lit_idx_score: scores is NULL");
-  if (!aligned(scores, 4) || (kmax && !aligned(kmax, 4)))
-    return fail(LIT_ERR_ALIGN, "lit_idx_score: scores/kmax must be 4-byte aligned");
+  if (!aligned(scores, 4) || (hints && !aligned(hints, 4)))
+    return fail(LIT_ERR_ALIGN, "lit_idx_score: scores/hints must be 4-byte aligned");
   const int nchunks = (int)cdiv(N, CHUNK);
+  const int hl = lit_idx_hints_len(N);
   const int MT = (in->H + 15) / 16;
   hipStream_t hs = (hipStream_t)stream;
   if (in->dtype == LIT_BF16) {
@@ -340,18 +366,18 @@ extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed
     const int S = total >= 4096 ? 4 : (total >= 2048 ? 2 : 1);
     dim3 grid((unsigned)cdiv(nchunks, S), (unsigned)B);
     switch (MT) {
-      case 1: launch_bf16<1>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
-      case 2: launch_bf16<2>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
-      case 3: launch_bf16<3>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
-      default: launch_bf16<4>(S, grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      case 1: launch_bf16<1>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
+      case 2: launch_bf16<2>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
+      case 3: launch_bf16<3>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
+      default: launch_bf16<4>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
     }
   } else {
     dim3 grid((unsigned)nchunks, (unsigned)B);
     switch (MT) {
-      case 1: launch_f32<1>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
-      case 2: launch_f32<2>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
-      case 3: launch_f32<3>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
-      default: launch_f32<4>(grid, hs, in, allowed, N, nchunks, scores, kmax); break;
+      case 1: launch_f32<1>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
+      case 2: launch_f32<2>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
+      case 3: launch_f32<3>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
+      default: launch_f32<4>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
     }
   }
   LIT_CHECK_LAUNCH("lit_idx_score");

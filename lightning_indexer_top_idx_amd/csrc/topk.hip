@@ -7,16 +7,21 @@
 // ids to the attention kernel. The pages build that mask on the host; here it
 // never leaves the device. Ties go to the lower index.
 //
-// One workgroup (1024 threads) per sequence:
-//   1. fp32 scores -> order-preserving u32 keys (in LDS when N <= 16384);
-//   2. MSB-first radix select (4 passes of 8 bits) finds the k-th largest key T;
-//   3. exact mode: every fp32 score is within Delta of its fp64 canonical value,
-//      where Delta bounds the fp32 MFMA/FMA rounding through the key norms
-//      (chunk maxima from lit_idx_score) and sum_h |w_h| |q_h|. Entries above
-//      T + 2 Delta are in for sure, entries below T - 2 Delta out for sure; the
-//      few in between are rescored in fp64 in canonical order and the best
-//      k - (#sure) of them are taken by (score desc, index asc);
-//   4. one ordered compaction pass writes ascending ids, the mask and the count.
+// One workgroup (1024 threads) per sequence. Fast path (with the hints of
+// lit_idx_score, N <= 131072):
+//   1. the k-th largest of the per-16-entry score maxima is a lower bound L of
+//      the k-th largest score (it is the k-th largest of a subset of the scores);
+//   2. only groups whose maximum reaches L can hold top-k entries: their entries
+//      >= L are gathered into LDS, in index order (~k groups are read, not N);
+//   3. an MSB-first radix select over those candidates gives the k-th score T;
+//   4. exact mode: every fp32 score is within Delta of its fp64 canonical value
+//      (Delta bounds the fp32 MFMA/FMA rounding through the key-norm hints and
+//      sum_h |w_h| |q_h|). Entries above T + 2 Delta are in for sure, entries below
+//      T - 2 Delta out; the few in between are rescored in fp64 in canonical
+//      order and the best of them taken by (score desc, index asc);
+//   5. a bitmap of the selection is compacted into ascending ids (and the mask).
+// Anything that does not fit (no hints, larger N, too many candidates after ties)
+// falls back to scanning every score with the same steps.
 #include <algorithm>
 #include <math.h>
 
@@ -30,9 +35,17 @@ lit_status check_idx_inputs(const lit_idx_in* in, int32_t B, int32_t N, const ch
 namespace {
 
 constexpr int TK_THREADS = 1024;
-constexpr int LDS_KEYS = 16384;                                // keys held per LDS chunk
-constexpr int LDS_KEY_WORDS = LDS_KEYS + (LDS_KEYS >> 5);      // one pad word per 32 keys
-constexpr int BAND_LDS = 2048;                                  // band entries kept in LDS
+constexpr int NWAVES = TK_THREADS / 64;
+// full-scan path
+constexpr int LDS_KEYS = 16384;                            // keys held per LDS chunk
+constexpr int LDS_KEY_WORDS = LDS_KEYS + (LDS_KEYS >> 5);  // one pad word per 32 keys
+constexpr int BAND_LDS = 2048;                             // band entries kept in LDS
+// fast path
+constexpr int GROUP = LIT_HINT_GROUP;
+constexpr int GM_CAP = 8192;                   // group maxima in LDS: N <= 131072
+constexpr int CAND_CAP = 2048;                 // candidates >= L in LDS
+constexpr int FBAND_CAP = 1024;                // exact band in LDS
+constexpr int SEL_WORDS = GM_CAP * GROUP / 32;  // selection bitmap
 // Safety factor on the rounding bound (2 already covers truncating adds).
 constexpr double ERR_SAFETY = 4.0;
 
@@ -46,27 +59,58 @@ struct TopkParams {
   const float* w;
   const void* kidx;
   int dtype, H;
-  const float* kmax;
-  int nchunks;
+  const float* hints;
+  int hints_len, nchunks;
   int32_t* ids;
   int32_t* count;
   uint8_t* mask;
-  double* ws_band_s;    // [B][N]
-  int32_t* ws_band_n;   // [B][N]
-  uint8_t* ws_band_sel; // [B][N]
+  double* ws_band_s;     // [B][N]
+  int32_t* ws_band_n;    // [B][N]
+  uint8_t* ws_band_sel;  // [B][N]
 };
 
-struct TopkLds {
+struct FullLds {
   SelectScratch sc;
   int imisc[8];
   double dmisc[4];
   float qT[LIT_IDX_DIM * 64];
-  float krow[TK_THREADS / 64][LIT_IDX_DIM];
+  float krow[NWAVES][LIT_IDX_DIM];
   double band_s[BAND_LDS];
   int32_t band_n[BAND_LDS];
   uint8_t band_sel[BAND_LDS];
   uint32_t keys[LDS_KEY_WORDS];
 };
+
+constexpr int QP_STRIDE = LIT_IDX_DIM + 4;  // fp32 q row stride in LDS (spreads banks)
+constexpr int RS = 2;                       // entries rescored together by one wave
+
+struct FastLds {
+  SelectScratch sc;
+  int imisc[8];
+  double dmisc[4];
+  double qn[64];
+  double wa[64];
+  float qP[64 * QP_STRIDE];
+  float krow[NWAVES][RS][LIT_IDX_DIM];
+  double psum[NWAVES][RS][64];
+  double band_s[FBAND_CAP];
+  int32_t band_n[FBAND_CAP];
+  uint32_t band_k[FBAND_CAP];
+  uint8_t cflag[CAND_CAP];
+  union {  // never live at the same time
+    uint32_t hist2k[2048];
+    uint16_t qlist[GM_CAP];
+    uint16_t binpos[CAND_CAP];
+  };
+  union {
+    uint32_t gkey[GM_CAP];
+    uint32_t sel[SEL_WORDS];
+  };
+  uint32_t ckey[CAND_CAP];
+  int32_t cidx[CAND_CAP];
+};
+
+static_assert(sizeof(FastLds) <= 160 * 1024 && sizeof(FullLds) <= 160 * 1024, "LDS budget of a gfx950 CU");
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -78,10 +122,576 @@ __device__ __forceinline__ float load_idx(const void* p, int dtype, size_t off) 
   return dtype == LIT_F32 ? ((const float*)p)[off] : bf16_to_f32(((const uint16_t*)p)[off]);
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  TopkLds& L = *reinterpret_cast<TopkLds*>(smem);
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// Exact-mode band edges around the k-th fp32 score `tkey`: keys outside
+// [*lo, *hi] are provably on the same side of the fp64 k-th score as their fp32
+// value says. Block-wide; uses krow[0][0..NWAVES) and dmisc as scratch.
+__device__ void exact_band(const TopkParams& P, int b, uint32_t tkey, float (*krow)[LIT_IDX_DIM], double* dmisc,
+                           uint32_t* lo, uint32_t* hi) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (wid == 0) {
+    double wq = 0.0, wa = 0.0;
+    if (lane < P.H) {
+      const size_t qo = ((size_t)b * P.H + lane) * LIT_IDX_DIM;
+      double n2 = 0.0;
+#pragma unroll 8
+      for (int d = 0; d < LIT_IDX_DIM; d++) {
+        const double x = (double)load_idx(P.q, P.dtype, qo + d);
+        n2 += x * x;
+      }
+      wa = fabs((double)P.w[(size_t)b * P.H + lane]);
+      wq = wa * sqrt(n2);
+    }
+    wq = wave_sum_f64(wq);
+    wa = wave_sum_f64(wa);
+    if (lane == 0) {
+      dmisc[0] = wq;
+      dmisc[1] = wa;
+    }
+  }
+  float km = 0.f;
+  for (int j = tid; j < P.nchunks; j += TK_THREADS) km = fmaxf(km, P.hints[(size_t)b * P.hints_len + j]);
+  km = wave_max(km);
+  if (lane == 0) krow[0][wid] = km;
+  __syncthreads();
+  if (tid == 0) {
+    float m = 0.f;
+    for (int i = 0; i < NWAVES; i++) m = fmaxf(m, krow[0][i]);
+    const double terms = (double)(LIT_IDX_DIM + P.H + 2);
+    const double delta = (ERR_SAFETY * 0x1p-24 * terms * dmisc[0] * (double)m +
+                          ERR_SAFETY * terms * 0x1p-126 * dmisc[1]) * (1.0 + 0x1p-20);
+    const double t = (double)key_score(tkey);
+    dmisc[2] = t - 2.0 * delta;
+    dmisc[3] = t + 2.0 * delta;
+  }
+  __syncthreads();
+  const uint32_t l = score_key(__double2float_rd(dmisc[2]));
+  *lo = l > 1u ? l : 1u;
+  *hi = score_key(__double2float_ru(dmisc[3]));
+  __syncthreads();
+}
+
+// Stages q transposed (qT[d*64 + h], zero for h >= H) for the fp64 rescoring.
+__device__ void stage_qT(const TopkParams& P, int b, float* qT) {
+  for (int idx = threadIdx.x; idx < LIT_IDX_DIM * 64; idx += TK_THREADS) {
+    const int d = idx >> 6, h = idx & 63;
+    qT[idx] = h < P.H ? load_idx(P.q, P.dtype, ((size_t)b * P.H + h) * LIT_IDX_DIM + d) : 0.f;
+  }
+  __syncthreads();
+}
+
+// fp64 canonical score of entry n, one wave.
+__device__ __forceinline__ double rescore(const TopkParams& P, int b, int n, const float* qT, float* krow,
+                                          float w_h) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = ((size_t)b * P.N + n) * LIT_IDX_DIM;
+  for (int d = lane; d < LIT_IDX_DIM; d += 64) krow[d] = load_idx(P.kidx, P.dtype, row + d);
+  wave_sync();
+  const double s = exact_score_wave(qT, krow, w_h, P.H);
+  wave_sync();
+  return s;
+}
+
+__device__ void report_violation(const TopkParams& P, int b, int32_t* ids, uint8_t* mask) {
+  for (int j = threadIdx.x; j < P.k; j += TK_THREADS) ids[j] = -1;
+  if (mask)
+    for (int i = threadIdx.x; i < P.N; i += TK_THREADS) mask[i] = 0;
+  if (threadIdx.x == 0) P.count[b] = -1;
+}
+
+// ---------------------------------------------------------------- fast path
+
+// Block-wide reduction of (sum, min, max) over all threads; uses sc->scan.
+__device__ __forceinline__ void block_sum_min_max(int& s, uint32_t& mn, uint32_t& mx, float& fm,
+                                                  SelectScratch* sc) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o);
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    fm = fmaxf(fm, __shfl_xor(fm, o));
+  }
+  __syncthreads();
+  if (lane == 0) {
+    sc->scan[wid] = s;
+    sc->hist[wid] = mn;
+    sc->hist[16 + wid] = mx;
+    sc->hist[32 + wid] = __float_as_uint(fm);
+  }
+  __syncthreads();
+  s = 0;
+  mn = 0xffffffffu;
+  mx = 0u;
+  fm = 0.f;
+  for (int i = 0; i < NWAVES; i++) {
+    s += sc->scan[i];
+    mn = min(mn, sc->hist[i]);
+    mx = max(mx, sc->hist[16 + i]);
+    fm = fmaxf(fm, __uint_as_float(sc->hist[32 + i]));
+  }
+  __syncthreads();
+}
+
+// One 2048-bin histogram pass over the non-zero keys in [kmin, kmax] (the bins
+// span the bits below the keys' common prefix). Finds the bin holding the r-th
+// largest key. Returns the bin's lower edge; *above = keys in higher bins,
+// *in_bin = keys in the bin; *binfn receives (prefix, shift) for bin numbers.
+template <typename KeyFn>
+__device__ uint32_t hist_kth(KeyFn key, int M, int r, uint32_t kmin, uint32_t kmax, uint32_t* hist2k,
+                             SelectScratch* sc, int* above, int* in_bin, uint32_t* prefix_out, int* shift_out) {
+  const int tid = threadIdx.x;
+  const uint32_t diff = kmin ^ kmax;
+  const int hb = diff ? 31 - __clz((int)diff) : 0;
+  const int shift = hb > 10 ? hb - 10 : 0;
+  const uint32_t prefix = kmax & ~((2u << hb) - 1u);
+  for (int i = tid; i < 2048; i += TK_THREADS) hist2k[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < M; i += TK_THREADS) {
+    const uint32_t kk = key(i);
+    if (kk != 0u) atomicAdd(&hist2k[(kk - prefix) >> shift], 1u);
+  }
+  __syncthreads();
+  // cumulative counts from the top bin down: thread t owns bins 2047-2t, 2046-2t
+  const int c0 = (int)hist2k[2047 - 2 * tid], c1 = (int)hist2k[2046 - 2 * tid];
+  int tot;
+  const int ab = block_excl_scan(c0 + c1, sc->scan, &tot);
+  if (ab < r && r <= ab + c0) {
+    sc->misc[0] = 2047 - 2 * tid;
+    sc->misc[1] = ab;
+    sc->misc[2] = c0;
+  } else if (ab + c0 < r && r <= ab + c0 + c1) {
+    sc->misc[0] = 2046 - 2 * tid;
+    sc->misc[1] = ab + c0;
+    sc->misc[2] = c1;
+  }
+  __syncthreads();
+  const int bin = sc->misc[0];
+  *above = sc->misc[1];
+  *in_bin = sc->misc[2];
+  *prefix_out = prefix;
+  *shift_out = shift;
+  __syncthreads();
+  return prefix + ((uint32_t)bin << shift);
+}
+
+// Gathers, in index order, the entries whose key is in [lo, hi) from the groups
+// whose maximum reaches lo. Appends at out_key/out_idx + base. Returns the
+// number found, or -1 (writing nothing) when base + found would exceed cap.
+// The qualifying groups are listed first so each thread loads about one group
+// (one 64-byte read) and all loads are in flight together.
+__device__ int gather_range(const float* sb, int N, const uint32_t* gkey, uint16_t* qlist, int G, uint32_t lo,
+                            uint32_t hi, uint32_t* out_key, int32_t* out_idx, int base, int cap,
+                            SelectScratch* sc) {
+  const int tid = threadIdx.x;
+  const bool vec = (reinterpret_cast<uintptr_t>(sb) & 15u) == 0;
+  auto load16 = [&](int g, float (&v)[GROUP]) {
+    const int e0 = GROUP * g;
+    if (vec && e0 + GROUP <= N) {
+#pragma unroll
+      for (int c = 0; c < GROUP / 4; c++) {
+        const f32x4 x = *(const f32x4*)(sb + e0 + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[4 * c + i] = x[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < GROUP; i++) v[i] = e0 + i < N ? sb[e0 + i] : -INFINITY;
+    }
+  };
+  auto in_range = [&](float x) -> bool {
+    const uint32_t kk = score_key(x);
+    return (kk >= lo) && (kk < hi) && (kk != 0u);
+  };
+  // 1. list the qualifying groups in index order
+  const int gseg = (G + TK_THREADS - 1) / TK_THREADS;
+  const int ga = min(G, tid * gseg), ge = min(G, ga + gseg);
+  int nq = 0;
+  for (int g = ga; g < ge; g++) nq += gkey[g] >= lo;
+  int Q;
+  int qp = block_excl_scan(nq, sc->scan, &Q);
+  for (int g = ga; g < ge; g++)
+    if (gkey[g] >= lo) qlist[qp++] = (uint16_t)g;
+  __syncthreads();
+  // 2. count per contiguous run of list positions; the first group stays in registers
+  const int qseg = (Q + TK_THREADS - 1) / TK_THREADS;
+  const int qa = min(Q, tid * qseg), qe = min(Q, qa + qseg);
+  float v0[GROUP];
+  int c = 0;
+  if (qa < qe) {
+    load16(qlist[qa], v0);
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) c += in_range(v0[i]);
+  }
+  for (int j = qa + 1; j < qe; j++) {
+    float v[GROUP];
+    load16(qlist[j], v);
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) c += in_range(v[i]);
+  }
+  int total;
+  int p = base + block_excl_scan(c, sc->scan, &total);
+  if (base + total > cap) return -1;
+  if (qa < qe) {
+    const int e0 = GROUP * qlist[qa];
+#pragma unroll
+    for (int i = 0; i < GROUP; i++)
+      if (in_range(v0[i])) {
+        out_key[p] = score_key(v0[i]);
+        out_idx[p] = e0 + i;
+        p++;
+      }
+  }
+  for (int j = qa + 1; j < qe; j++) {
+    float v[GROUP];
+    const int g = qlist[j];
+    load16(g, v);
+#pragma unroll
+    for (int i = 0; i < GROUP; i++)
+      if (in_range(v[i])) {
+        out_key[p] = score_key(v[i]);
+        out_idx[p] = GROUP * g + i;
+        p++;
+      }
+  }
+  __syncthreads();
+  return total;
+}
+
+// One lane's share (dims 2*lane, 2*lane+1) of a key row, for the fp64 rescoring.
+__device__ __forceinline__ float2 key_pair(const TopkParams& P, int b, int n) {
+  const int lane = threadIdx.x & 63;
+  const size_t off = ((size_t)b * P.N + n) * LIT_IDX_DIM + 2 * lane;
+  if (P.dtype == LIT_BF16) {
+    const uint32_t v = *(const uint32_t*)((const uint16_t*)P.kidx + off);
+    return make_float2(bf16_lo(v), bf16_hi(v));
+  }
+  return *(const float2*)((const float*)P.kidx + off);
+}
+
+// fp64 canonical scores of NC entries by one wave, their chains interleaved:
+// lane h owns head h (q row in qP); each entry's key row is staged in krow[c]
+// from the lanes' pairs kp[c] and read back as broadcasts; the per-head
+// products go through psum[c] and are summed in head order. Every lane returns
+// the NC scores.
+template <int NC>
+__device__ __forceinline__ void rescore_multi(const float* qP, const float2 (&kp)[NC], float w_h, int H,
+                                              float (*krow)[LIT_IDX_DIM], double (*psum)[64], double (&out)[NC]) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < NC; c++) *(float2*)(krow[c] + 2 * lane) = kp[c];
+  wave_sync();
+  const float* qr = qP + lane * QP_STRIDE;
+  double acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; c++) acc[c] = 0.0;
+#pragma unroll 2
+  for (int d0 = 0; d0 < LIT_IDX_DIM; d0 += 8) {
+    const f32x4 qa = *(const f32x4*)(qr + d0), qb = *(const f32x4*)(qr + d0 + 4);
+    f32x4 ka[NC], kb[NC];
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+      ka[c] = *(const f32x4*)(krow[c] + d0);
+      kb[c] = *(const f32x4*)(krow[c] + d0 + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) acc[c] = fma((double)qa[j], (double)ka[c][j], acc[c]);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) acc[c] = fma((double)qb[j], (double)kb[c][j], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; c++) {
+    const double r = acc[c] > 0.0 ? acc[c] : 0.0;
+    psum[c][lane] = (double)w_h * r;
+    out[c] = 0.0;
+  }
+  wave_sync();
+  if (lane == 0) {
+    int h = 0;
+    for (; h + 8 <= H; h += 8) {
+      double t[NC][8];
+#pragma unroll
+      for (int c = 0; c < NC; c++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) t[c][i] = psum[c][h + i];
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int c = 0; c < NC; c++) out[c] = out[c] + t[c][i];
+    }
+    for (; h < H; h++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) out[c] = out[c] + psum[c][h];
+  }
+#pragma unroll
+  for (int c = 0; c < NC; c++) out[c] = __shfl(out[c], 0);
+  wave_sync();
+}
+
+// Returns false, having written nothing, when the sequence does not fit.
+__device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int N = P.N, k = P.k;
+  const float* sb = P.scores + (size_t)b * N;
+  const float* gmx = P.hints + (size_t)b * P.hints_len + P.nchunks;
+  int32_t* ids = P.ids + (size_t)b * k;
+  uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
+  const int G = (N + GROUP - 1) / GROUP;
+  const int W = (N + 31) / 32;
+
+  // 0. exact mode: q rows (fp32) and |w_h| |q_h|, one 8-dim piece per thread
+  if (P.exact) {
+    const int h = tid >> 4, d8 = tid & 15;
+    float x[8];
+    if (h < P.H) {
+      const size_t off = ((size_t)b * P.H + h) * LIT_IDX_DIM + 8 * d8;
+      if (P.dtype == LIT_BF16) {
+        const u32x4 v = *(const u32x4*)((const uint16_t*)P.q + off);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          x[2 * i] = bf16_lo(v[i]);
+          x[2 * i + 1] = bf16_hi(v[i]);
+        }
+      } else {
+        const f32x4 v0 = *(const f32x4*)((const float*)P.q + off), v1 = *(const f32x4*)((const float*)P.q + off + 4);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          x[i] = v0[i];
+          x[4 + i] = v1[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = 0.f;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      L.qP[h * QP_STRIDE + 8 * d8 + i] = x[i];
+      ss += (double)x[i] * (double)x[i];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+    if (d8 == 0) {
+      const double wa = h < P.H ? fabs((double)P.w[(size_t)b * P.H + h]) : 0.0;
+      L.qn[h] = wa * sqrt(ss);
+      L.wa[h] = wa;
+    }
+  }
+
+  // 1. group keys (+ the largest key-norm bound in exact mode)
+  int ns = 0;
+  uint32_t kmin = 0xffffffffu, kmx = 0u;
+  float knorm = 0.f;
+  for (int g = tid; g < G; g += TK_THREADS) {
+    const uint32_t kk = score_key(gmx[g]);
+    L.gkey[g] = kk;
+    if (kk) {
+      ns++;
+      kmin = min(kmin, kk);
+      kmx = max(kmx, kk);
+    }
+  }
+  if (P.exact)
+    for (int j = tid; j < P.nchunks; j += TK_THREADS) knorm = fmaxf(knorm, P.hints[(size_t)b * P.hints_len + j]);
+  block_sum_min_max(ns, kmin, kmx, knorm, &L.sc);
+  if (ns == 0) {
+    for (int j = tid; j < k; j += TK_THREADS) ids[j] = -1;
+    if (mask)
+      for (int n = tid; n < N; n += TK_THREADS) mask[n] = 0;
+    if (tid == 0) P.count[b] = 0;
+    return true;
+  }
+
+  // 2. lower bound L: the lower edge of the histogram bin holding the k-th group maximum
+  uint32_t lkey = 1u;
+  if (ns >= k) {
+    int above, inb, shift;
+    uint32_t prefix;
+    lkey = hist_kth([&](int i) -> uint32_t { return L.gkey[i]; }, G, k, kmin, kmx, L.hist2k, &L.sc, &above, &inb,
+                    &prefix, &shift);
+  }
+
+  // 3. candidates >= L in index order
+  const int M1 = gather_range(sb, N, L.gkey, L.qlist, G, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc);
+  if (M1 < 0) return false;
+  // (a key of 0xffffffff would be a NaN pattern: score_key maps NaN to 0)
+
+  uint32_t* sel = L.sel;  // aliases gkey: cleared once gkey is no longer read
+  if (M1 <= k) {
+    for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
+    __syncthreads();
+    for (int i = tid; i < M1; i += TK_THREADS) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
+  } else {
+    // 4. the k-th candidate: histogram bin, then exact ranks inside the bin
+    uint32_t cmin = 0xffffffffu, cmx = 0u;
+    int dummy = 0;
+    float fd = 0.f;
+    for (int i = tid; i < M1; i += TK_THREADS) {
+      cmin = min(cmin, L.ckey[i]);
+      cmx = max(cmx, L.ckey[i]);
+    }
+    block_sum_min_max(dummy, cmin, cmx, fd, &L.sc);
+    int above, inb, shift;
+    uint32_t prefix;
+    const uint32_t bin_lo = hist_kth([&](int i) -> uint32_t { return L.ckey[i]; }, M1, k, cmin, cmx, L.hist2k,
+                                     &L.sc, &above, &inb, &prefix, &shift);
+    const uint32_t bin_id = (bin_lo - prefix) >> shift;
+    const int r = k - above;  // members of the bin that are selected
+    // rank inside the bin by (key desc, index asc); the r-th gives T. The bin's
+    // members are listed first (candidate positions, index order) so the ranking
+    // only compares members with each other.
+    {
+      const int cs = (M1 + TK_THREADS - 1) / TK_THREADS;
+      const int c0 = min(M1, tid * cs), c1 = min(M1, c0 + cs);
+      int nin = 0;
+      for (int i = c0; i < c1; i++) nin += ((L.ckey[i] - prefix) >> shift) == bin_id;
+      int m;
+      int bp = block_excl_scan(nin, L.sc.scan, &m);
+      for (int i = c0; i < c1; i++) {
+        L.cflag[i] = 0;
+        if (((L.ckey[i] - prefix) >> shift) == bin_id) L.binpos[bp++] = (uint16_t)i;
+      }
+      __syncthreads();
+      for (int t = tid; t < m; t += TK_THREADS) {
+        const int i = L.binpos[t];
+        const uint32_t ki = L.ckey[i];
+        const int ni = L.cidx[i];
+        int rank = 0;
+        for (int j = 0; j < m; j++) {
+          const int pj = L.binpos[j];
+          const uint32_t kj = L.ckey[pj];
+          rank += (kj > ki) || (kj == ki && L.cidx[pj] < ni);
+        }
+        L.cflag[i] = rank < r;
+        if (rank == r - 1) L.sc.misc[4] = (int)ki;
+      }
+    }
+    __syncthreads();
+    const uint32_t T = (uint32_t)L.sc.misc[4];
+    if (!P.exact) {
+      for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
+      __syncthreads();
+      for (int i = tid; i < M1; i += TK_THREADS) {
+        const uint32_t ki = L.ckey[i];
+        const uint32_t bi = (ki - prefix) >> shift;
+        if (bi > bin_id || (bi == bin_id && L.cflag[i])) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
+      }
+    } else {
+      // 5. exact band around T
+      if (tid == 0) {
+        double Q = 0.0, Wa = 0.0;
+        for (int h = 0; h < P.H; h++) {
+          Q += L.qn[h];
+          Wa += L.wa[h];
+        }
+        const double terms = (double)(LIT_IDX_DIM + P.H + 2);
+        const double delta = (ERR_SAFETY * 0x1p-24 * terms * Q * (double)knorm +
+                              ERR_SAFETY * terms * 0x1p-126 * Wa) * (1.0 + 0x1p-20);
+        const double t = (double)key_score(T);
+        L.dmisc[2] = t - 2.0 * delta;
+        L.dmisc[3] = t + 2.0 * delta;
+      }
+      __syncthreads();
+      const uint32_t lo0 = score_key(__double2float_rd(L.dmisc[2]));
+      const uint32_t lo = lo0 > 1u ? lo0 : 1u;
+      const uint32_t hi = score_key(__double2float_ru(L.dmisc[3]));
+      // band members among the candidates (index order) and the sure ones
+      const int cseg = (M1 + TK_THREADS - 1) / TK_THREADS;
+      const int ca = min(M1, tid * cseg), ce = min(M1, ca + cseg);
+      int nd = 0, nb = 0;
+      for (int i = ca; i < ce; i++) {
+        const uint32_t kk = L.ckey[i];
+        nd += kk > hi;
+        nb += (kk >= lo) && (kk <= hi);
+      }
+      int tot;
+      int bpos = block_excl_scan((nd << 16) | nb, L.sc.scan, &tot);
+      bpos &= 0xffff;
+      const int A = tot >> 16;
+      const int Mc = tot & 0xffff;
+      if (Mc > FBAND_CAP) return false;
+      for (int i = ca; i < ce; i++) {
+        const uint32_t kk = L.ckey[i];
+        if ((kk >= lo) && (kk <= hi)) {
+          L.band_n[bpos] = L.cidx[i];
+          L.band_k[bpos] = kk;
+          bpos++;
+        }
+      }
+      __syncthreads();
+      int M = Mc;
+      if (lo < lkey) {  // entries below L can still sit in the band
+        const int ext = gather_range(sb, N, L.gkey, L.qlist, G, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc);
+        if (ext < 0) return false;
+        M += ext;
+      }
+      const int rr = k - A;
+      if (rr < 1 || rr > M) {
+        report_violation(P, b, ids, mask);
+        return true;
+      }
+      // fp64 rescoring: each wave takes RS entries at a time
+      const float w_h = lane < P.H ? P.w[(size_t)b * P.H + lane] : 0.f;
+      for (int i0 = wid * RS; i0 < M; i0 += NWAVES * RS) {
+        float2 kp[RS];
+#pragma unroll
+        for (int c = 0; c < RS; c++) kp[c] = i0 + c < M ? key_pair(P, b, L.band_n[i0 + c]) : make_float2(0.f, 0.f);
+        double sc[RS];
+        rescore_multi<RS>(L.qP, kp, w_h, P.H, L.krow[wid], L.psum[wid], sc);
+        if (lane == 0)
+#pragma unroll
+          for (int c = 0; c < RS; c++)
+            if (i0 + c < M) L.band_s[i0 + c] = sc[c];
+      }
+      for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
+      __syncthreads();
+      for (int i = tid; i < M; i += TK_THREADS) {
+        const double si = L.band_s[i];
+        const int ni = L.band_n[i];
+        int rank = 0;
+        for (int j = 0; j < M; j++) {
+          const double sj = L.band_s[j];
+          rank += (sj > si) || (sj == si && L.band_n[j] < ni);
+        }
+        if (rank < rr) atomicOr(&sel[ni >> 5], 1u << (ni & 31));
+      }
+      for (int i = tid; i < M1; i += TK_THREADS)
+        if (L.ckey[i] > hi) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
+    }
+  }
+  __syncthreads();
+
+  // 6. bitmap -> ascending ids, mask, count
+  const int wseg = (W + TK_THREADS - 1) / TK_THREADS;
+  const int wa = min(W, tid * wseg), we = min(W, wa + wseg);
+  int c = 0;
+  for (int w = wa; w < we; w++) c += __popc(sel[w]);
+  int total;
+  int opos = block_excl_scan(c, L.sc.scan, &total);
+  for (int w = wa; w < we; w++) {
+    uint32_t bits = sel[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      ids[opos++] = w * 32 + bit;
+      bits &= bits - 1u;
+    }
+  }
+  if (mask)
+    for (int n = tid; n < N; n += TK_THREADS) mask[n] = (sel[n >> 5] >> (n & 31)) & 1u;
+  for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
+  if (tid == 0) P.count[b] = total;
+  return true;
+}
+
+// ---------------------------------------------------------------- full scan
+
+__device__ void full_path(const TopkParams& P, FullLds& L, int b) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int N = P.N, k = P.k;
   const float* sb = P.scores + (size_t)b * N;
   const bool in_lds = N <= LDS_KEYS;
@@ -91,7 +701,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   int32_t* g_band_n = P.ws_band_n + (size_t)b * N;
   uint8_t* g_band_sel = P.ws_band_sel + (size_t)b * N;
 
-  // 1. keys
   int nsel = 0;
   for (int i = tid; i < N; i += TK_THREADS) {
     const uint32_t kk = score_key(sb[i]);
@@ -105,54 +714,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   // Selection rule: key > def_key, or band_lo <= key <= band_hi and chosen.
   uint32_t def_key = 0u, band_lo = 1u, band_hi = 0u;  // empty band
   int r_eq = 0;
-  bool exact_band = false;
+  bool exact_band_on = false;
   if (total_sel > k) {
     const uint32_t T = radix_select<uint32_t>(key, N, k, &L.sc, &r_eq);
     if (!P.exact) {
       def_key = T;
       band_lo = band_hi = T;
     } else {
-      // 3. rounding bound
-      if (wid == 0) {
-        double wq = 0.0, wa = 0.0;
-        if (lane < P.H) {
-          const size_t qo = ((size_t)b * P.H + lane) * LIT_IDX_DIM;
-          double n2 = 0.0;
-          for (int d = 0; d < LIT_IDX_DIM; d++) {
-            const double x = (double)load_idx(P.q, P.dtype, qo + d);
-            n2 += x * x;
-          }
-          wa = fabs((double)P.w[(size_t)b * P.H + lane]);
-          wq = wa * sqrt(n2);
-        }
-        wq = wave_sum_f64(wq);
-        wa = wave_sum_f64(wa);
-        if (lane == 0) {
-          L.dmisc[0] = wq;
-          L.dmisc[1] = wa;
-        }
-      }
-      float km = 0.f;
-      for (int j = tid; j < P.nchunks; j += TK_THREADS) km = fmaxf(km, P.kmax[(size_t)b * P.nchunks + j]);
-      km = wave_max(km);
-      if (lane == 0) L.krow[0][wid] = km;
-      __syncthreads();
-      if (tid == 0) {
-        float m = 0.f;
-        for (int i = 0; i < TK_THREADS / 64; i++) m = fmaxf(m, L.krow[0][i]);
-        const double terms = (double)(LIT_IDX_DIM + P.H + 2);
-        const double delta = (ERR_SAFETY * 0x1p-24 * terms * L.dmisc[0] * (double)m +
-                              ERR_SAFETY * terms * 0x1p-126 * L.dmisc[1]) * (1.0 + 0x1p-20);
-        const double t = (double)key_score(T);
-        L.dmisc[2] = t - 2.0 * delta;
-        L.dmisc[3] = t + 2.0 * delta;
-      }
-      __syncthreads();
-      const uint32_t lo = score_key(__double2float_rd(L.dmisc[2]));
-      band_lo = lo > 1u ? lo : 1u;
-      band_hi = score_key(__double2float_ru(L.dmisc[3]));
+      exact_band(P, b, T, L.krow, L.dmisc, &band_lo, &band_hi);
       def_key = band_hi;
-      exact_band = true;
+      exact_band_on = true;
     }
   }
 
@@ -167,8 +738,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   };
 
   int M = 0;
-  if (exact_band) {
-    // gather the band in index order, count the sure ones
+  if (exact_band_on) {
     int A = 0;
     for (int c0 = 0; c0 < N; c0 += CH) {
       const int len = min(CH, N - c0);
@@ -193,40 +763,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
     }
     const int r = k - A;
     if (r < 1 || r > M) {
-      // The rounding bound was violated: report instead of guessing.
-      for (int j = tid; j < k; j += TK_THREADS) ids[j] = -1;
-      if (mask)
-        for (int i = tid; i < N; i += TK_THREADS) mask[i] = 0;
-      if (tid == 0) P.count[b] = -1;
+      report_violation(P, b, ids, mask);
       return;
     }
+    __threadfence();
     __syncthreads();
     const bool band_in_lds = M <= BAND_LDS;
     if (band_in_lds)
       for (int i = tid; i < M; i += TK_THREADS) L.band_n[i] = g_band_n[i];
-    // rescore in fp64, canonical order
-    for (int idx = tid; idx < LIT_IDX_DIM * 64; idx += TK_THREADS) {
-      const int d = idx >> 6, h = idx & 63;
-      L.qT[idx] = h < P.H ? load_idx(P.q, P.dtype, ((size_t)b * P.H + h) * LIT_IDX_DIM + d) : 0.f;
-    }
-    __syncthreads();
+    stage_qT(P, b, L.qT);
     const float w_h = lane < P.H ? P.w[(size_t)b * P.H + lane] : 0.f;
-    for (int i = wid; i < M; i += TK_THREADS / 64) {
+    for (int i = wid; i < M; i += NWAVES) {
       const int n = band_in_lds ? L.band_n[i] : g_band_n[i];
-      const size_t row = ((size_t)b * N + n) * LIT_IDX_DIM;
-      for (int d = lane; d < LIT_IDX_DIM; d += 64) L.krow[wid][d] = load_idx(P.kidx, P.dtype, row + d);
-      wave_sync();
-      const double s = exact_score_wave(L.qT, L.krow[wid], w_h, P.H);
+      const double s = rescore(P, b, n, L.qT, L.krow[wid], w_h);
       if (lane == 0) {
         if (band_in_lds)
           L.band_s[i] = s;
         else
           g_band_s[i] = s;
       }
-      wave_sync();
     }
+    __threadfence();
     __syncthreads();
-    // choose the best r of the band: (score desc, index asc); the band is in index order
+    // the band is in index order: position order is index order
     if (band_in_lds) {
       for (int i = tid; i < M; i += TK_THREADS) {
         const double si = L.band_s[i];
@@ -243,13 +802,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
       const uint64_t T64 = radix_select<uint64_t>(bkey, M, r, &L.sc, &req);
       mark_top<uint64_t>(bkey, M, T64, req, g_band_sel, &L.sc);
     }
+    __threadfence();
     __syncthreads();
   }
 
-  // 4. ordered compaction: ids ascending, mask, count
+  // ordered compaction: ids ascending, mask, count
   const bool band_in_lds = M <= BAND_LDS;
   auto chosen = [&](int pos) -> bool {
-    if (!exact_band) return pos < r_eq;
+    if (!exact_band_on) return pos < r_eq;
     return band_in_lds ? L.band_sel[pos] != 0 : g_band_sel[pos] != 0;
   };
   int out_base = 0, band_base = 0;
@@ -299,6 +859,16 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   if (tid == 0) P.count[b] = out_base;
 }
 
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int b = blockIdx.x;
+  if (P.hints && P.N <= GM_CAP * GROUP) {
+    if (fast_path(P, *reinterpret_cast<FastLds*>(smem), b)) return;
+    __syncthreads();
+  }
+  full_path(P, *reinterpret_cast<FullLds*>(smem), b);
+}
+
 }  // namespace
 }  // namespace lit
 
@@ -312,18 +882,18 @@ extern "C" size_t lit_topk_workspace_bytes(int32_t B, int32_t N, int32_t k) {
 }
 
 extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k, const lit_idx_in* exact,
-                                      const float* kmax, int32_t* ids, int32_t* count, uint8_t* mask, void* ws,
+                                      const float* hints, int32_t* ids, int32_t* count, uint8_t* mask, void* ws,
                                       size_t ws_bytes, void* stream) {
   clear_error();
   if (!scores || !ids || !count) return fail(LIT_ERR_NULL, "lit_topk_select: scores, ids and count must be non-NULL");
   if (B < 1 || N < 1 || k < 1) return fail(LIT_ERR_SHAPE, "lit_topk_select: B=%d N=%d k=%d must be >= 1", B, N, k);
   if (N > (1 << 24)) return fail(LIT_ERR_SHAPE, "lit_topk_select: N=%d above 2^24", N);
-  if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(count, 4))
-    return fail(LIT_ERR_ALIGN, "lit_topk_select: scores, ids and count must be 4-byte aligned");
+  if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(count, 4) || (hints && !aligned(hints, 4)))
+    return fail(LIT_ERR_ALIGN, "lit_topk_select: scores, hints, ids and count must be 4-byte aligned");
   if (exact) {
     lit_status st = check_idx_inputs(exact, B, N, "lit_topk_select(exact)");
     if (st != LIT_OK) return st;
-    if (!kmax) return fail(LIT_ERR_NULL, "lit_topk_select: exact mode needs the kmax side output of lit_idx_score");
+    if (!hints) return fail(LIT_ERR_NULL, "lit_topk_select: exact mode needs the hints side output of lit_idx_score");
   }
   const size_t need = lit_topk_workspace_bytes(B, N, k);
   if (!ws || ws_bytes < need)
@@ -341,7 +911,8 @@ extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N,
   P.kidx = exact ? exact->k : nullptr;
   P.dtype = exact ? (int)exact->dtype : 0;
   P.H = exact ? exact->H : 0;
-  P.kmax = kmax;
+  P.hints = hints;
+  P.hints_len = lit_idx_hints_len(N);
   P.nchunks = (int)cdiv(N, LIT_KNORM_CHUNK);
   P.ids = ids;
   P.count = count;
@@ -349,7 +920,7 @@ extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N,
   P.ws_band_s = (double*)w8;
   P.ws_band_n = (int32_t*)(w8 + round_up(per * sizeof(double), 256));
   P.ws_band_sel = w8 + round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256);
-  const size_t lds = sizeof(TopkLds);
+  const size_t lds = std::max(sizeof(FullLds), sizeof(FastLds));
   lit_status st = allow_lds((const void*)topk_kernel, lds, "lit_topk_select");
   if (st != LIT_OK) return st;
   topk_kernel<<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);

@@ -68,10 +68,10 @@ def test_topk_validation(L):
                              None) == 5
     assert L.lit_topk_select(p(0x4000), 2, 1000, 64, None, None, p(0x1000), p(0x2000), None, None, need, None) == 5
     d = _idx()
-    # exact mode without the kmax side output
+    # exact mode without the hints side output
     assert L.lit_topk_select(p(0x4000), 2, 1000, 64, ctypes.byref(d), None, p(0x1000), p(0x2000), None, p(0x3000),
                              need, None) == 1
-    assert "kmax" in lit.last_error()
+    assert "hints" in lit.last_error()
 
 
 def test_attention_validation(L):

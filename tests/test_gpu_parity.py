@@ -57,10 +57,10 @@ def assert_attn_close(out, ref, tol=ATTN_TOL):
 
 def run_select(inp, k, exact=True, allowed=None):
     q, w, kk = dev(inp.q_idx), dev(inp.w), dev(inp.k_idx)
-    scores, kmax = lit.idx_score(q, w, kk, dev(allowed))
-    ids, cnt, mask = lit.topk_select(scores, k, exact=(q, w, kk) if exact else None, kmax=kmax)
+    scores, hints = lit.idx_score(q, w, kk, dev(allowed))
+    ids, cnt, mask = lit.topk_select(scores, k, exact=(q, w, kk) if exact else None, hints=hints)
     torch.cuda.synchronize()
-    return scores, kmax, ids, cnt, mask
+    return scores, hints, ids, cnt, mask
 
 
 def oracle_select(inp, k, allowed=None):
@@ -95,8 +95,10 @@ SEL_CASES = [
     ("ragged_b2", W.CTX64K, 2, 5003, 512),
     ("k_above_n", W.CTX64K, 1, 300, 512),
     ("n_one", W.CTX64K, 1, 1, 1),
-    ("global_mode", W.CTX64K, 1, 40000, 512),
+    ("n40000", W.CTX64K, 1, 40000, 512),
     ("pro_k1024", W.CTX64K, 3, 16384, 1024),
+    ("ctx500k", W.CTX500K, 1, None, 512),
+    ("full_scan_140k", W.CTX64K, 1, 140000, 512),
 ]
 
 
@@ -104,27 +106,34 @@ SEL_CASES = [
 def test_score_and_exact_topk(name, wl, B, N, k):
     print(f"case {name}", flush=True)
     inp = W.layer_inputs(wl, 0, "cpu", B=B, N=N).idx
-    scores, kmax, ids, cnt, mask = run_select(inp, k)
+    scores, hints, ids, cnt, mask = run_select(inp, k)
     s64, rids, rcnt, rmask = oracle_select(inp, k)
     # fp32 scores within the bound of the fp64 ones; empirically far tighter
     err = np.abs(scores.double().cpu().numpy() - s64).max(-1)
     bound = score_bound(inp.q_idx, inp.w, inp.k_idx).numpy()
     assert (err <= bound).all(), f"score error {err} above bound {bound}"
     assert (err <= 1e-5 * np.abs(s64).max(-1) + 1e-30).all()
-    # kmax covers every chunk's largest key norm, tightly
+    # hints: key-norm chunk bounds cover every chunk's largest norm tightly, and
+    # the group maxima are exactly the maxima of the scores written
     norms = inp.k_idx.double().norm(dim=-1)
     Nn = norms.shape[1]
+    nch = -(-Nn // 256)
     pad = (-Nn) % 256
     cm = torch.nn.functional.pad(norms, (0, pad)).reshape(norms.shape[0], -1, 256).amax(-1).numpy()
-    km = kmax.double().cpu().numpy()
+    hn = hints.double().cpu()
+    km = hn[:, :nch].numpy()
     assert (km >= cm).all() and (km <= cm * (1 + 1e-4) + 1e-30).all()
+    sc = scores.cpu()
+    gpad = (-Nn) % 16
+    gref = torch.nn.functional.pad(sc, (0, gpad), value=float("-inf")).reshape(sc.shape[0], -1, 16).amax(-1)
+    assert torch.equal(hints.cpu()[:, nch:], gref)
     check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, name)
 
 
 def test_exact_grid_ties_bit_exact_scores_and_selection():
     g = torch.Generator().manual_seed(7)
     inp = synth.make_exact_grid(2, 4000, 8, g, "cpu")
-    scores, kmax, ids, cnt, mask = run_select(inp, 100)
+    scores, hints, ids, cnt, mask = run_select(inp, 100)
     s64, rids, rcnt, rmask = oracle_select(inp, 100)
     np.testing.assert_array_equal(scores.double().cpu().numpy(), s64)  # exact in any order
     check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, "exact_grid")
@@ -133,7 +142,7 @@ def test_exact_grid_ties_bit_exact_scores_and_selection():
 def test_all_zero_keys_select_first_k():
     inp = W.layer_inputs(W.CTX64K, 0, "cpu", B=1, N=2000).idx
     inp.k_idx.zero_()
-    scores, kmax, ids, cnt, mask = run_select(inp, 64)
+    scores, hints, ids, cnt, mask = run_select(inp, 64)
     assert (scores.cpu() == 0).all()
     assert ids.cpu()[0].tolist() == list(range(64)) and cnt.item() == 64
 
@@ -143,7 +152,7 @@ def test_gated_candidate_set():
     allowed = torch.zeros(2, 4000, dtype=torch.uint8)
     allowed[0, torch.randperm(4000, generator=torch.Generator().manual_seed(1))[:300]] = 1  # fewer than k
     allowed[1, torch.randperm(4000, generator=torch.Generator().manual_seed(2))[:2500]] = 1
-    scores, kmax, ids, cnt, mask = run_select(inp, 512, allowed=allowed)
+    scores, hints, ids, cnt, mask = run_select(inp, 512, allowed=allowed)
     s64, rids, rcnt, rmask = oracle_select(inp, 512, allowed.numpy())
     assert torch.isneginf(scores.cpu()[allowed == 0]).all()
     check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, "gated")
@@ -161,6 +170,18 @@ def test_topk_on_given_scores_with_heavy_ties():
         torch.cuda.synchronize()
         rids, rcnt, rmask = oracle.topk(s.double().numpy(), k)
         check_selection(ids, cnt, mask, rids, rcnt, rmask, None, f"given_scores N={N}")
+
+
+def test_topk_with_hints_on_fp32_order():
+    # without `exact` the fp32 scores define the order; the hinted path must agree
+    for B, N, k in ((2, 16384, 512), (1, 5000, 4000), (1, 125000, 1024)):
+        inp = W.layer_inputs(W.CTX64K, 3, "cpu", B=B, N=N).idx
+        q, w, kk = dev(inp.q_idx), dev(inp.w), dev(inp.k_idx)
+        scores, hints = lit.idx_score(q, w, kk)
+        ids, cnt, mask = lit.topk_select(scores, k, hints=hints)
+        torch.cuda.synchronize()
+        rids, rcnt, rmask = oracle.topk(scores.double().cpu().numpy(), k)
+        check_selection(ids, cnt, mask, rids, rcnt, rmask, None, f"fp32 order N={N} k={k}")
 
 
 def test_idx_score_exact_matches_oracle_bit_for_bit():
@@ -302,8 +323,8 @@ def test_lsa_gate_layers_or():
 def test_tiny_end_to_end_step():
     L = W.layer_inputs(W.TINY, 0, "cpu")
     q_idx, w, k_idx = dev(L.idx.q_idx), dev(L.idx.w), dev(L.idx.k_idx)
-    scores, kmax = lit.idx_score(q_idx, w, k_idx)
-    ids, cnt, mask = lit.topk_select(scores, 64, exact=(q_idx, w, k_idx), kmax=kmax)
+    scores, hints = lit.idx_score(q_idx, w, k_idx)
+    ids, cnt, mask = lit.topk_select(scores, 64, exact=(q_idx, w, k_idx), hints=hints)
     out, lse = lit.sparse_attn_decode(dev(L.q), kv_dev(L.kv), ids, cnt, 16, SCALE)
     gids, gcnt, gmask, _ = lit.golden_topk(dev(L.q), kv_dev(L.kv), 64, SCALE)
     inter, _, _ = lit.recall(mask, gmask)
