@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not supported "
@@ -201,6 +203,14 @@ def main():
     lit.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a copy of known size: its counter reading per byte scales the kernels' readings
+        src = torch.ones(512 << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = W.CTX64K_B
     scale = 1.0 / math.sqrt(512)
     print(f"[bench] generating {wl.name}: {wl.layers} layers x {wl.B} sequences x N={wl.N}", file=sys.stderr,

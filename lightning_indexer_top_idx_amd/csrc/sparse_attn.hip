@@ -29,7 +29,6 @@ namespace {
 constexpr int TILE = 32;
 constexpr int ROW_STRIDE = 520;  // bf16 per LDS row: 512 + 8 pad (spreads banks)
 constexpr int PART = 516;        // floats per partial: O[512], m, l, 2 pad
-constexpr int TARGET_WGS = 512;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -46,6 +45,7 @@ struct AttnParams {
   int k_cap, window;  // window already clamped to N
   float scale_log2;   // scale * log2(e)
   int splits, rows_per_split;
+  int B;
   float* out;
   float* lse;
   float* part;  // [B][splits][Hq][PART] when splits > 1
@@ -92,13 +92,122 @@ struct RowList {
   }
 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnParams P) {
-  __shared__ __align__(16) uint16_t tile[TILE * ROW_STRIDE];
-  __shared__ int rows[TILE];
-  __shared__ uint32_t dup[LIT_MAX_WINDOW / 32];
-  constexpr int NT = NW * 64;
-  const int b = blockIdx.x / P.splits, s = blockIdx.x % P.splits;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TR = 64;            // rows per tile: wave w scores rows 16w .. 16w+15
+constexpr int HG_HEADS = 16;      // query heads per workgroup
+constexpr int TARGET_WGS = 512;   // two workgroups per CU
+constexpr int DW = LIT_KV_DIM / 4;  // output dims owned by one wave
+
+struct AttnLds {
+  uint16_t tile[TR * ROW_STRIDE];      // gathered rows, row-major (BF16)
+  uint16_t pbuf[HG_HEADS * (TR + 8)];  // softmax weights P[head][row] (BF16)
+  int rows[2][TR];
+  uint32_t dup[LIT_MAX_WINDOW / 32];
+  float wmax[4][HG_HEADS];  // per-wave tile maxima
+  float wl[4][HG_HEADS];    // per-wave running sums
+};
+constexpr int PSTRIDE = TR + 8;
+
+// Row slices and head groups -> workgroups: the head groups of one slice get
+// workgroup ids equal modulo 8, i.e. the same XCD, so its L2 serves the rows
+// to all of them.
+__device__ __forceinline__ bool decode_unit(int X, int HG, int U, int* u, int* hg) {
+  const int per = 8 * HG;
+  const int blk = X / per, rem = X % per;
+  *hg = rem / 8;
+  *u = blk * 8 + rem % 8;
+  return *u < U;
+}
+
+// Register-staged gather of one 64-row tile: BF16 rows are 64 chunks of 16 B;
+// FP8 rows 28 chunks of 16 E4M3 bytes (dequantised on the store) + 8 chunks of
+// RoPE BF16.
+template <int KVT>
+struct TileRegs {
+  static constexpr int CHUNKS = KVT == 0 ? 64 : 36;
+  static constexpr int UNITS = TR * CHUNKS;
+  static constexpr int PER = (UNITS + 255) / 256;
+  u32x4 v[PER];
+  uint8_t sc[PER];
+};
+
+template <int KVT>
+__device__ __forceinline__ void tile_load(const AttnParams& P, size_t seq_rows, const int* rows, TileRegs<KVT>& R) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TileRegs<KVT>::PER; i++) {
+    const int u = tid + 256 * i;
+    const int r = u / TileRegs<KVT>::CHUNKS, ch = u % TileRegs<KVT>::CHUNKS;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    uint8_t sc = 127;
+    const int row = u < TileRegs<KVT>::UNITS ? rows[r] : -1;
+    if (row >= 0) {
+      const size_t rr = seq_rows + row;
+      if (KVT == 0) {
+        v = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)P.data + rr * LIT_KV_DIM + ch * 8));
+      } else if (ch < 28) {
+        v = __builtin_nontemporal_load((const u32x4*)(P.data + rr * LIT_KV_FP8_DIMS + ch * 16));
+        sc = P.scale[rr * LIT_KV_SCALE_STRIDE + (ch >> 2)];
+      } else {
+        v = __builtin_nontemporal_load((const u32x4*)(P.rope + rr * LIT_KV_ROPE_DIMS + (ch - 28) * 8));
+      }
+    }
+    R.v[i] = v;
+    R.sc[i] = sc;
+  }
+}
+
+template <int KVT>
+__device__ __forceinline__ void tile_store(uint16_t* tile, const TileRegs<KVT>& R) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < TileRegs<KVT>::PER; i++) {
+    const int u = tid + 256 * i;
+    if (u >= TileRegs<KVT>::UNITS) continue;
+    const int r = u / TileRegs<KVT>::CHUNKS, ch = u % TileRegs<KVT>::CHUNKS;
+    if (KVT == 0) {
+      *(u32x4*)(tile + r * ROW_STRIDE + ch * 8) = R.v[i];
+    } else if (ch < 28) {
+      const float sc = e8m0_f32(R.sc[i]);
+      u32x4 o0, o1;
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        const uint32_t wv = R.v[i][w];
+        const uint32_t h0 = e4m3_bf16(wv & 255u, sc), h1 = e4m3_bf16((wv >> 8) & 255u, sc);
+        const uint32_t h2 = e4m3_bf16((wv >> 16) & 255u, sc), h3 = e4m3_bf16(wv >> 24, sc);
+        if (w < 2) {
+          o0[2 * w] = h0 | (h1 << 16);
+          o0[2 * w + 1] = h2 | (h3 << 16);
+        } else {
+          o1[2 * (w - 2)] = h0 | (h1 << 16);
+          o1[2 * (w - 2) + 1] = h2 | (h3 << 16);
+        }
+      }
+      *(u32x4*)(tile + r * ROW_STRIDE + ch * 16) = o0;
+      *(u32x4*)(tile + r * ROW_STRIDE + ch * 16 + 8) = o1;
+    } else {
+      *(u32x4*)(tile + r * ROW_STRIDE + LIT_KV_FP8_DIMS + (ch - 28) * 8) = R.v[i];
+    }
+  }
+}
+
+// One workgroup: one sequence, one group of 16 query heads, one slice of the
+// row list. Per 64-row tile, wave w scores rows 16w..16w+15 for the 16 heads
+// (S^T = K Q^T on v_mfma_f32_16x16x32_bf16), the waves agree on each head's
+// running max through LDS, and each wave accumulates its own quarter of the
+// output dims, O[:, 128w .. 128w+127] += P V, over all 64 rows
+// (v_mfma_f32_16x16x16_bf16, P from LDS). The next tile is in flight in
+// registers during the math.
+template <int KVT>
+__global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  AttnLds& L = *reinterpret_cast<AttnLds*>(smem);
+  const int HG = (P.Hq + HG_HEADS - 1) / HG_HEADS;
+  const int U = P.B * P.splits;
+  int u, hg;
+  if (!decode_unit(blockIdx.x, HG, U, &u, &hg)) return;
+  const int b = u / P.splits, s = u % P.splits;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int Hq = P.Hq;
@@ -106,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnParams P) {
   RowList RL;
   RL.dense = P.ids == nullptr;
   RL.N = P.N;
-  RL.dup = dup;
+  RL.dup = L.dup;
   if (RL.dense) {
     RL.ids = nullptr;
     RL.c = 0;
@@ -123,18 +232,18 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnParams P) {
   const int p0 = s * P.rows_per_split;
   const int p1 = min(RL.total, p0 + P.rows_per_split);
   if (!RL.dense && p1 > RL.c && RL.Wc > 0) {
-    for (int i = tid; i < (RL.Wc + 31) / 32; i += NT) dup[i] = 0u;
+    for (int i = tid; i < (RL.Wc + 31) / 32; i += 256) L.dup[i] = 0u;
     __syncthreads();
     const int lo = P.N - RL.Wc;
-    for (int j = tid; j < RL.c; j += NT) {
+    for (int j = tid; j < RL.c; j += 256) {
       const int id = RL.ids[j];
-      if (id >= lo && id < P.N) atomicOr(&dup[(id - lo) >> 5], 1u << ((id - lo) & 31));
+      if (id >= lo && id < P.N) atomicOr(&L.dup[(id - lo) >> 5], 1u << ((id - lo) & 31));
     }
   }
   __syncthreads();
 
-  // This wave's 16 heads as B operands: K-step j, lane (c16 + 16 g) holds dims 8g + 32j .. +7.
-  const int head = wid * 16 + c16;
+  // the 16 heads as B operands of S^T = K Q^T: K-step j, lane (c16 + 16 g) holds dims 8g + 32j .. +7
+  const int head = hg * HG_HEADS + c16;
   u32x4 qreg[16];
   {
     const uint16_t* qh = P.q + ((size_t)b * Hq + head) * LIT_KV_DIM;
@@ -145,172 +254,133 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(AttnParams P) {
       qreg[j] = v;
     }
   }
-  f32x4 o[32];
+  // O[head 4g+i][dim 128 wid + 16 nt + c16]
+  f32x4 o[DW / 16];
 #pragma unroll
-  for (int nt = 0; nt < 32; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
+  for (int nt = 0; nt < DW / 16; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_col = -INFINITY;  // running max of head c16 (every wave holds the same)
+  float l_run = 0.f;        // this wave's share of head c16's sum (its rows, lane group g)
   const size_t seq_rows = (size_t)b * P.N;
-#pragma unroll 1
-  for (int t0 = p0; t0 < p1; t0 += TILE) {
-    if (tid < TILE) rows[tid] = (t0 + tid < p1) ? RL.row(t0 + tid) : -1;
-    __syncthreads();
-    // gather
-    if (P.kv_dtype == LIT_BF16) {
-      const uint16_t* base = (const uint16_t*)P.data;
-      for (int u = tid; u < TILE * 64; u += NT) {
-        const int r = u >> 6, ch = u & 63;
-        const int row = rows[r];
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row >= 0) v = *(const u32x4*)(base + (seq_rows + row) * LIT_KV_DIM + ch * 8);
-        *(u32x4*)(tile + r * ROW_STRIDE + ch * 8) = v;
-      }
-    } else {
-      // FP8: 28 chunks of 16 E4M3 bytes + 8 chunks of 8 BF16 RoPE dims per row
-      for (int u = tid; u < TILE * 36; u += NT) {
-        const int r = u / 36, ch = u % 36;
-        const int row = rows[r];
-        if (ch < 28) {
-          u32x4 out0 = {0u, 0u, 0u, 0u}, out1 = {0u, 0u, 0u, 0u};
-          if (row >= 0) {
-            const size_t rr = seq_rows + row;
-            const u32x4 v = *(const u32x4*)(P.data + rr * LIT_KV_FP8_DIMS + ch * 16);
-            const float sc = e8m0_f32(P.scale[rr * LIT_KV_SCALE_STRIDE + (ch >> 2)]);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const uint32_t wv = v[i];
-              const uint32_t h0 = e4m3_bf16(wv & 255u, sc), h1 = e4m3_bf16((wv >> 8) & 255u, sc);
-              const uint32_t h2 = e4m3_bf16((wv >> 16) & 255u, sc), h3 = e4m3_bf16(wv >> 24, sc);
-              if (i < 2) {
-                out0[2 * i] = h0 | (h1 << 16);
-                out0[2 * i + 1] = h2 | (h3 << 16);
-              } else {
-                out1[2 * (i - 2)] = h0 | (h1 << 16);
-                out1[2 * (i - 2) + 1] = h2 | (h3 << 16);
-              }
-            }
-          }
-          *(u32x4*)(tile + r * ROW_STRIDE + ch * 16) = out0;
-          *(u32x4*)(tile + r * ROW_STRIDE + ch * 16 + 8) = out1;
-        } else {
-          const int rc = ch - 28;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (row >= 0)
-            v = *(const u32x4*)(P.rope + (seq_rows + row) * LIT_KV_ROPE_DIMS + rc * 8);
-          *(u32x4*)(tile + r * ROW_STRIDE + LIT_KV_FP8_DIMS + rc * 8) = v;
-        }
-      }
-    }
-    __syncthreads();
 
-    // S^T = K Q^T : acc[t] holds rows 16t + 4g + i for head c16
-    f32x4 acc[2];
+  int cur = 0;
+  if (p0 < p1) {
+    if (tid < TR) L.rows[0][tid] = (p0 + tid < p1) ? RL.row(p0 + tid) : -1;
+    __syncthreads();
+    TileRegs<KVT> R;
+    tile_load<KVT>(P, seq_rows, L.rows[0], R);
+    tile_store<KVT>(L.tile, R);
+    __syncthreads();
+  }
+#pragma unroll 1
+  for (int t0 = p0; t0 < p1; t0 += TR) {
+    const int nxt = cur ^ 1;
+    const bool more = t0 + TR < p1;
+    if (more && tid < TR) L.rows[nxt][tid] = (t0 + TR + tid < p1) ? RL.row(t0 + TR + tid) : -1;
+    __syncthreads();
+    TileRegs<KVT> R;
+    if (more) tile_load<KVT>(P, seq_rows, L.rows[nxt], R);  // the next tile is in flight during the math
+
+    // S^T for this wave's 16 rows: lane (g, c16) gets rows 16w + 4g + i of head c16
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* krow = L.tile + (16 * wid + c16) * ROW_STRIDE + 8 * g;
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = tile + (16 * t + c16) * ROW_STRIDE + 8 * g;
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const u32x4 a = *(const u32x4*)(krow + 32 * j);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                         __builtin_bit_cast(bf16x8, qreg[j]), acc[t], 0, 0, 0);
+      for (int j = 0; j < 16; j += 2) {
+        const u32x4 a0 = *(const u32x4*)(krow + 32 * j), a1 = *(const u32x4*)(krow + 32 * (j + 1));
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, qreg[j]),
+                                                       acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                       __builtin_bit_cast(bf16x8, qreg[j + 1]), acc1, 0, 0, 0);
       }
     }
-    // online softmax (log2 domain)
-    float x[8];
+    float x[4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const bool valid = rows[16 * t + 4 * g + i] >= 0;
-        const float v = valid ? acc[t][i] * P.scale_log2 : -INFINITY;
-        x[4 * t + i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+    for (int i = 0; i < 4; i++) {
+      const bool valid = L.rows[cur][16 * wid + 4 * g + i] >= 0;
+      x[i] = valid ? (acc0[i] + acc1[i]) * P.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    if (g == 0) L.wmax[wid][c16] = tmax;
+    __syncthreads();
+    const float t_all = fmaxf(fmaxf(L.wmax[0][c16], L.wmax[1][c16]), fmaxf(L.wmax[2][c16], L.wmax[3][c16]));
+    const float m_new = fmaxf(m_col, t_all);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);  // m_run = -inf gives 0
+    const float alpha = exp2f(m_col - m_use);  // head c16
+    m_col = m_new;
     float psum = 0.f;
-    uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const float p0v = exp2f(x[i] - m_use), p1v = exp2f(x[4 + i] - m_use);
-      psum += p0v + p1v;
-      x[i] = p0v;
-      x[4 + i] = p1v;
-    }
-    // pack P as the A operand: element kk -> row kk<4 ? 4g+kk : 16+4g+kk-4
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint32_t lo = __float_as_uint(x[2 * i]), hi = __float_as_uint(x[2 * i + 1]);
-      // round to nearest even into bf16
-      const uint32_t lo16 = (lo + 0x7fffu + ((lo >> 16) & 1u)) >> 16;
-      const uint32_t hi16 = (hi + 0x7fffu + ((hi >> 16) & 1u)) >> 16;
-      pk[i] = lo16 | (hi16 << 16);
+      const float pv = exp2f(x[i] - m_use);
+      psum += pv;
+      const uint32_t bits = __float_as_uint(pv);
+      L.pbuf[c16 * PSTRIDE + 16 * wid + 4 * g + i] = (uint16_t)((bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16);
     }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rescale O: O rows are heads 4g+i; their alpha lives in lane 4g+i
-    float al[4];
+    __syncthreads();
+    // rescale this wave's O rows (heads 4g+i) when some running max moved
+    if (__any(alpha != 1.0f)) {
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) al[i] = __shfl(alpha, 4 * g + i);
+      for (int i = 0; i < 4; i++) al[i] = __shfl(alpha, 4 * g + i);
 #pragma unroll
-    for (int nt = 0; nt < 32; nt++)
+      for (int nt = 0; nt < DW / 16; nt++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) o[nt][i] *= al[i];
-    const u32x4 pa = {pk[0], pk[1], pk[2], pk[3]};
-    const bf16x8 pa8 = __builtin_bit_cast(bf16x8, pa);
-    // O += P V : B operand lane (c16 + 16g) = V[rows 4g..4g+3, 16+4g..16+4g+3][16 nt + c16]
-    const uint16_t* v0 = tile + (4 * g) * ROW_STRIDE + c16;
-    const uint16_t* v1 = tile + (16 + 4 * g) * ROW_STRIDE + c16;
-#pragma unroll
-    for (int nt = 0; nt < 32; nt++) {
-      const int d = 16 * nt;
-      u32x4 vb;
-      vb[0] = (uint32_t)v0[d] | ((uint32_t)v0[ROW_STRIDE + d] << 16);
-      vb[1] = (uint32_t)v0[2 * ROW_STRIDE + d] | ((uint32_t)v0[3 * ROW_STRIDE + d] << 16);
-      vb[2] = (uint32_t)v1[d] | ((uint32_t)v1[ROW_STRIDE + d] << 16);
-      vb[3] = (uint32_t)v1[2 * ROW_STRIDE + d] | ((uint32_t)v1[3 * ROW_STRIDE + d] << 16);
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa8, __builtin_bit_cast(bf16x8, vb), o[nt], 0, 0, 0);
+        for (int i = 0; i < 4; i++) o[nt][i] *= al[i];
     }
+    // O[:, dims of wave w] += P[16 x 64] V[64 x 128]: A = P (head c16, rows 16kb + 4g .. +3)
+#pragma unroll
+    for (int kb = 0; kb < TR / 16; kb++) {
+      const s16x4 pa = *(const s16x4*)(L.pbuf + c16 * PSTRIDE + 16 * kb + 4 * g);
+      const uint16_t* vr = L.tile + (16 * kb + 4 * g) * ROW_STRIDE + DW * wid + c16;
+#pragma unroll
+      for (int nt = 0; nt < DW / 16; nt++) {
+        const int d = 16 * nt;
+        u32x2 vb;
+        vb[0] = (uint32_t)vr[d] | ((uint32_t)vr[ROW_STRIDE + d] << 16);
+        vb[1] = (uint32_t)vr[2 * ROW_STRIDE + d] | ((uint32_t)vr[3 * ROW_STRIDE + d] << 16);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), o[nt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (more) tile_store<KVT>(L.tile, R);
+    cur = nxt;
     __syncthreads();
   }
 
-  // finish: l per head (column c16) summed over the four row groups
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  float lh[4], mh[4];
+  // l per head: the four lane groups of every wave
+  float l_w = l_run;
+  l_w += __shfl_xor(l_w, 16);
+  l_w += __shfl_xor(l_w, 32);
+  if (g == 0) L.wl[wid][c16] = l_w;
+  __syncthreads();
+  float Ls[4], Ms[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    lh[i] = __shfl(l_tot, 4 * g + i);
-    mh[i] = __shfl(m_run, 4 * g + i);
+    const int hh = 4 * g + i;
+    Ls[i] = (L.wl[0][hh] + L.wl[1][hh]) + (L.wl[2][hh] + L.wl[3][hh]);
+    Ms[i] = __shfl(m_col, hh);
   }
-  if (P.splits == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int h = wid * 16 + 4 * g + i;
-      if (h >= Hq) continue;
-      float* oh = P.out + ((size_t)b * Hq + h) * LIT_KV_DIM;
-      const float inv = lh[i] > 0.f ? 1.f / lh[i] : 0.f;
+  for (int i = 0; i < 4; i++) {
+    const int h = hg * HG_HEADS + 4 * g + i;
+    if (h >= Hq) continue;
+    if (P.splits == 1) {
+      float* oh = P.out + ((size_t)b * Hq + h) * LIT_KV_DIM + DW * wid;
+      const float inv = Ls[i] > 0.f ? 1.f / Ls[i] : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < 32; nt++) oh[16 * nt + c16] = o[nt][i] * inv;
-      if (P.lse && c16 == 0) P.lse[(size_t)b * Hq + h] = lh[i] > 0.f ? mh[i] * LN2 + logf(lh[i]) : -INFINITY;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int h = wid * 16 + 4 * g + i;
-      if (h >= Hq) continue;
+      for (int nt = 0; nt < DW / 16; nt++) oh[16 * nt + c16] = o[nt][i] * inv;
+      if (P.lse && wid == 0 && c16 == 0)
+        P.lse[(size_t)b * Hq + h] = Ls[i] > 0.f ? Ms[i] * LN2 + logf(Ls[i]) : -INFINITY;
+    } else {
       float* ph = P.part + (((size_t)b * P.splits + s) * Hq + h) * PART;
 #pragma unroll
-      for (int nt = 0; nt < 32; nt++) ph[16 * nt + c16] = o[nt][i];
-      if (c16 == 0) {
-        ph[512] = mh[i];
-        ph[513] = lh[i];
+      for (int nt = 0; nt < DW / 16; nt++) ph[DW * wid + 16 * nt + c16] = o[nt][i];
+      if (wid == 0 && c16 == 0) {
+        ph[512] = Ms[i];
+        ph[513] = Ls[i];
       }
     }
   }
@@ -423,14 +493,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   if (lse && tid == 0) lse[(size_t)b * Hq + h] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-void plan_splits(int B, int rows_max, int* splits, int* rows_per_split) {
-  const int tiles = std::max(1, (rows_max + TILE - 1) / TILE);
-  const int want = std::max(1, (TARGET_WGS + B - 1) / B);
+void plan_splits(int B, int HG, int rows_max, int* splits, int* rows_per_split) {
+  const int tiles = std::max(1, (rows_max + TR - 1) / TR);
+  const int want = std::max(1, (TARGET_WGS + B * HG - 1) / (B * HG));
   int s = std::min(tiles, want);
   const int tiles_per = (tiles + s - 1) / s;
   s = (tiles + tiles_per - 1) / tiles_per;
   *splits = s;
-  *rows_per_split = tiles_per * TILE;
+  *rows_per_split = tiles_per * TR;
 }
 
 }  // namespace
@@ -441,7 +511,7 @@ using namespace lit;
 extern "C" size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
   int s, rps;
-  plan_splits(B, N + LIT_MAX_WINDOW, &s, &rps);
+  plan_splits(B, (Hq + HG_HEADS - 1) / HG_HEADS, N + LIT_MAX_WINDOW, &s, &rps);
   if (s <= 1) return 256;
   return round_up((size_t)B * s * Hq * PART * sizeof(float), 256);
 }
@@ -484,7 +554,9 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   }
   const int rows_max = ids ? (k_cap + Wc) : N;
   AttnParams P;
-  plan_splits(B, rows_max, &P.splits, &P.rows_per_split);
+  const int HG = (Hq + HG_HEADS - 1) / HG_HEADS;
+  plan_splits(B, HG, rows_max, &P.splits, &P.rows_per_split);
+  P.B = B;
   if (P.splits > 1) {
     const size_t need = round_up((size_t)B * P.splits * Hq * PART * sizeof(float), 256);
     if (!ws || ws_bytes < need)
@@ -506,13 +578,17 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   P.out = out;
   P.lse = lse;
   P.part = (float*)ws;
-  const int nw = (Hq + 15) / 16;
-  dim3 grid((unsigned)(B * P.splits));
-  switch (nw) {
-    case 1: attn_mfma_kernel<1><<<grid, 64, 0, st>>>(P); break;
-    case 2: attn_mfma_kernel<2><<<grid, 128, 0, st>>>(P); break;
-    case 3: attn_mfma_kernel<3><<<grid, 192, 0, st>>>(P); break;
-    default: attn_mfma_kernel<4><<<grid, 256, 0, st>>>(P); break;
+  const int U = B * P.splits;
+  dim3 grid((unsigned)(((U + 7) / 8) * 8 * HG));
+  const size_t lds = sizeof(AttnLds);
+  if (kv->dtype == LIT_BF16) {
+    lit_status ls = allow_lds((const void*)attn_hg_kernel<0>, lds, who);
+    if (ls != LIT_OK) return ls;
+    attn_hg_kernel<0><<<grid, 256, lds, st>>>(P);
+  } else {
+    lit_status ls = allow_lds((const void*)attn_hg_kernel<1>, lds, who);
+    if (ls != LIT_OK) return ls;
+    attn_hg_kernel<1><<<grid, 256, lds, st>>>(P);
   }
   LIT_CHECK_LAUNCH(who);
   if (P.splits > 1) {
