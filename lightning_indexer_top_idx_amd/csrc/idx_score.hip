@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
     qlds[(mt * 4 + j) * 64 + hh + 16 * gg] = v;
   }
   if (tid < 64) wlds[tid] = tid < H ? w[(size_t)b * H + tid] : 0.f;
-  __syncthreads();
+  lds_barrier();
   float wr[MT][4];
   load_lane_weights<MT>(wlds, wr);
 

@@ -58,6 +58,12 @@ __device__ __forceinline__ uint64_t score_key64(double d) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS
+// operations (lgkmcnt) but not for outstanding global loads, so prefetches
+// stay in flight across it. (__syncthreads also drains vmcnt.) Use it only
+// where no thread reads global memory written by another thread of the block.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Wave-level reductions over all 64 lanes.
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -93,14 +99,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int inc = wave_incl_scan(v);
   if (lane == 63) tmp[wid] = inc;
-  __syncthreads();
+  lds_barrier();
   if (wid == 0) {
     int t = lane < nw ? tmp[lane] : 0;
     int ti = wave_incl_scan(t);
     if (lane < nw) tmp[lane] = ti - t;
     if (lane == nw - 1) tmp[nw] = ti;
   }
-  __syncthreads();
+  lds_barrier();
   int r = tmp[wid] + inc - v;
   *total = tmp[nw];
   return r;

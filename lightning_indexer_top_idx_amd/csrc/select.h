@@ -29,12 +29,12 @@ __device__ KeyT radix_select(KeyFn key, int M, int r, SelectScratch* sc, int* r_
 #pragma unroll 1
   for (int shift = BITS - 8; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += nthr) sc->hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < M; i += nthr) {
       const KeyT kk = key(i);
       if ((kk & pmask) == prefix) atomicAdd(&sc->hist[(uint32_t)(kk >> shift) & 255u], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     if (wid == 0) {
       int c[4];
 #pragma unroll
@@ -54,11 +54,11 @@ __device__ KeyT radix_select(KeyFn key, int M, int r, SelectScratch* sc, int* r_
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     prefix |= (KeyT)sc->misc[0] << shift;
     pmask |= (KeyT)255 << shift;
     r = sc->misc[1];
-    __syncthreads();
+    lds_barrier();
   }
   *r_eq = r;
   return prefix;
@@ -87,7 +87,7 @@ __device__ void mark_top(KeyFn key, int M, KeyT T, int r_eq, uint8_t* sel, Selec
     }
     sel[i] = s;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Writes ids (ascending, tail -1 up to k), count and the optional mask of one

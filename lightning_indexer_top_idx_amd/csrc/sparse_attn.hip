@@ -233,14 +233,14 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
   const int p1 = min(RL.total, p0 + P.rows_per_split);
   if (!RL.dense && p1 > RL.c && RL.Wc > 0) {
     for (int i = tid; i < (RL.Wc + 31) / 32; i += 256) L.dup[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     const int lo = P.N - RL.Wc;
     for (int j = tid; j < RL.c; j += 256) {
       const int id = RL.ids[j];
       if (id >= lo && id < P.N) atomicOr(&L.dup[(id - lo) >> 5], 1u << ((id - lo) & 31));
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // the 16 heads as B operands of S^T = K Q^T: K-step j, lane (c16 + 16 g) holds dims 8g + 32j .. +7
   const int head = hg * HG_HEADS + c16;
@@ -265,18 +265,18 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
   int cur = 0;
   if (p0 < p1) {
     if (tid < TR) L.rows[0][tid] = (p0 + tid < p1) ? RL.row(p0 + tid) : -1;
-    __syncthreads();
+    lds_barrier();
     TileRegs<KVT> R;
     tile_load<KVT>(P, seq_rows, L.rows[0], R);
     tile_store<KVT>(L.tile, R);
-    __syncthreads();
+    lds_barrier();
   }
 #pragma unroll 1
   for (int t0 = p0; t0 < p1; t0 += TR) {
     const int nxt = cur ^ 1;
     const bool more = t0 + TR < p1;
     if (more && tid < TR) L.rows[nxt][tid] = (t0 + TR + tid < p1) ? RL.row(t0 + TR + tid) : -1;
-    __syncthreads();
+    lds_barrier();
     TileRegs<KVT> R;
     if (more) tile_load<KVT>(P, seq_rows, L.rows[nxt], R);  // the next tile is in flight during the math
 
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     if (g == 0) L.wmax[wid][c16] = tmax;
-    __syncthreads();
+    lds_barrier();
     const float t_all = fmaxf(fmaxf(L.wmax[0][c16], L.wmax[1][c16]), fmaxf(L.wmax[2][c16], L.wmax[3][c16]));
     const float m_new = fmaxf(m_col, t_all);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
       L.pbuf[c16 * PSTRIDE + 16 * wid + 4 * g + i] = (uint16_t)((bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16);
     }
     l_run = l_run * alpha + psum;
-    __syncthreads();
+    lds_barrier();
     // rescale this wave's O rows (heads 4g+i) when some running max moved
     if (__any(alpha != 1.0f)) {
       float al[4];
@@ -344,10 +344,10 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), o[nt], 0, 0, 0);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (more) tile_store<KVT>(L.tile, R);
     cur = nxt;
-    __syncthreads();
+    lds_barrier();
   }
 
   // l per head: the four lane groups of every wave
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
   l_w += __shfl_xor(l_w, 16);
   l_w += __shfl_xor(l_w, 32);
   if (g == 0) L.wl[wid][c16] = l_w;
-  __syncthreads();
+  lds_barrier();
   float Ls[4], Ms[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {

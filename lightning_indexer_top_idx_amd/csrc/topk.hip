@@ -211,14 +211,14 @@ __device__ __forceinline__ void block_sum_min_max(int& s, uint32_t& mn, uint32_t
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
     fm = fmaxf(fm, __shfl_xor(fm, o));
   }
-  __syncthreads();
+  lds_barrier();
   if (lane == 0) {
     sc->scan[wid] = s;
     sc->hist[wid] = mn;
     sc->hist[16 + wid] = mx;
     sc->hist[32 + wid] = __float_as_uint(fm);
   }
-  __syncthreads();
+  lds_barrier();
   s = 0;
   mn = 0xffffffffu;
   mx = 0u;
@@ -229,7 +229,7 @@ __device__ __forceinline__ void block_sum_min_max(int& s, uint32_t& mn, uint32_t
     mx = max(mx, sc->hist[16 + i]);
     fm = fmaxf(fm, __uint_as_float(sc->hist[32 + i]));
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // One 2048-bin histogram pass over the non-zero keys in [kmin, kmax] (the bins
@@ -245,12 +245,12 @@ __device__ uint32_t hist_kth(KeyFn key, int M, int r, uint32_t kmin, uint32_t km
   const int shift = hb > 10 ? hb - 10 : 0;
   const uint32_t prefix = kmax & ~((2u << hb) - 1u);
   for (int i = tid; i < 2048; i += TK_THREADS) hist2k[i] = 0u;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < M; i += TK_THREADS) {
     const uint32_t kk = key(i);
     if (kk != 0u) atomicAdd(&hist2k[(kk - prefix) >> shift], 1u);
   }
-  __syncthreads();
+  lds_barrier();
   // cumulative counts from the top bin down: thread t owns bins 2047-2t, 2046-2t
   const int c0 = (int)hist2k[2047 - 2 * tid], c1 = (int)hist2k[2046 - 2 * tid];
   int tot;
@@ -264,13 +264,13 @@ __device__ uint32_t hist_kth(KeyFn key, int M, int r, uint32_t kmin, uint32_t km
     sc->misc[1] = ab + c0;
     sc->misc[2] = c1;
   }
-  __syncthreads();
+  lds_barrier();
   const int bin = sc->misc[0];
   *above = sc->misc[1];
   *in_bin = sc->misc[2];
   *prefix_out = prefix;
   *shift_out = shift;
-  __syncthreads();
+  lds_barrier();
   return prefix + ((uint32_t)bin << shift);
 }
 
@@ -311,7 +311,7 @@ __device__ int gather_range(const float* sb, int N, const uint32_t* gkey, uint16
   int qp = block_excl_scan(nq, sc->scan, &Q);
   for (int g = ga; g < ge; g++)
     if (gkey[g] >= lo) qlist[qp++] = (uint16_t)g;
-  __syncthreads();
+  lds_barrier();
   // 2. count per contiguous run of list positions; the first group stays in registers
   const int qseg = (Q + TK_THREADS - 1) / TK_THREADS;
   const int qa = min(Q, tid * qseg), qe = min(Q, qa + qseg);
@@ -353,7 +353,37 @@ __device__ int gather_range(const float* sb, int N, const uint32_t* gkey, uint16
         p++;
       }
   }
-  __syncthreads();
+  lds_barrier();
+  return total;
+}
+
+// Same as gather_range when every group is held in a thread's registers
+// (thread t owns group t, N <= 16 * blockDim): no memory access at all.
+__device__ int gather_small(const float (&sv)[GROUP], int G, const uint32_t* gkey, uint32_t lo, uint32_t hi,
+                            uint32_t* out_key, int32_t* out_idx, int base, int cap, SelectScratch* sc) {
+  const int tid = threadIdx.x;
+  const bool mine = tid < G && gkey[tid] >= lo;
+  int c = 0;
+  if (mine)
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) {
+      const uint32_t kk = score_key(sv[i]);
+      c += (kk >= lo) && (kk < hi) && (kk != 0u);
+    }
+  int total;
+  int p = base + block_excl_scan(c, sc->scan, &total);
+  if (base + total > cap) return -1;
+  if (mine)
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) {
+      const uint32_t kk = score_key(sv[i]);
+      if ((kk >= lo) && (kk < hi) && (kk != 0u)) {
+        out_key[p] = kk;
+        out_idx[p] = GROUP * tid + i;
+        p++;
+      }
+    }
+  lds_barrier();
   return total;
 }
 
@@ -442,6 +472,29 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
   const int G = (N + GROUP - 1) / GROUP;
   const int W = (N + 31) / 32;
+  // N <= 16 * 1024: thread t keeps the scores of group t in registers, loaded
+  // up front together with q and the key-norm hints (one round trip)
+  const bool small = G <= TK_THREADS;
+  float sv[GROUP];
+  if (small) {
+    const int e0 = GROUP * tid;
+    if (tid < G && e0 + GROUP <= N && (reinterpret_cast<uintptr_t>(sb) & 15u) == 0) {
+#pragma unroll
+      for (int c = 0; c < GROUP / 4; c++) {
+        const f32x4 x = *(const f32x4*)(sb + e0 + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 4; i++) sv[4 * c + i] = x[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < GROUP; i++) sv[i] = (tid < G && e0 + i < N) ? sb[e0 + i] : -INFINITY;
+    }
+  }
+
+  // the largest key-norm bound (exact mode), also loaded up front
+  float knorm = 0.f;
+  if (P.exact)
+    for (int j = tid; j < P.nchunks; j += TK_THREADS) knorm = fmaxf(knorm, P.hints[(size_t)b * P.hints_len + j]);
 
   // 0. exact mode: q rows (fp32) and |w_h| |q_h|, one 8-dim piece per thread
   if (P.exact) {
@@ -486,18 +539,29 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   // 1. group keys (+ the largest key-norm bound in exact mode)
   int ns = 0;
   uint32_t kmin = 0xffffffffu, kmx = 0u;
-  float knorm = 0.f;
-  for (int g = tid; g < G; g += TK_THREADS) {
-    const uint32_t kk = score_key(gmx[g]);
-    L.gkey[g] = kk;
-    if (kk) {
-      ns++;
-      kmin = min(kmin, kk);
-      kmx = max(kmx, kk);
+  if (small) {
+    if (tid < G) {
+      uint32_t kk = 0u;
+#pragma unroll
+      for (int i = 0; i < GROUP; i++) kk = max(kk, score_key(sv[i]));
+      L.gkey[tid] = kk;
+      if (kk) {
+        ns++;
+        kmin = kk;
+        kmx = kk;
+      }
+    }
+  } else {
+    for (int g = tid; g < G; g += TK_THREADS) {
+      const uint32_t kk = score_key(gmx[g]);
+      L.gkey[g] = kk;
+      if (kk) {
+        ns++;
+        kmin = min(kmin, kk);
+        kmx = max(kmx, kk);
+      }
     }
   }
-  if (P.exact)
-    for (int j = tid; j < P.nchunks; j += TK_THREADS) knorm = fmaxf(knorm, P.hints[(size_t)b * P.hints_len + j]);
   block_sum_min_max(ns, kmin, kmx, knorm, &L.sc);
   if (ns == 0) {
     for (int j = tid; j < k; j += TK_THREADS) ids[j] = -1;
@@ -517,14 +581,15 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   }
 
   // 3. candidates >= L in index order
-  const int M1 = gather_range(sb, N, L.gkey, L.qlist, G, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc);
+  const int M1 = small ? gather_small(sv, G, L.gkey, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc)
+                       : gather_range(sb, N, L.gkey, L.qlist, G, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc);
   if (M1 < 0) return false;
   // (a key of 0xffffffff would be a NaN pattern: score_key maps NaN to 0)
 
   uint32_t* sel = L.sel;  // aliases gkey: cleared once gkey is no longer read
   if (M1 <= k) {
     for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < M1; i += TK_THREADS) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
   } else {
     // 4. the k-th candidate: histogram bin, then exact ranks inside the bin
@@ -556,7 +621,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         L.cflag[i] = 0;
         if (((L.ckey[i] - prefix) >> shift) == bin_id) L.binpos[bp++] = (uint16_t)i;
       }
-      __syncthreads();
+      lds_barrier();
       for (int t = tid; t < m; t += TK_THREADS) {
         const int i = L.binpos[t];
         const uint32_t ki = L.ckey[i];
@@ -571,11 +636,11 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         if (rank == r - 1) L.sc.misc[4] = (int)ki;
       }
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t T = (uint32_t)L.sc.misc[4];
     if (!P.exact) {
       for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < M1; i += TK_THREADS) {
         const uint32_t ki = L.ckey[i];
         const uint32_t bi = (ki - prefix) >> shift;
@@ -596,7 +661,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         L.dmisc[2] = t - 2.0 * delta;
         L.dmisc[3] = t + 2.0 * delta;
       }
-      __syncthreads();
+      lds_barrier();
       const uint32_t lo0 = score_key(__double2float_rd(L.dmisc[2]));
       const uint32_t lo = lo0 > 1u ? lo0 : 1u;
       const uint32_t hi = score_key(__double2float_ru(L.dmisc[3]));
@@ -623,10 +688,11 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
           bpos++;
         }
       }
-      __syncthreads();
+      lds_barrier();
       int M = Mc;
       if (lo < lkey) {  // entries below L can still sit in the band
-        const int ext = gather_range(sb, N, L.gkey, L.qlist, G, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc);
+        const int ext = small ? gather_small(sv, G, L.gkey, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc)
+                              : gather_range(sb, N, L.gkey, L.qlist, G, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc);
         if (ext < 0) return false;
         M += ext;
       }
@@ -649,7 +715,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
             if (i0 + c < M) L.band_s[i0 + c] = sc[c];
       }
       for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < M; i += TK_THREADS) {
         const double si = L.band_s[i];
         const int ni = L.band_n[i];
@@ -664,7 +730,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         if (L.ckey[i] > hi) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // 6. bitmap -> ascending ids, mask, count
   const int wseg = (W + TK_THREADS - 1) / TK_THREADS;
