@@ -39,13 +39,17 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// Order-preserving 32-bit key of an fp32 score: larger score -> larger key.
-// -inf and NaN map to 0, the "never selected" key; every finite score and
-// +inf map above 0.
+// Order-preserving 32-bit key of an fp32 score: larger score -> larger key,
+// equal scores -> equal keys. -inf and NaN map to 0, the "never selected" key;
+// every finite score and +inf map above 0.
 __device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f != f || u == 0xff800000u) return 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // -0.0 becomes +0.0 first (the two compare equal); then every bit of a
+  // negative value is flipped, only the sign bit of a positive one; keys below
+  // that of -FLT_MAX (-inf, negative NaNs) or above that of +inf (positive
+  // NaNs) become 0. Branch-free: one add, one compare and one select.
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return key - 0x00800000u <= 0xff800000u - 0x00800000u ? key : 0u;
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -53,7 +57,7 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 }
 // Same for fp64 values.
 __device__ __forceinline__ uint64_t score_key64(double d) {
-  uint64_t u = (uint64_t)__double_as_longlong(d);
+  uint64_t u = (uint64_t)__double_as_longlong(d + 0.0);  // -0.0 -> +0.0
   if (d != d || u == 0xfff0000000000000ull) return 0ull;
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
@@ -90,6 +94,101 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     if (lane >= o) v += t;
   }
   return v;
+}
+
+// ---- wave primitives on DPP lane moves (VALU only, no LDS round trip).
+// GFX9 DPP controls: row_shr:n = 0x110 + n, row_bcast:15 = 0x142 (lane 15 of
+// each row into the next row), row_bcast:31 = 0x143 (lane 31 into rows 2, 3).
+// A lane whose source lies outside its row, or whose row is masked off,
+// receives `old`, the identity of the operation.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ double dpp_f64(double v) {  // identity +0.0
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL, ROWS>(0u, (uint32_t)u), hi = dpp_u32<CTRL, ROWS>(0u, (uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele inside each row of 16,
+// then the row totals carried up by the two broadcasts).
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += (int)dpp_u32<0x111>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x112>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x114>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x118>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x142, 0xa>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x143, 0xc>(0u, (uint32_t)v);
+  return v;
+}
+// Wave totals (the scan's last lane, read back as a wave-uniform value).
+__device__ __forceinline__ int wave_sum_dpp(int v) { return __builtin_amdgcn_readlane(wave_incl_scan_dpp(v), 63); }
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {  // identity 0
+  v = max(v, dpp_u32<0x111>(0u, v));
+  v = max(v, dpp_u32<0x112>(0u, v));
+  v = max(v, dpp_u32<0x114>(0u, v));
+  v = max(v, dpp_u32<0x118>(0u, v));
+  v = max(v, dpp_u32<0x142, 0xa>(0u, v));
+  v = max(v, dpp_u32<0x143, 0xc>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {  // identity ~0
+  v = min(v, dpp_u32<0x111>(~0u, v));
+  v = min(v, dpp_u32<0x112>(~0u, v));
+  v = min(v, dpp_u32<0x114>(~0u, v));
+  v = min(v, dpp_u32<0x118>(~0u, v));
+  v = min(v, dpp_u32<0x142, 0xa>(~0u, v));
+  v = min(v, dpp_u32<0x143, 0xc>(~0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_f64<0x111>(v);
+  v += dpp_f64<0x112>(v);
+  v += dpp_f64<0x114>(v);
+  v += dpp_f64<0x118>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  v += dpp_f64<0x143, 0xc>(v);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Lane l's value of a double, wave-uniform.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum inside each row of 16 lanes.
+__device__ __forceinline__ int row_incl_scan_dpp(int v) {
+  v += (int)dpp_u32<0x111>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x112>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x114>(0u, (uint32_t)v);
+  v += (int)dpp_u32<0x118>(0u, (uint32_t)v);
+  return v;
+}
+
+// Exclusive prefix sum over a block of up to 16 waves in thread order, with
+// one barrier: every wave posts its total to part[wid] (part[] is LDS that no
+// other scan may reuse before a later barrier); then each wave scans the posted
+// totals in one row of lanes and reads off its own offset. *total receives the
+// block total.
+template <int NW>
+__device__ __forceinline__ int block_excl_scan1(int v, int* part, int* total) {
+  static_assert(NW >= 1 && NW <= 16, "one row of lanes scans the wave totals");
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int inc = wave_incl_scan_dpp(v);
+  if (lane == 63) part[wid] = inc;
+  lds_barrier();
+  const int ps = row_incl_scan_dpp((lane & 15) < NW ? part[lane & 15] : 0);
+  *total = __builtin_amdgcn_readlane(ps, NW - 1);
+  const int before = __builtin_amdgcn_readlane(ps, wid > 0 ? wid - 1 : 0);
+  return (wid > 0 ? before : 0) + inc - v;
 }
 
 // Exclusive prefix sum over the whole block in thread order. `tmp` holds at

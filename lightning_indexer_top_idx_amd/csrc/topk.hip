@@ -7,8 +7,9 @@
 // ids to the attention kernel. The pages build that mask on the host; here it
 // never leaves the device. Ties go to the lower index.
 //
-// One workgroup (1024 threads) per sequence. Fast path (with the hints of
-// lit_idx_score, N <= 131072):
+// One workgroup (1024 threads) per sequence. Up to 16384 entries a kernel of
+// its own keeps every score in registers (see the small path below). Fast path
+// (with the hints of lit_idx_score, 16384 < N <= 131072):
 //   1. the k-th largest of the per-16-entry score maxima is a lower bound L of
 //      the k-th largest score (it is the k-th largest of a subset of the scores);
 //   2. only groups whose maximum reaches L can hold top-k entries: their entries
@@ -357,36 +358,6 @@ __device__ int gather_range(const float* sb, int N, const uint32_t* gkey, uint16
   return total;
 }
 
-// Same as gather_range when every group is held in a thread's registers
-// (thread t owns group t, N <= 16 * blockDim): no memory access at all.
-__device__ int gather_small(const float (&sv)[GROUP], int G, const uint32_t* gkey, uint32_t lo, uint32_t hi,
-                            uint32_t* out_key, int32_t* out_idx, int base, int cap, SelectScratch* sc) {
-  const int tid = threadIdx.x;
-  const bool mine = tid < G && gkey[tid] >= lo;
-  int c = 0;
-  if (mine)
-#pragma unroll
-    for (int i = 0; i < GROUP; i++) {
-      const uint32_t kk = score_key(sv[i]);
-      c += (kk >= lo) && (kk < hi) && (kk != 0u);
-    }
-  int total;
-  int p = base + block_excl_scan(c, sc->scan, &total);
-  if (base + total > cap) return -1;
-  if (mine)
-#pragma unroll
-    for (int i = 0; i < GROUP; i++) {
-      const uint32_t kk = score_key(sv[i]);
-      if ((kk >= lo) && (kk < hi) && (kk != 0u)) {
-        out_key[p] = kk;
-        out_idx[p] = GROUP * tid + i;
-        p++;
-      }
-    }
-  lds_barrier();
-  return total;
-}
-
 // One lane's share (dims 2*lane, 2*lane+1) of a key row, for the fp64 rescoring.
 __device__ __forceinline__ float2 key_pair(const TopkParams& P, int b, int n) {
   const int lane = threadIdx.x & 63;
@@ -472,25 +443,6 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
   const int G = (N + GROUP - 1) / GROUP;
   const int W = (N + 31) / 32;
-  // N <= 16 * 1024: thread t keeps the scores of group t in registers, loaded
-  // up front together with q and the key-norm hints (one round trip)
-  const bool small = G <= TK_THREADS;
-  float sv[GROUP];
-  if (small) {
-    const int e0 = GROUP * tid;
-    if (tid < G && e0 + GROUP <= N && (reinterpret_cast<uintptr_t>(sb) & 15u) == 0) {
-#pragma unroll
-      for (int c = 0; c < GROUP / 4; c++) {
-        const f32x4 x = *(const f32x4*)(sb + e0 + 4 * c);
-#pragma unroll
-        for (int i = 0; i < 4; i++) sv[4 * c + i] = x[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < GROUP; i++) sv[i] = (tid < G && e0 + i < N) ? sb[e0 + i] : -INFINITY;
-    }
-  }
-
   // the largest key-norm bound (exact mode), also loaded up front
   float knorm = 0.f;
   if (P.exact)
@@ -539,27 +491,13 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   // 1. group keys (+ the largest key-norm bound in exact mode)
   int ns = 0;
   uint32_t kmin = 0xffffffffu, kmx = 0u;
-  if (small) {
-    if (tid < G) {
-      uint32_t kk = 0u;
-#pragma unroll
-      for (int i = 0; i < GROUP; i++) kk = max(kk, score_key(sv[i]));
-      L.gkey[tid] = kk;
-      if (kk) {
-        ns++;
-        kmin = kk;
-        kmx = kk;
-      }
-    }
-  } else {
-    for (int g = tid; g < G; g += TK_THREADS) {
-      const uint32_t kk = score_key(gmx[g]);
-      L.gkey[g] = kk;
-      if (kk) {
-        ns++;
-        kmin = min(kmin, kk);
-        kmx = max(kmx, kk);
-      }
+  for (int g = tid; g < G; g += TK_THREADS) {
+    const uint32_t kk = score_key(gmx[g]);
+    L.gkey[g] = kk;
+    if (kk) {
+      ns++;
+      kmin = min(kmin, kk);
+      kmx = max(kmx, kk);
     }
   }
   block_sum_min_max(ns, kmin, kmx, knorm, &L.sc);
@@ -581,8 +519,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   }
 
   // 3. candidates >= L in index order
-  const int M1 = small ? gather_small(sv, G, L.gkey, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc)
-                       : gather_range(sb, N, L.gkey, L.qlist, G, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc);
+  const int M1 = gather_range(sb, N, L.gkey, L.qlist, G, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc);
   if (M1 < 0) return false;
   // (a key of 0xffffffff would be a NaN pattern: score_key maps NaN to 0)
 
@@ -691,8 +628,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
       lds_barrier();
       int M = Mc;
       if (lo < lkey) {  // entries below L can still sit in the band
-        const int ext = small ? gather_small(sv, G, L.gkey, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc)
-                              : gather_range(sb, N, L.gkey, L.qlist, G, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc);
+        const int ext = gather_range(sb, N, L.gkey, L.qlist, G, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc);
         if (ext < 0) return false;
         M += ext;
       }
@@ -749,6 +685,402 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   }
   if (mask)
     for (int n = tid; n < N; n += TK_THREADS) mask[n] = (sel[n >> 5] >> (n & 31)) & 1u;
+  for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
+  if (tid == 0) P.count[b] = total;
+  return true;
+}
+
+// ---------------------------------------------------------------- small path
+
+// N <= 16 * 1024 has a kernel of its own (its own register budget): thread t
+// keeps the scores of entries 16t .. 16t+15 in registers. One histogram of all
+// keys finds the bin of the k-th score, whose few members are ranked exactly;
+// exact mode rescores the band around that score; the output is written from
+// the registers in thread order, which is index order. Every global read is
+// issued up front, reductions and scans run on DPP lane moves, and each step
+// costs one barrier.
+constexpr int SBIN_CAP = 2048;  // members of the k-th score's histogram bin
+struct SmallLds {
+  float qP[64 * QP_STRIDE];
+  float krow[NWAVES][RS][LIT_IDX_DIM];
+  double psum[NWAVES][RS][64];
+  double band_s[FBAND_CAP];
+  int32_t band_n[FBAND_CAP];
+  uint32_t hist2k[2048 + 1];  // + a slot for the keys that are never selected
+  uint32_t bkey[SBIN_CAP];
+  int32_t bidx[SBIN_CAP];
+  uint32_t sel[TK_THREADS * GROUP / 32];
+  int part[6][NWAVES];  // one per block scan
+  uint32_t red_u[3][NWAVES];
+  double red_d[2][NWAVES];
+  int misc[4];
+};
+
+// fp64 canonical scores of NC entries by one wave, their chains interleaved:
+// lane h owns head h (q row in qP); each entry's key row is staged in krow[c]
+// from the lanes' pairs kp[c] and read back as broadcasts. The head terms go
+// through psum[c] and every lane adds them up in head order (lanes h >= H post
+// +0.0, which leaves a sum that starts at +0.0 unchanged), so all lanes return
+// the NC scores.
+template <int NC>
+__device__ __forceinline__ void rescore_lanes(const float* qP, const float2 (&kp)[NC], float w_h, int H,
+                                              float (*krow)[LIT_IDX_DIM], double (*psum)[64], double (&out)[NC]) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < NC; c++) *(float2*)(krow[c] + 2 * lane) = kp[c];
+  wave_sync();
+  const float* qr = qP + lane * QP_STRIDE;
+  double acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; c++) acc[c] = 0.0;
+#pragma unroll 2
+  for (int d0 = 0; d0 < LIT_IDX_DIM; d0 += 8) {
+    const f32x4 qa = *(const f32x4*)(qr + d0), qb = *(const f32x4*)(qr + d0 + 4);
+    f32x4 ka[NC], kb[NC];
+#pragma unroll
+    for (int c = 0; c < NC; c++) {
+      ka[c] = *(const f32x4*)(krow[c] + d0);
+      kb[c] = *(const f32x4*)(krow[c] + d0 + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) acc[c] = fma((double)qa[j], (double)ka[c][j], acc[c]);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) acc[c] = fma((double)qb[j], (double)kb[c][j], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; c++) {
+    const double a = acc[c] > 0.0 ? acc[c] : 0.0;
+    psum[c][lane] = lane < H ? (double)w_h * a : 0.0;
+    out[c] = 0.0;
+  }
+  wave_sync();
+  for (int h0 = 0; h0 < H; h0 += 8) {
+    double t[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; c++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) t[c][i] = psum[c][h0 + i];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) out[c] = out[c] + t[c][i];
+  }
+  wave_sync();  // krow and psum are refilled by the next call
+}
+
+static_assert(sizeof(SmallLds) <= 160 * 1024, "LDS budget of a gfx950 CU");
+
+// One lane's share (dims 2*lane, 2*lane+1) of a key row, dtype fixed at compile time.
+template <bool BF16>
+__device__ __forceinline__ float2 key_pair_t(const TopkParams& P, int b, int n) {
+  const int lane = threadIdx.x & 63;
+  const size_t off = ((size_t)b * P.N + n) * LIT_IDX_DIM + 2 * lane;
+  if (BF16) {
+    const uint32_t v = *(const uint32_t*)((const uint16_t*)P.kidx + off);
+    return make_float2(bf16_lo(v), bf16_hi(v));
+  }
+  return *(const float2*)((const float*)P.kidx + off);
+}
+
+// Returns false, having written nothing, when a capacity is exceeded. BF16:
+// the index q and keys are bf16 (else fp32; unused without exact mode).
+template <bool BF16>
+__device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int N = P.N, k = P.k;
+  const float* sb = P.scores + (size_t)b * N;
+  int32_t* ids = P.ids + (size_t)b * k;
+  uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
+  const int e0 = GROUP * tid;
+
+  // 0. every global read up front: my 16 scores; in exact mode the key-norm
+  //    bounds, w and this thread's 8-dim piece of q (head tid/16)
+  //    (loads at clamped addresses, masked afterwards: nothing waits on a
+  //    branch before the next load is issued)
+  f32x4 sv[GROUP / 4];
+  if (e0 + GROUP <= N && (reinterpret_cast<uintptr_t>(sb) & 15u) == 0) {
+#pragma unroll
+    for (int c = 0; c < GROUP / 4; c++) sv[c] = __builtin_nontemporal_load((const f32x4*)(sb + e0 + 4 * c));
+  } else {
+#pragma unroll
+    for (int c = 0; c < GROUP / 4; c++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) sv[c][i] = sb[min(e0 + 4 * c + i, N - 1)];
+  }
+  const int qh = tid >> 4, d8 = tid & 15;
+  // exact mode: indices clamped into range so that no load sits in a branch
+  float knorm = 0.f, w_h = 0.f, w_q = 0.f;
+  u32x4 qraw[2];
+  if (P.exact) {
+    const int H = P.H;
+    knorm = P.hints[(size_t)b * P.hints_len + min(tid, P.nchunks - 1)];
+    w_h = P.w[(size_t)b * H + min(lane, H - 1)];
+    w_q = P.w[(size_t)b * H + min(qh, H - 1)];
+    const size_t off = ((size_t)b * H + min(qh, H - 1)) * LIT_IDX_DIM + 8 * d8;
+    if (BF16) {
+      qraw[0] = *(const u32x4*)((const uint16_t*)P.q + off);
+    } else {
+      qraw[0] = *(const u32x4*)((const float*)P.q + off);
+      qraw[1] = *(const u32x4*)((const float*)P.q + off + 4);
+    }
+  }
+  for (int i = tid; i < 2048 + 1; i += TK_THREADS) L.hist2k[i] = 0u;
+  for (int i = tid; i < TK_THREADS * GROUP / 32; i += TK_THREADS) L.sel[i] = 0u;
+  uint32_t kv[GROUP];
+#pragma unroll
+  for (int i = 0; i < GROUP; i++) kv[i] = score_key(sv[i / 4][i % 4]) & (e0 + i < N ? 0xffffffffu : 0u);
+
+  // 1. count, min and max of the selectable keys; exact mode also stages q,
+  //    and reduces sum_h |w_h| |q_h|, sum_h |w_h| and the largest key norm
+  int ns = 0;
+  uint32_t kmin = 0xffffffffu, kmx = 0u;
+#pragma unroll
+  for (int i = 0; i < GROUP; i++)
+    if (kv[i]) {
+      ns++;
+      kmin = min(kmin, kv[i]);
+      kmx = max(kmx, kv[i]);
+    }
+  double qn = 0.0, wa = 0.0;
+  if (P.exact) {
+    if (tid >= P.nchunks) knorm = 0.f;
+    if (lane >= P.H) w_h = 0.f;
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (BF16) {
+        x[2 * i] = bf16_lo(qraw[0][i]);
+        x[2 * i + 1] = bf16_hi(qraw[0][i]);
+      } else {
+        x[i] = __uint_as_float(qraw[0][i]);
+        x[4 + i] = __uint_as_float(qraw[1][i]);
+      }
+    }
+    if (qh >= P.H) {
+      w_q = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = 0.f;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      L.qP[qh * QP_STRIDE + 8 * d8 + i] = x[i];
+      ss += (double)x[i] * (double)x[i];
+    }
+    // 16 lanes per head: their sum of squares lands in the head's d8 == 15 lane
+    ss += dpp_f64<0x111>(ss);
+    ss += dpp_f64<0x112>(ss);
+    ss += dpp_f64<0x114>(ss);
+    ss += dpp_f64<0x118>(ss);
+    if (d8 == 15) {
+      wa = fabs((double)w_q);
+      qn = wa * sqrt(ss);
+    }
+  }
+  {
+    const int s_w = wave_sum_dpp(ns);
+    const uint32_t mn_w = wave_min_dpp(kmin), mx_w = wave_max_dpp(kmx);
+    const uint32_t kn_w = wave_max_dpp(__float_as_uint(knorm));  // non-negative floats order as integers
+    double qn_w = 0.0, wa_w = 0.0;
+    if (P.exact) {
+      qn_w = wave_sum_f64_dpp(qn);
+      wa_w = wave_sum_f64_dpp(wa);
+    }
+    if (lane == 0) {
+      L.part[0][wid] = s_w;
+      L.red_u[0][wid] = mn_w;
+      L.red_u[1][wid] = mx_w;
+      L.red_u[2][wid] = kn_w;
+      L.red_d[0][wid] = qn_w;
+      L.red_d[1][wid] = wa_w;
+    }
+  }
+  lds_barrier();
+  // the per-wave values, one per lane of each row, reduced across the row
+  const int slot = lane & 15;
+  ns = __builtin_amdgcn_readlane(row_incl_scan_dpp(L.part[0][slot]), 15);
+  uint32_t kn_u;
+  {
+    uint32_t mn = L.red_u[0][slot], mx = L.red_u[1][slot], kn = L.red_u[2][slot];
+    mn = min(mn, dpp_u32<0x111>(~0u, mn));
+    mn = min(mn, dpp_u32<0x112>(~0u, mn));
+    mn = min(mn, dpp_u32<0x114>(~0u, mn));
+    mn = min(mn, dpp_u32<0x118>(~0u, mn));
+    mx = max(mx, dpp_u32<0x111>(0u, mx));
+    mx = max(mx, dpp_u32<0x112>(0u, mx));
+    mx = max(mx, dpp_u32<0x114>(0u, mx));
+    mx = max(mx, dpp_u32<0x118>(0u, mx));
+    kn = max(kn, dpp_u32<0x111>(0u, kn));
+    kn = max(kn, dpp_u32<0x112>(0u, kn));
+    kn = max(kn, dpp_u32<0x114>(0u, kn));
+    kn = max(kn, dpp_u32<0x118>(0u, kn));
+    kmin = (uint32_t)__builtin_amdgcn_readlane((int)mn, 15);
+    kmx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 15);
+    kn_u = (uint32_t)__builtin_amdgcn_readlane((int)kn, 15);
+  }
+  double Q = 0.0, Wa = 0.0;
+  if (P.exact) {
+    double q = L.red_d[0][slot], a = L.red_d[1][slot];
+    q += dpp_f64<0x111>(q);
+    a += dpp_f64<0x111>(a);
+    q += dpp_f64<0x112>(q);
+    a += dpp_f64<0x112>(a);
+    q += dpp_f64<0x114>(q);
+    a += dpp_f64<0x114>(a);
+    q += dpp_f64<0x118>(q);
+    a += dpp_f64<0x118>(a);
+    Q = readlane_f64(q, 15);
+    Wa = readlane_f64(a, 15);
+  }
+
+  // selected: key > hi (bits in `mine`, taken as soon as hi is known so that
+  // the keys die early), or a band or bin member marked in sel
+  auto keys_above = [&](uint32_t hi) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) m |= (uint32_t)(kv[i] > hi) << i;
+    return m;
+  };
+  uint32_t mine;
+  if (ns <= k) {
+    mine = keys_above(0u);  // every selectable entry
+  } else {
+    // 2. one histogram of all keys over the bits below their common prefix
+    const uint32_t diff = kmin ^ kmx;
+    const int hb = diff ? 31 - __clz((int)diff) : 0;
+    const int shift = hb > 10 ? hb - 10 : 0;
+    const uint32_t prefix = kmx & ~((2u << hb) - 1u);
+    auto binof = [&](uint32_t kk) -> uint32_t { return (kk - prefix) >> shift; };
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) atomicAdd(&L.hist2k[kv[i] ? binof(kv[i]) : 2048u], 1u);
+    lds_barrier();
+    const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
+    int tot;
+    const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.part[1], &tot);
+    if (ab < k && k <= ab + c0) {
+      L.misc[0] = 2047 - 2 * tid;
+      L.misc[1] = ab;
+    } else if (ab + c0 < k && k <= ab + c0 + c1) {
+      L.misc[0] = 2046 - 2 * tid;
+      L.misc[1] = ab + c0;
+    }
+    lds_barrier();
+    const uint32_t bin_t = (uint32_t)L.misc[0];
+    const int r = k - L.misc[1];  // members of bin_t that are selected
+    // 3. the members of bin_t, in index order, ranked exactly
+    int nb = 0;
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) nb += kv[i] && binof(kv[i]) == bin_t;
+    int m;
+    int bp = block_excl_scan1<NWAVES>(nb, L.part[2], &m);
+    if (m > SBIN_CAP) return false;
+#pragma unroll
+    for (int i = 0; i < GROUP; i++)
+      if (kv[i] && binof(kv[i]) == bin_t) {
+        L.bkey[bp] = kv[i];
+        L.bidx[bp] = e0 + i;
+        bp++;
+      }
+    lds_barrier();
+    for (int t = tid; t < m; t += TK_THREADS) {
+      const uint32_t ki = L.bkey[t];
+      int rank = 0;
+      for (int j = 0; j < m; j++) {
+        const uint32_t kj = L.bkey[j];
+        rank += (kj > ki) || (kj == ki && j < t);
+      }
+      if (!P.exact && rank < r) atomicOr(&L.sel[L.bidx[t] >> 5], 1u << (L.bidx[t] & 31));
+      if (rank == r - 1) L.misc[2] = (int)ki;
+    }
+    lds_barrier();
+    const uint32_t T = (uint32_t)L.misc[2];
+    if (!P.exact) {
+      mine = 0u;  // everything in higher bins
+#pragma unroll
+      for (int i = 0; i < GROUP; i++) mine |= (uint32_t)(kv[i] != 0u && binof(kv[i]) > bin_t) << i;
+    } else {
+      // 4. exact band around T: fp32 scores are within delta of their fp64
+      //    values, so entries above T + 2 delta are in, below T - 2 delta out
+      const double terms = (double)(LIT_IDX_DIM + P.H + 2);
+      const double delta = (ERR_SAFETY * 0x1p-24 * terms * Q * (double)__uint_as_float(kn_u) +
+                            ERR_SAFETY * terms * 0x1p-126 * Wa) * (1.0 + 0x1p-20);
+      const double t = (double)key_score(T);
+      const uint32_t lo0 = score_key(__double2float_rd(t - 2.0 * delta));
+      const uint32_t lo = lo0 > 1u ? lo0 : 1u;
+      const uint32_t hi = score_key(__double2float_ru(t + 2.0 * delta));
+      mine = keys_above(hi);
+      int nd = 0, nbd = 0;
+#pragma unroll
+      for (int i = 0; i < GROUP; i++) {
+        nd += kv[i] > hi;
+        nbd += kv[i] >= lo && kv[i] <= hi;
+      }
+      int tb;
+      int pos = block_excl_scan1<NWAVES>((nd << 16) | nbd, L.part[3], &tb);
+      pos &= 0xffff;
+      const int A = tb >> 16, M = tb & 0xffff;
+      if (M > FBAND_CAP) return false;
+#pragma unroll
+      for (int i = 0; i < GROUP; i++)
+        if (kv[i] >= lo && kv[i] <= hi) L.band_n[pos++] = e0 + i;
+      lds_barrier();
+      const int rr = k - A;
+      if (rr < 1 || rr > M) {
+        report_violation(P, b, ids, mask);
+        return true;
+      }
+      // the band's key rows: every wave loads its first RS rows before any math
+      for (int i0 = wid * RS; i0 < M; i0 += NWAVES * RS) {
+        float2 kp[RS];
+#pragma unroll
+        for (int c = 0; c < RS; c++) kp[c] = i0 + c < M ? key_pair_t<BF16>(P, b, L.band_n[i0 + c]) : make_float2(0.f, 0.f);
+        double sc[RS];
+        rescore_lanes<RS>(L.qP, kp, w_h, P.H, L.krow[wid], L.psum[wid], sc);
+#pragma unroll
+        for (int c = 0; c < RS; c++)
+          if (lane == c && i0 + c < M) L.band_s[i0 + c] = sc[c];
+      }
+      lds_barrier();
+      for (int i = tid; i < M; i += TK_THREADS) {
+        const double si = L.band_s[i];
+        int rank = 0;
+        for (int j = 0; j < M; j++) {
+          const double sj = L.band_s[j];
+          rank += (sj > si) || (sj == si && j < i);  // the band is in index order
+        }
+        if (rank < rr) atomicOr(&L.sel[L.band_n[i] >> 5], 1u << (L.band_n[i] & 31));
+      }
+    }
+    lds_barrier();
+  }
+
+  // 5. output in thread order = index order
+  mine |= (L.sel[e0 >> 5] >> (e0 & 31)) & 0xffffu;
+  int total;
+  int opos = block_excl_scan1<NWAVES>(__popc(mine), L.part[4], &total);
+#pragma unroll
+  for (int i = 0; i < GROUP; i++)
+    if ((mine >> i) & 1u) {
+      if (opos < k) ids[opos] = e0 + i;
+      opos++;
+    }
+  if (mask && e0 < N) {
+    if (e0 + GROUP <= N && (reinterpret_cast<uintptr_t>(mask) & 15u) == 0) {
+      u32x4 mv;
+#pragma unroll
+      for (int w = 0; w < 4; w++)
+        mv[w] = ((mine >> (4 * w)) & 1u) | (((mine >> (4 * w + 1)) & 1u) << 8) | (((mine >> (4 * w + 2)) & 1u) << 16) |
+                (((mine >> (4 * w + 3)) & 1u) << 24);
+      *(u32x4*)(mask + e0) = mv;
+    } else {
+      for (int i = 0; i < GROUP && e0 + i < N; i++) mask[e0 + i] = (mine >> i) & 1u;
+    }
+  }
   for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
   if (tid == 0) P.count[b] = total;
   return true;
@@ -935,6 +1267,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   full_path(P, *reinterpret_cast<FullLds*>(smem), b);
 }
 
+// The small kernel's fallback, out of line so that its registers do not weigh
+// on the small path.
+__device__ __noinline__ void full_path_call(TopkParams P, int b) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  full_path(P, *reinterpret_cast<FullLds*>(smem), b);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(TK_THREADS) void topk_small_kernel(TopkParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int b = blockIdx.x;
+  if (small_path<BF16>(P, *reinterpret_cast<SmallLds*>(smem), b)) return;
+  __syncthreads();
+  full_path_call(P, b);
+}
+
 }  // namespace
 }  // namespace lit
 
@@ -986,6 +1334,19 @@ extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N,
   P.ws_band_s = (double*)w8;
   P.ws_band_n = (int32_t*)(w8 + round_up(per * sizeof(double), 256));
   P.ws_band_sel = w8 + round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256);
+  if (N <= TK_THREADS * GROUP) {
+    const size_t lds = std::max(sizeof(FullLds), sizeof(SmallLds));
+    const bool bf16 = P.exact && P.dtype == LIT_BF16;
+    const void* kern = bf16 ? (const void*)topk_small_kernel<true> : (const void*)topk_small_kernel<false>;
+    lit_status st = allow_lds(kern, lds, "lit_topk_select");
+    if (st != LIT_OK) return st;
+    if (bf16)
+      topk_small_kernel<true><<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);
+    else
+      topk_small_kernel<false><<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);
+    LIT_CHECK_LAUNCH("lit_topk_select");
+    return LIT_OK;
+  }
   const size_t lds = std::max(sizeof(FullLds), sizeof(FastLds));
   lit_status st = allow_lds((const void*)topk_kernel, lds, "lit_topk_select");
   if (st != LIT_OK) return st;

@@ -166,6 +166,11 @@ def test_topk_on_given_scores_with_heavy_ties():
         s = torch.round(torch.randn(3, N, generator=g) * 4) / 4  # many exact ties
         s[0, :50] = float("-inf")
         s[1, 7] = float("nan")
+        # row 2: the k-th score is zero and +0.0 / -0.0 (equal values) are mixed:
+        # the lower index must win between them as between any equal scores
+        z = torch.where(torch.rand(N, generator=g) < 0.5, torch.tensor(-0.0), torch.tensor(0.0))
+        z[torch.randperm(N, generator=g)[: k // 2]] = torch.rand(k // 2, generator=g) + 1.0
+        s[2] = z
         ids, cnt, mask = lit.topk_select(s.cuda(), k)
         torch.cuda.synchronize()
         rids, rcnt, rmask = oracle.topk(s.double().numpy(), k)
