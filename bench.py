@@ -43,9 +43,10 @@ def algo_bytes_per_query(N, H, k, window, Hq, kv_row_bytes=1024):
 
 
 def idx_score_bytes_per_query(N, H):
-    """Algorithmic bytes of one query of the indexer-score kernel: the keys, the
-    queries and weights, the fp32 scores written and the key-norm chunk maxima."""
-    return N * 128 * 2 + H * 128 * 2 + H * 4 + N * 4 + (-(-N // 256)) * 4
+    """Algorithmic bytes of one query of the indexer-score kernel: the bf16 keys
+    and queries, the fp32 weights, the fp32 scores written and the hints written
+    (one key-norm bound per 256 entries, one score maximum per 16 entries)."""
+    return N * 128 * 2 + H * 128 * 2 + H * 4 + N * 4 + ((-(-N // 256)) + (-(-N // 16))) * 4
 
 
 class Path:
@@ -125,17 +126,27 @@ def time_graph(g, reps):
     return start.elapsed_time(end) / 1e3  # seconds
 
 
-def stored_traffic(kernel_src, workload):
+# the sources the indexer-score kernel is compiled from
+IDX_SCORE_SOURCES = ("lightning_indexer_top_idx_amd/csrc/idx_score.hip", "lightning_indexer_top_idx_amd/csrc/lit_common.h",
+                     "include/lit.h")
+
+
+def source_hash(paths=IDX_SCORE_SOURCES):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload):
     """Per-launch HBM bytes of the indexer-score kernel from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"idx_score_{workload}_counters.json")
-    src = os.path.join(ROOT, "lightning_indexer_top_idx_amd", "csrc", kernel_src)
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != h:
+        if rec.get("source_sha256") != source_hash():
             return None
         return rec.get("hbm_bytes_per_launch")
     except Exception:
@@ -204,11 +215,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration:
-        # a copy of known size: its counter reading per byte scales the kernels' readings
+        # copies of known size (512 MiB read, 512 MiB written): their counter
+        # readings per byte scale the kernels' readings. One is the runtime's
+        # blit copy, one a vectorized elementwise kernel (16-byte accesses).
         src = torch.ones(512 << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
     wl = W.CTX64K_B
@@ -258,7 +272,7 @@ def main():
     launch_s = sec_s / (reps * len(paths))
     score_bytes = idx_score_bytes_per_query(wl.N, wl.H) * wl.B
     achieved = score_bytes / launch_s / 1e9
-    traffic = stored_traffic("idx_score.hip", wl.name)
+    traffic = stored_traffic(wl.name)
     roofline = {"bound": "hbm", "kernel": "idx_score (indexer scores, MFMA bf16)", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "avg_launch_us": round(launch_s * 1e6, 2),
