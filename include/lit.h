@@ -199,9 +199,12 @@ lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k,
  * ids    : [B][k_cap] ascending ids (tail -1) with count[b] valid, or NULL for
  *          every row (then count and window are ignored).
  * window : 0..LIT_MAX_WINDOW, clamped to N.
- * out    : [B][Hq][512] fp32 output; lse: [B][Hq] fp32 output or NULL.
+ * out    : [B][Hq][512] fp32 output (16-byte aligned); lse: [B][Hq] fp32 output or NULL.
+ * q, kv->data and kv->rope must be 16-byte aligned. Errors: LIT_ERR_NULL,
+ * LIT_ERR_SHAPE (B, Hq outside 1..64, window), LIT_ERR_DTYPE (unsupported row
+ * or query dtype), LIT_ERR_ALIGN, LIT_ERR_WORKSPACE.
  * An empty R (count 0 and window 0) gives out = 0 and lse = -inf.
- * Workspace: lit_attn_workspace_bytes(B, Hq, N) bytes. */
+ * Workspace: lit_attn_workspace_bytes(B, Hq, N) bytes, 16-byte aligned. */
 size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N);
 lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,
                                   int32_t B, const int32_t* ids, const int32_t* count,

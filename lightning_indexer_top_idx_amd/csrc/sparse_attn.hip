@@ -79,17 +79,19 @@ struct RowList {
   int c, N, Wc, total;
   bool dense;
   const uint32_t* dup;  // LDS bitmap over the window rows
-  __device__ __forceinline__ int row(int p) const {
+  // The global read behind list position p (any p: the index is clamped into
+  // the ids, so the load needs no branch and can be issued ahead of its use).
+  __device__ __forceinline__ int fetch(int p) const { return (!dense && c > 0) ? ids[max(min(p, c - 1), 0)] : 0; }
+  // The row of list position p, given f = fetch(p).
+  __device__ __forceinline__ int resolve(int p, int f) const {
     if (p >= total) return -1;
     if (dense) return p;
-    if (p < c) {
-      const int r = ids[p];
-      return (r >= 0 && r < N) ? r : -1;  // ids outside the rows are skipped
-    }
+    if (p < c) return (f >= 0 && f < N) ? f : -1;  // ids outside the rows are skipped
     const int j = p - c;
     if ((dup[j >> 5] >> (j & 31)) & 1u) return -1;
     return N - Wc + j;
   }
+  __device__ __forceinline__ int row(int p) const { return resolve(p, fetch(p)); }
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -263,19 +265,30 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
   const size_t seq_rows = (size_t)b * P.N;
 
   int cur = 0;
+  int fnext = 0;  // ids read of the next tile's rows (threads < TR), one tile ahead
   if (p0 < p1) {
-    if (tid < TR) L.rows[0][tid] = (p0 + tid < p1) ? RL.row(p0 + tid) : -1;
+    if (tid < TR) {
+      L.rows[0][tid] = (p0 + tid < p1) ? RL.row(p0 + tid) : -1;
+      fnext = RL.fetch(p0 + TR + tid);
+    }
     lds_barrier();
     TileRegs<KVT> R;
     tile_load<KVT>(P, seq_rows, L.rows[0], R);
     tile_store<KVT>(L.tile, R);
     lds_barrier();
   }
+  // Nothing issued before the loop (queries, ids, first tile) may still be in
+  // flight at its head; otherwise the first use of the queries inside the loop
+  // would wait for every load, the next tile's prefetch included.
+  __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll 1
   for (int t0 = p0; t0 < p1; t0 += TR) {
     const int nxt = cur ^ 1;
     const bool more = t0 + TR < p1;
-    if (more && tid < TR) L.rows[nxt][tid] = (t0 + TR + tid < p1) ? RL.row(t0 + TR + tid) : -1;
+    if (tid < TR) {
+      if (more) L.rows[nxt][tid] = (t0 + TR + tid < p1) ? RL.resolve(t0 + TR + tid, fnext) : -1;
+      fnext = RL.fetch(t0 + 2 * TR + tid);  // lands with the tile loads below
+    }
     lds_barrier();
     TileRegs<KVT> R;
     if (more) tile_load<KVT>(P, seq_rows, L.rows[nxt], R);  // the next tile is in flight during the math
@@ -386,25 +399,54 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
   }
 }
 
-// Log-sum-exp merge of the row slices of one (sequence, head).
-__global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part, int splits, int Hq,
+// Log-sum-exp merge of the row slices of one (sequence, head): 128 threads,
+// four dims each. Every slice's (m, l) and partial output are requested at
+// once (no load waits on another), then merged in slice order.
+constexpr int COMBINE_MAX = 8;  // slices merged per pass (all of a pass requested at once)
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int splits, int Hq,
                                                            float* __restrict__ out, float* __restrict__ lse) {
-  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
+  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d4 = threadIdx.x;
   const float* base = part + ((size_t)b * splits * Hq + h) * PART;
   const size_t stride = (size_t)Hq * PART;
   float M = -INFINITY;
-  for (int s = 0; s < splits; s++) M = fmaxf(M, base[s * stride + 512]);
-  float L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += COMBINE_MAX) {
+    float mv[COMBINE_MAX];
+#pragma unroll
+    for (int i = 0; i < COMBINE_MAX; i++) mv[i] = s0 + i < splits ? base[(s0 + i) * stride + 512] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < COMBINE_MAX; i++) M = fmaxf(M, mv[i]);
+  }
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
-    for (int s = 0; s < splits; s++) {
-      const float* ps = base + s * stride;
-      const float wgt = exp2f(ps[512] - M);  // empty slices have m = -inf -> 0
-      L += wgt * ps[513];
-      acc += wgt * ps[d];
+    for (int s0 = 0; s0 < splits; s0 += COMBINE_MAX) {
+      f32x4 ov[COMBINE_MAX];
+      float ml[COMBINE_MAX][2];
+#pragma unroll
+      for (int i = 0; i < COMBINE_MAX; i++) {
+        const bool in = s0 + i < splits;
+        const float* ps = base + (size_t)(in ? s0 + i : 0) * stride;
+        ov[i] = *(const f32x4*)(ps + 4 * d4);
+        ml[i][0] = in ? ps[512] : -INFINITY;
+        ml[i][1] = ps[513];
+      }
+#pragma unroll
+      for (int i = 0; i < COMBINE_MAX; i++) {
+        const float wgt = exp2f(ml[i][0] - M);  // empty slices and padding have m = -inf -> 0
+        if (wgt > 0.f) {
+          L += wgt * ml[i][1];
+#pragma unroll
+          for (int j = 0; j < 4; j++) acc[j] += wgt * ov[i][j];
+        }
+      }
     }
   }
-  out[((size_t)b * Hq + h) * LIT_KV_DIM + d] = L > 0.f ? acc / L : 0.f;
-  if (lse && d == 0) lse[(size_t)b * Hq + h] = L > 0.f ? M * LN2 + logf(L) : -INFINITY;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  f32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; j++) o[j] = acc[j] * inv;
+  *(f32x4*)(out + ((size_t)b * Hq + h) * LIT_KV_DIM + 4 * d4) = o;
+  if (lse && d4 == 0) lse[(size_t)b * Hq + h] = L > 0.f ? M * LN2 + logf(L) : -INFINITY;
 }
 
 // FP32 rows and queries: one workgroup per (sequence, head), fp32 VALU with an
@@ -493,6 +535,381 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   if (lse && tid == 0) lse[(size_t)b * Hq + h] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
+// ---------------------------------------------------------------- all heads per workgroup (BF16 rows)
+
+// One workgroup of 8 waves: one sequence, all (up to 64) query heads, one slice
+// of the row list, so every gathered row is read from memory once. Tiles of 64
+// rows go straight from global memory into LDS (global_load_lds, 16 bytes per
+// lane: one wave instruction moves one 1 KiB row), double-buffered in two
+// separate LDS arrays so that reading one buffer never waits for the loads into
+// the other. Wave w owns head block hb = w & 3 (16 heads):
+//   scores: rows 32 (w >> 2) .. +31 of the tile, S^T = K Q^T on
+//           v_mfma_f32_16x16x32_bf16 (A = rows from LDS, B = queries in registers);
+//   output: dims 256 (w >> 2) .. +255, O += P V on the same instruction, with the
+//           V operand read transposed by ds_read_b64_tr_b16 (lane (g, s) points at
+//           row 8g + s/4 (+4), dims 4(s % 4) .. +3 of the 16-dim block).
+// The two waves of a head block agree on each head's running maximum through LDS.
+constexpr int MH_THREADS = 512;
+constexpr int MH_WAVES = MH_THREADS / 64;
+constexpr int MH_ROWS_PER_WAVE = 64 / MH_WAVES;  // tile rows each wave loads
+constexpr int MH_TR = 64;        // rows per tile
+constexpr int MH_RS = 520;       // bf16 per LDS row: 1040 B keeps rows 16-byte aligned and spreads banks
+constexpr int MH_PS = MH_TR + 8;  // bf16 per LDS row of P (one head)
+constexpr int MH_TARGET = 256;   // workgroups aimed at: one per CU
+constexpr int MH_ROWS_CAP = 1152;  // rows of a selection slice resolved up front (a multiple of MH_TR)
+
+struct MhTile {
+  uint16_t v[MH_TR * MH_RS];
+};
+
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+
+// Wave w issues the loads of its share of the tile rows (one instruction per row).
+// Rows that are not attended (-1) load row 0 instead: their weight is 0, and a
+// finite value keeps 0 * value = 0.
+__device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, const int* rws, MhTile& T) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  // the row ids first: no LDS read sits between the loads
+  int rid[MH_ROWS_PER_WAVE];
+#pragma unroll
+  for (int v = 0; v < MH_ROWS_PER_WAVE / 4; v++) {
+    const u32x4 r4 = *(const u32x4*)(rws + MH_ROWS_PER_WAVE * wid + 4 * v);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rid[4 * v + i] = __builtin_amdgcn_readfirstlane((int)r4[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) {
+    const int slot = MH_ROWS_PER_WAVE * wid + i;
+    const int r = rid[i];
+    const size_t rr = seq_rows + (size_t)(r >= 0 ? r : 0);
+    const uint16_t* src = (const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane;
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(T.v + slot * MH_RS), 16, 0, 0);
+  }
+}
+
+// The 64 query rows of sequence b (heads past Hq repeat the last head: their
+// outputs are never written) into a tile buffer, same layout as key rows.
+__device__ __forceinline__ void mh_issue_q(const AttnParams& P, int b, MhTile& T) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) {
+    const int h = MH_ROWS_PER_WAVE * wid + i;
+    const uint16_t* src = P.q + ((size_t)b * P.Hq + min(h, P.Hq - 1)) * LIT_KV_DIM + 8 * lane;
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(T.v + h * MH_RS), 16, 0, 0);
+  }
+}
+
+// vmcnt waits: the loads of one tile (of this wave) allowed to stay in flight, or none.
+static_assert(MH_ROWS_PER_WAVE == 8, "wait_tile encodes vmcnt(8)");
+__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F78); }  // vmcnt(8)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+struct MhState {
+  f32x4 o[2][8];   // O[head 32 hp + 16 x + 4g + i][dim 128 qt + 16 nt + c16]
+  float m_o[2];    // running max of head 32 hp + 16 x + c16 (the output's heads)
+  float m_s;       // running max of head 16 hb + c16 (the scored heads)
+  float l_run;     // this lane's share of the sum of head 16 hb + c16
+};
+
+// Two roles per wave w, each sized so that the queries, the output and the
+// operands in flight fit in the registers of two waves per SIMD:
+//   scores  hb = w & 3, rh = w >> 2: heads 16 hb .. +15 (queries in registers)
+//           over tile rows 32 rh .. +31, S^T = K Q^T;
+//   output  hp = w & 1, qt = w >> 1: heads 32 hp .. +31 (two 16-head blocks x)
+//           over dims 128 qt .. +127, O += P V; each V read feeds both blocks.
+// Every wave follows the running maxima of the heads of both roles from the
+// same LDS values, so they agree without further exchange.
+__device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, int nvalid, const u32x4 (&qreg)[16],
+                                        MhState& S, float (*smax)[64], uint16_t* pbuf) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int hb = wid & 3, rh = wid >> 2, hp = wid & 1, qt = wid >> 1;
+  // S^T[rb]: rows 32 rh + 16 rb + 4g + i, head 16 hb + c16; the operands of
+  // K-step j + 2 are read while step j multiplies (the scheduling barrier keeps
+  // the compiler from hoisting every read, which would exhaust the registers)
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const uint16_t* krow = T.v + (32 * rh + c16) * MH_RS + 8 * g;
+  auto kld = [&](int j, int rb) { return *(const u32x4*)(krow + 16 * rb * MH_RS + 32 * j); };
+  u32x4 ka[2] = {kld(0, 0), kld(0, 1)}, kb[2] = {kld(1, 0), kld(1, 1)};
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    u32x4 kc[2] = {ka[0], ka[1]};
+    if (j + 2 < 16) {
+      kc[0] = kld(j + 2, 0);
+      kc[1] = kld(j + 2, 1);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[rb]), __builtin_bit_cast(bf16x8, qreg[j]),
+                                                        acc[rb], 0, 0, 0);
+    ka[0] = kb[0];
+    ka[1] = kb[1];
+    kb[0] = kc[0];
+    kb[1] = kc[1];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float xs[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const bool valid = 32 * rh + 16 * rb + 4 * g + i < nvalid;
+      xs[rb][i] = valid ? acc[rb][i] * P.scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, xs[rb][i]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  if (g == 0) smax[rh][16 * hb + c16] = tmax;
+  lds_barrier();
+  {
+    const int h = 16 * hb + c16;
+    const float m_new = fmaxf(S.m_s, fmaxf(smax[0][h], smax[1][h]));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(S.m_s - m_use);
+    S.m_s = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+      uint32_t hbits[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float pv = exp2f(xs[rb][i] - m_use);
+        psum += pv;
+        const uint32_t bits = __float_as_uint(pv);
+        hbits[i] = (bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16;  // round to nearest even
+      }
+      u32x2 pk;
+      pk[0] = hbits[0] | (hbits[1] << 16);
+      pk[1] = hbits[2] | (hbits[3] << 16);
+      *(u32x2*)(pbuf + h * MH_PS + 32 * rh + 16 * rb + 4 * g) = pk;
+    }
+    S.l_run = S.l_run * alpha + psum;
+  }
+  // the output role's heads: their maxima moved the same way
+  float alpha_o[2];
+#pragma unroll
+  for (int x = 0; x < 2; x++) {
+    const int h = 32 * hp + 16 * x + c16;
+    const float m_new = fmaxf(S.m_o[x], fmaxf(smax[0][h], smax[1][h]));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    alpha_o[x] = exp2f(S.m_o[x] - m_use);
+    S.m_o[x] = m_new;
+  }
+  lds_barrier();
+  // rescale O (heads 32 hp + 16 x + 4g + i) when a running max moved
+  if (__any(alpha_o[0] != 1.0f || alpha_o[1] != 1.0f)) {
+#pragma unroll
+    for (int x = 0; x < 2; x++) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) al[i] = __shfl(alpha_o[x], 4 * g + i);
+#pragma unroll
+      for (int nt = 0; nt < 8; nt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) S.o[x][nt][i] *= al[i];
+    }
+  }
+  // O += P V over the 64 rows (two K-steps of 32, eight 16-dim blocks each);
+  // the V operands of step it + 2 are read while step it multiplies
+  const uint16_t* vbase = T.v + (8 * g + (c16 >> 2)) * MH_RS + 128 * qt + 4 * (c16 & 3);
+  auto vld = [&](int it) {
+    const uint16_t* vb = vbase + 32 * (it >> 3) * MH_RS + 16 * (it & 7);
+    const s16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4v*)vb);
+    const s16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4v*)(vb + 4 * MH_RS));
+    u32x4 bv;
+    bv[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    bv[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    bv[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    bv[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return bv;
+  };
+  bf16x8 pa[2];
+  u32x4 va = vld(0), vbn = vld(1);
+#pragma unroll
+  for (int it = 0; it < 16; it++) {
+    const int kk = it >> 3, nt = it & 7;
+    if (nt == 0)
+#pragma unroll
+      for (int x = 0; x < 2; x++)
+        pa[x] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pbuf + (32 * hp + 16 * x + c16) * MH_PS + 32 * kk + 8 * g));
+    u32x4 vc = va;
+    if (it + 2 < 16) vc = vld(it + 2);
+#pragma unroll
+    for (int x = 0; x < 2; x++)
+      S.o[x][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[x], __builtin_bit_cast(bf16x8, va), S.o[x][nt], 0, 0, 0);
+    va = vbn;
+    vbn = vc;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
+  __shared__ MhTile TA, TB;
+  __shared__ __align__(16) uint16_t pbuf[64 * MH_PS];
+  __shared__ __align__(16) int rows_all[MH_ROWS_CAP];  // the slice's rows, or a ring of 4 tiles for long dense slices
+  __shared__ uint32_t dup[LIT_MAX_WINDOW / 32];
+  __shared__ float smax[2][64];
+  __shared__ float ssum[2][64];
+  __shared__ int part[16];
+  const int b = blockIdx.x / P.splits, s = blockIdx.x % P.splits;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15, hb = wid & 3, rh = wid >> 2, hp = wid & 1, qt = wid >> 1;
+  const int Hq = P.Hq;
+  // the queries travel first, into the second tile buffer, while the row list is built
+  mh_issue_q(P, b, TB);
+
+  RowList RL;
+  RL.dense = P.ids == nullptr;
+  RL.N = P.N;
+  RL.dup = dup;
+  if (RL.dense) {
+    RL.ids = nullptr;
+    RL.c = 0;
+    RL.Wc = 0;
+    RL.total = P.N;
+  } else {
+    RL.ids = P.ids + (size_t)b * P.k_cap;
+    int c = P.count[b];
+    c = c < 0 ? 0 : (c > P.k_cap ? P.k_cap : c);
+    RL.c = c;
+    RL.Wc = P.window;
+    RL.total = c + P.window;
+  }
+  const int p0 = s * P.rows_per_split;
+  const int p1 = min(RL.total, p0 + P.rows_per_split);
+  if (!RL.dense && p1 > RL.c && RL.Wc > 0) {
+    for (int i = tid; i < (RL.Wc + 31) / 32; i += MH_THREADS) dup[i] = 0u;
+    lds_barrier();
+    const int lo = P.N - RL.Wc;
+    for (int j = tid; j < RL.c; j += MH_THREADS) {
+      const int id = RL.ids[j];
+      if (id >= lo && id < P.N) atomicOr(&dup[(id - lo) >> 5], 1u << ((id - lo) & 31));
+    }
+  }
+  lds_barrier();
+  // Every row of a selection slice is resolved here (the planner keeps those
+  // slices within MH_ROWS_CAP) and compacted, so the attended rows are list
+  // positions 0 .. n-1 and the tile loop reads nothing but the tiles. Longer
+  // slices are dense: their rows are their positions, computed per tile.
+  const int nrows = max(p1 - p0, 0);
+  const bool all_rows = nrows <= MH_ROWS_CAP;
+  int n = nrows;  // attended rows of the slice
+  if (all_rows) {
+    int r[MH_ROWS_CAP / MH_THREADS + 1];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < MH_ROWS_CAP / MH_THREADS + 1; k++) {
+      const int i = tid + MH_THREADS * k;
+      r[k] = i < nrows ? RL.row(p0 + i) : -1;
+      cnt += r[k] >= 0;
+    }
+    int pos = block_excl_scan1<MH_THREADS / 64>(cnt, part, &n);
+#pragma unroll
+    for (int k = 0; k < MH_ROWS_CAP / MH_THREADS + 1; k++)
+      if (r[k] >= 0) rows_all[pos++] = r[k];
+    lds_barrier();
+    const int upto = (n + MH_TR - 1) / MH_TR * MH_TR;
+    for (int i = n + tid; i < upto; i += MH_THREADS) rows_all[i] = -1;
+  } else if (tid < 2 * MH_TR) {
+    const int p = p0 + tid;
+    rows_all[tid] = p < p1 ? p : -1;
+  }
+  // the queries of head block hb as B operands, from the second tile buffer:
+  // K-step j, lane (g, c16) holds dims 32j + 8g .. +7 of head 16 hb + c16
+  wait_vm0();
+  lds_barrier();
+  u32x4 qreg[16];
+#pragma unroll
+  for (int j = 0; j < 16; j++) qreg[j] = *(const u32x4*)(TB.v + (16 * hb + c16) * MH_RS + 32 * j + 8 * g);
+  lds_barrier();
+  const size_t seq_rows = (size_t)b * P.N;
+  // (one LDS array, so that the compiler can tell its reads from the tile loads in flight)
+  auto tile_rows = [&](int tt) -> const int* { return rows_all + MH_TR * (all_rows ? tt : (tt & 3)); };
+  if (0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
+  if (MH_TR < n) mh_issue(P, seq_rows, tile_rows(1), TB);
+
+  MhState S;
+#pragma unroll
+  for (int x = 0; x < 2; x++) {
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) S.o[x][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    S.m_o[x] = -INFINITY;
+  }
+  S.m_s = -INFINITY;
+  S.l_run = 0.f;
+
+  // tile t uses buffer t & 1; tile t + 2 is issued into the same buffer once
+  // every wave is done with tile t
+#pragma unroll 1
+  for (int t = 0; MH_TR * t < n; t += 2) {
+#pragma unroll
+    for (int ab = 0; ab < 2; ab++) {
+      const int tt = t + ab;
+      const int q0 = MH_TR * tt;
+      if (q0 >= n) break;
+      if (q0 + MH_TR < n)
+        wait_tile();  // tile tt + 1 may stay in flight
+      else
+        wait_vm0();
+      if (!all_rows && tid < MH_TR) {
+        const int p = p0 + q0 + 2 * MH_TR + tid;
+        rows_all[MH_TR * ((tt + 2) & 3) + tid] = p < p1 ? p : -1;
+      }
+      lds_barrier();
+      mh_tile(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf);
+      lds_barrier();
+      if (q0 + 2 * MH_TR < n) mh_issue(P, seq_rows, tile_rows(tt + 2), ab == 0 ? TA : TB);
+    }
+  }
+
+  // l per head: the two row halves of the scoring role
+  {
+    float lw = S.l_run;
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+    if (g == 0) ssum[rh][16 * hb + c16] = lw;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int x = 0; x < 2; x++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int hh = 32 * hp + 16 * x + 4 * g + i;
+      const float Ls = ssum[0][hh] + ssum[1][hh];
+      const float Ms = __shfl(S.m_o[x], 4 * g + i);
+      if (hh >= Hq) continue;
+      if (P.splits == 1) {
+        float* oh = P.out + ((size_t)b * Hq + hh) * LIT_KV_DIM + 128 * qt;
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < 8; nt++) oh[16 * nt + c16] = S.o[x][nt][i] * inv;
+        if (P.lse && qt == 0 && c16 == 0) P.lse[(size_t)b * Hq + hh] = Ls > 0.f ? Ms * LN2 + logf(Ls) : -INFINITY;
+      } else {
+        float* ph = P.part + (((size_t)b * P.splits + s) * Hq + hh) * PART;
+#pragma unroll
+        for (int nt = 0; nt < 8; nt++) ph[128 * qt + 16 * nt + c16] = S.o[x][nt][i];
+        if (qt == 0 && c16 == 0) {
+          ph[512] = Ms;
+          ph[513] = Ls;
+        }
+      }
+    }
+}
+
+void plan_mh(int B, int rows_max, bool sparse, int* splits, int* rows_per_split) {
+  const int tiles = std::max(1, (rows_max + MH_TR - 1) / MH_TR);
+  const int want = std::max(1, (MH_TARGET + B - 1) / B);
+  int s = std::min(tiles, want);
+  if (sparse) s = std::max(s, (tiles * MH_TR + MH_ROWS_CAP - 1) / MH_ROWS_CAP);
+  const int tiles_per = (tiles + s - 1) / s;
+  s = (tiles + tiles_per - 1) / tiles_per;
+  *splits = s;
+  *rows_per_split = tiles_per * MH_TR;
+}
+
 void plan_splits(int B, int HG, int rows_max, int* splits, int* rows_per_split) {
   const int tiles = std::max(1, (rows_max + TR - 1) / TR);
   const int want = std::max(1, (TARGET_WGS + B * HG - 1) / (B * HG));
@@ -510,8 +927,13 @@ using namespace lit;
 
 extern "C" size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
-  int s, rps;
-  plan_splits(B, (Hq + HG_HEADS - 1) / HG_HEADS, N + LIT_MAX_WINDOW, &s, &rps);
+  int s1, s2, rps;
+  plan_splits(B, (Hq + HG_HEADS - 1) / HG_HEADS, N + LIT_MAX_WINDOW, &s1, &rps);
+  plan_mh(B, N + LIT_MAX_WINDOW, true, &s2, &rps);
+  int s3;
+  plan_mh(B, N, false, &s3, &rps);
+  s2 = std::max(s2, s3);
+  const int s = std::max(s1, s2);
   if (s <= 1) return 256;
   return round_up((size_t)B * s * Hq * PART * sizeof(float), 256);
 }
@@ -543,8 +965,8 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   } else {
     return fail(LIT_ERR_DTYPE, "%s: kv dtype %d unsupported", who, (int)kv->dtype);
   }
-  if (!aligned(q, 16) || !aligned(kv->data, 16) || (kv->rope && !aligned(kv->rope, 16)) || !aligned(out, 4))
-    return fail(LIT_ERR_ALIGN, "%s: q, kv->data and kv->rope must be 16-byte aligned", who);
+  if (!aligned(q, 16) || !aligned(kv->data, 16) || (kv->rope && !aligned(kv->rope, 16)) || !aligned(out, 16))
+    return fail(LIT_ERR_ALIGN, "%s: q, kv->data, kv->rope and out must be 16-byte aligned", who);
   hipStream_t st = (hipStream_t)stream;
   if (kv->dtype == LIT_F32) {
     attn_f32_kernel<<<dim3((unsigned)(B * Hq)), dim3(256), 0, st>>>((const float*)q, Hq, (const float*)kv->data, N,
@@ -555,7 +977,11 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   const int rows_max = ids ? (k_cap + Wc) : N;
   AttnParams P;
   const int HG = (Hq + HG_HEADS - 1) / HG_HEADS;
-  plan_splits(B, HG, rows_max, &P.splits, &P.rows_per_split);
+  const bool mh = kv->dtype == LIT_BF16;  // BF16 rows: all heads per workgroup
+  if (mh)
+    plan_mh(B, rows_max, ids != nullptr, &P.splits, &P.rows_per_split);
+  else
+    plan_splits(B, HG, rows_max, &P.splits, &P.rows_per_split);
   P.B = B;
   if (P.splits > 1) {
     const size_t need = round_up((size_t)B * P.splits * Hq * PART * sizeof(float), 256);
@@ -581,10 +1007,8 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   const int U = B * P.splits;
   dim3 grid((unsigned)(((U + 7) / 8) * 8 * HG));
   const size_t lds = sizeof(AttnLds);
-  if (kv->dtype == LIT_BF16) {
-    lit_status ls = allow_lds((const void*)attn_hg_kernel<0>, lds, who);
-    if (ls != LIT_OK) return ls;
-    attn_hg_kernel<0><<<grid, 256, lds, st>>>(P);
+  if (mh) {
+    attn_mh_kernel<<<dim3((unsigned)U), dim3(MH_THREADS), 0, st>>>(P);
   } else {
     lit_status ls = allow_lds((const void*)attn_hg_kernel<1>, lds, who);
     if (ls != LIT_OK) return ls;
@@ -592,7 +1016,7 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   }
   LIT_CHECK_LAUNCH(who);
   if (P.splits > 1) {
-    attn_combine_kernel<<<dim3((unsigned)(B * Hq)), dim3(512), 0, st>>>((const float*)ws, P.splits, Hq, out, lse);
+    attn_combine_kernel<<<dim3((unsigned)(B * Hq)), dim3(128), 0, st>>>((const float*)ws, P.splits, Hq, out, lse);
     LIT_CHECK_LAUNCH(who);
   }
   return LIT_OK;
