@@ -56,29 +56,34 @@ __device__ __forceinline__ float weighted_relu(const f32x4 (&acc)[MT], const flo
   return p;
 }
 
-__device__ __forceinline__ float sumsq_bf16x8(u32x4 v) {
-  float s = 0.f;
+// Sum of squares of eight bf16 values (exact products, fp32 adds).
+__device__ __forceinline__ float sumsq_bf16x8(u32x4 v, float s) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
+    const float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
     s = fmaf(a, a, s);
     s = fmaf(b, b, s);
   }
   return s;
 }
 
-// Loads the keys of 64 entries (4 column groups of 16) as B operands.
+// Upper bound of a key norm from a computed sum of squares m of 128 values:
+// 128 x 2^-126 covers any product lost below the normal range, and the factor
+// the fp32 rounding of the sum (<= 128 x 2^-24 relative) and of the sqrt.
+__device__ __forceinline__ float norm_bound(float m) { return sqrtf(m + 0x1p-119f) * (1.0f + 0x1p-16f); }
+
+// Loads the keys of 64 entries (4 column groups of 16) as B operands. Entries
+// at or past N load row N-1 instead (in bounds; their scores are never stored
+// and a real row's norm keeps the chunk bound valid), so no load sits in a
+// branch and the next step's loads can stay in flight during this step's math.
 __device__ __forceinline__ void load_keys_bf16(const uint16_t* kb, int base, int N, int g, int c,
                                                u32x4 (&kr)[4][4]) {
 #pragma unroll
   for (int G = 0; G < 4; G++) {
-    const int e = base + 16 * G + c;
+    const int e = min(base + 16 * G + c, N - 1);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (e < N) v = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 8 * g + 32 * j));
-      kr[G][j] = v;
-    }
+    for (int j = 0; j < 4; j++)
+      kr[G][j] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 8 * g + 32 * j));
   }
 }
 
@@ -100,7 +105,7 @@ __device__ __forceinline__ float store_score(float v, int e, int N, const uint8_
 }
 
 template <int MT, int S>
-__global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ w,
                                                              const uint16_t* __restrict__ k,
                                                              const uint8_t* __restrict__ allowed, int H,
@@ -114,9 +119,10 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
   const int g = lane >> 4, c = lane & 15;
   const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
   const int wg_base = blockIdx.x * (S * CHUNK);
-  // the first step's keys are in flight while q is staged
-  u32x4 kr[4][4];
-  load_keys_bf16(kb, wg_base + wid * 64, N, g, c, kr);
+  // the first step's keys are in flight while q is staged; later steps'
+  // keys are loaded one step ahead (two register buffers)
+  u32x4 kr[2][4][4];
+  load_keys_bf16(kb, wg_base + wid * 64, N, g, c, kr[0]);
 
   // Stage q as MFMA A operands: operand (mt, j) lane (hh + 16*gg) holds head
   // 16*mt + hh, dims 8*gg + 32*j .. +7.
@@ -137,10 +143,11 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
   float* sb = scores + (size_t)b * N;
   float* gm = hints ? hints + (size_t)b * hints_len + nchunks : nullptr;
 
-#pragma unroll 1
+#pragma unroll
   for (int s = 0; s < S; s++) {
     const int base = wg_base + s * CHUNK + wid * 64;
-    if (s > 0) load_keys_bf16(kb, base, N, g, c, kr);
+    if (s + 1 < S) load_keys_bf16(kb, base + CHUNK, N, g, c, kr[(s + 1) & 1]);
+    const u32x4 (&kc)[4][4] = kr[s & 1];
     f32x4 acc[4][MT];
 #pragma unroll
     for (int G = 0; G < 4; G++)
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
         const bf16x8 a = __builtin_bit_cast(bf16x8, qlds[(mt * 4 + j) * 64 + lane]);
 #pragma unroll
         for (int G = 0; G < 4; G++)
-          acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kr[G][j]),
+          acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kc[G][j]),
                                                                acc[G][mt], 0, 0, 0);
       }
     float my_score = 0.f, my_n2 = 0.f;
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
       const float p = weighted_relu<MT>(acc[G], wr);
       float n2 = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; j++) n2 += sumsq_bf16x8(kr[G][j]);
+      for (int j = 0; j < 4; j++) n2 = sumsq_bf16x8(kc[G][j], n2);
       n2 += __shfl_xor(n2, 16);
       n2 += __shfl_xor(n2, 32);
       if (G == g) {
@@ -182,8 +189,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
     const int chunk = blockIdx.x * S + tid;
     if (chunk < nchunks) {
       const float m = fmaxf(fmaxf(nmax[0][tid], nmax[1][tid]), fmaxf(nmax[2][tid], nmax[3][tid]));
-      // outward: sqrt and the fp32 sum of squares are each within a few ulp
-      hints[(size_t)b * hints_len + chunk] = sqrtf(m) * (1.0f + 0x1p-18f);
+      hints[(size_t)b * hints_len + chunk] = norm_bound(m);
     }
   }
 }
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
   __syncthreads();
   if (hints && tid == 0 && (int)blockIdx.x < nchunks) {
     const float mm = fmaxf(fmaxf(nmax[0], nmax[1]), fmaxf(nmax[2], nmax[3]));
-    hints[(size_t)b * hints_len + blockIdx.x] = sqrtf(mm) * (1.0f + 0x1p-18f);
+    hints[(size_t)b * hints_len + blockIdx.x] = norm_bound(mm);
   }
 }
 
@@ -361,9 +367,11 @@ extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed
   const int MT = (in->H + 15) / 16;
   hipStream_t hs = (hipStream_t)stream;
   if (in->dtype == LIT_BF16) {
-    // More chunks per workgroup when there is plenty of work: amortises the q staging.
+    // More chunks per workgroup when there is plenty of work: amortises the q
+    // staging and lets every workgroup keep its next chunk's keys in flight;
+    // about 512 workgroups (two per CU) keep all of them resident at once.
     const int64_t total = (int64_t)B * nchunks;
-    const int S = total >= 4096 ? 4 : (total >= 2048 ? 2 : 1);
+    const int S = total >= 2048 ? 4 : (total >= 1024 ? 2 : 1);
     dim3 grid((unsigned)cdiv(nchunks, S), (unsigned)B);
     switch (MT) {
       case 1: launch_bf16<1>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
