@@ -155,6 +155,27 @@ __device__ __forceinline__ double wave_sum_f64_dpp(double v) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
+// Butterfly steps across 16-lane rows with no LDS round trip: gfx950's
+// v_permlane16_swap / v_permlane32_swap, given the same value twice, hand every
+// lane the pair {v[l], v[l ^ 16]} (resp. l ^ 32); max and sum are symmetric in it.
+// Call them with every lane of the wave active (inactive lanes are not read).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Lane l's value of a double, wave-uniform.
 __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);

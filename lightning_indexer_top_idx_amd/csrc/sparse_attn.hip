@@ -535,27 +535,31 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   if (lse && tid == 0) lse[(size_t)b * Hq + h] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-// ---------------------------------------------------------------- all heads per workgroup (BF16 rows)
+// ---------------------------------------------------------------- BF16 rows, 16 heads per workgroup
 
-// One workgroup of 8 waves: one sequence, all (up to 64) query heads, one slice
-// of the row list, so every gathered row is read from memory once. Tiles of 64
-// rows go straight from global memory into LDS (global_load_lds, 16 bytes per
-// lane: one wave instruction moves one 1 KiB row), double-buffered in two
+// One workgroup of 4 waves: one sequence, one group of 16 query heads, one
+// slice of the row list. The head groups of a slice sit on one XCD (workgroup
+// ids equal modulo 8), so its L2 serves the slice's rows to all of them. Tiles
+// of 64 rows go straight from global memory into LDS (global_load_lds, 16 bytes
+// per lane: one wave instruction moves one 1 KiB row), double-buffered in two
 // separate LDS arrays so that reading one buffer never waits for the loads into
-// the other. Wave w owns head block hb = w & 3 (16 heads):
-//   scores: rows 32 (w >> 2) .. +31 of the tile, S^T = K Q^T on
-//           v_mfma_f32_16x16x32_bf16 (A = rows from LDS, B = queries in registers);
-//   output: dims 256 (w >> 2) .. +255, O += P V on the same instruction, with the
-//           V operand read transposed by ds_read_b64_tr_b16 (lane (g, s) points at
-//           row 8g + s/4 (+4), dims 4(s % 4) .. +3 of the 16-dim block).
-// The two waves of a head block agree on each head's running maximum through LDS.
-constexpr int MH_THREADS = 512;
+// the other. Wave w:
+//   scores: tile rows 16w .. +15, S^T = K Q^T on v_mfma_f32_16x16x32_bf16
+//           (A = rows from LDS, B = the 16 queries in registers), the 16 K-steps
+//           spread over four accumulators so that four MFMA chains are in flight;
+//   output: dims 128w .. +127, O^T += V^T P^T on the same instruction, so that
+//           a lane's output column is the head whose softmax it keeps; the V^T
+//           operand is read transposed by ds_read_b64_tr_b16 (lane (g, s) points
+//           at row 8g + s/4 (+4), dims 4(s % 4) .. +3 of the 16-dim block).
+// The four waves agree on each head's running maximum through LDS.
+constexpr int MH_THREADS = 256;
 constexpr int MH_WAVES = MH_THREADS / 64;
-constexpr int MH_ROWS_PER_WAVE = 64 / MH_WAVES;  // tile rows each wave loads
-constexpr int MH_TR = 64;        // rows per tile
-constexpr int MH_RS = 520;       // bf16 per LDS row: 1040 B keeps rows 16-byte aligned and spreads banks
-constexpr int MH_PS = MH_TR + 8;  // bf16 per LDS row of P (one head)
-constexpr int MH_TARGET = 256;   // workgroups aimed at: one per CU
+constexpr int MH_TR = 64;                           // rows per tile
+constexpr int MH_ROWS_PER_WAVE = MH_TR / MH_WAVES;  // tile rows each wave loads
+constexpr int MH_HEADS = 16;                        // query heads per workgroup
+constexpr int MH_RS = 520;         // bf16 per LDS row: 1040 B keeps rows 16-byte aligned and spreads banks
+constexpr int MH_PS = MH_TR + 8;   // bf16 per LDS row of P (one head)
+constexpr int MH_TARGET = 256;     // workgroups aimed at: one per CU
 constexpr int MH_ROWS_CAP = 1152;  // rows of a selection slice resolved up front (a multiple of MH_TR)
 
 struct MhTile {
@@ -588,133 +592,96 @@ __device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, c
   }
 }
 
-// The 64 query rows of sequence b (heads past Hq repeat the last head: their
-// outputs are never written) into a tile buffer, same layout as key rows.
-__device__ __forceinline__ void mh_issue_q(const AttnParams& P, int b, MhTile& T) {
+// The 16 query rows of head group hg of sequence b into rows 0..15 of a tile
+// buffer (heads past Hq repeat the last head: their outputs are never written).
+__device__ __forceinline__ void mh_issue_q(const AttnParams& P, int b, int hg, MhTile& T) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) {
-    const int h = MH_ROWS_PER_WAVE * wid + i;
-    const uint16_t* src = P.q + ((size_t)b * P.Hq + min(h, P.Hq - 1)) * LIT_KV_DIM + 8 * lane;
+  for (int i = 0; i < MH_HEADS / MH_WAVES; i++) {
+    const int hl = (MH_HEADS / MH_WAVES) * wid + i;
+    const int h = min(MH_HEADS * hg + hl, P.Hq - 1);
+    const uint16_t* src = P.q + ((size_t)b * P.Hq + h) * LIT_KV_DIM + 8 * lane;
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(T.v + h * MH_RS), 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(T.v + hl * MH_RS), 16, 0, 0);
   }
 }
 
 // vmcnt waits: the loads of one tile (of this wave) allowed to stay in flight, or none.
-static_assert(MH_ROWS_PER_WAVE == 8, "wait_tile encodes vmcnt(8)");
-__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x0F78); }  // vmcnt(8)
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+static_assert(MH_ROWS_PER_WAVE == 16, "wait_tile encodes vmcnt(16)");
+__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x4F70); }  // vmcnt(16): bits [15:14] = 1
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 struct MhState {
-  f32x4 o[2][8];   // O[head 32 hp + 16 x + 4g + i][dim 128 qt + 16 nt + c16]
-  float m_o[2];    // running max of head 32 hp + 16 x + c16 (the output's heads)
-  float m_s;       // running max of head 16 hb + c16 (the scored heads)
-  float l_run;     // this lane's share of the sum of head 16 hb + c16
+  f32x4 o[8];   // O[head c16][dim 128 w + 16 nt + 4g + i]
+  float m_run;  // running max of head c16 (log2 domain), the same in every wave
+  float l_run;  // this lane's share of head c16's sum (its wave's rows)
 };
 
-// Two roles per wave w, each sized so that the queries, the output and the
-// operands in flight fit in the registers of two waves per SIMD:
-//   scores  hb = w & 3, rh = w >> 2: heads 16 hb .. +15 (queries in registers)
-//           over tile rows 32 rh .. +31, S^T = K Q^T;
-//   output  hp = w & 1, qt = w >> 1: heads 32 hp .. +31 (two 16-head blocks x)
-//           over dims 128 qt .. +127, O += P V; each V read feeds both blocks.
-// Every wave follows the running maxima of the heads of both roles from the
-// same LDS values, so they agree without further exchange.
+// nvalid: rows 0 .. nvalid-1 of the tile are attended, the rest are padding.
 __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, int nvalid, const u32x4 (&qreg)[16],
-                                        MhState& S, float (*smax)[64], uint16_t* pbuf) {
+                                        MhState& S, float (*smax)[16], uint16_t* pbuf) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int hb = wid & 3, rh = wid >> 2, hp = wid & 1, qt = wid >> 1;
-  // S^T[rb]: rows 32 rh + 16 rb + 4g + i, head 16 hb + c16; the operands of
-  // K-step j + 2 are read while step j multiplies (the scheduling barrier keeps
-  // the compiler from hoisting every read, which would exhaust the registers)
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const uint16_t* krow = T.v + (32 * rh + c16) * MH_RS + 8 * g;
-  auto kld = [&](int j, int rb) { return *(const u32x4*)(krow + 16 * rb * MH_RS + 32 * j); };
-  u32x4 ka[2] = {kld(0, 0), kld(0, 1)}, kb[2] = {kld(1, 0), kld(1, 1)};
+  // S^T: rows 16w + 4g + i, head c16. K-step j accumulates into chain j % 4;
+  // the operands of step j + KD are read while step j multiplies (the
+  // scheduling barrier keeps the compiler from hoisting every read)
+  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const uint16_t* krow = T.v + (16 * wid + c16) * MH_RS + 8 * g;
+  constexpr int KD = 4;  // operand reads in flight ahead of the multiply
+  u32x4 kq[KD];
+#pragma unroll
+  for (int j = 0; j < KD; j++) kq[j] = *(const u32x4*)(krow + 32 * j);
 #pragma unroll
   for (int j = 0; j < 16; j++) {
-    u32x4 kc[2] = {ka[0], ka[1]};
-    if (j + 2 < 16) {
-      kc[0] = kld(j + 2, 0);
-      kc[1] = kld(j + 2, 1);
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++)
-      acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[rb]), __builtin_bit_cast(bf16x8, qreg[j]),
-                                                        acc[rb], 0, 0, 0);
-    ka[0] = kb[0];
-    ka[1] = kb[1];
-    kb[0] = kc[0];
-    kb[1] = kc[1];
+    const u32x4 ka = kq[j % KD];
+    if (j + KD < 16) kq[j % KD] = *(const u32x4*)(krow + 32 * (j + KD));
+    acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qreg[j]),
+                                                         acc[j & 3], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
-  float xs[2][4];
+  float xs[4];
   float tmax = -INFINITY;
 #pragma unroll
-  for (int rb = 0; rb < 2; rb++)
+  for (int i = 0; i < 4; i++) {
+    const bool valid = 16 * wid + 4 * g + i < nvalid;
+    const float sv = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+    xs[i] = valid ? sv * P.scale_log2 : -INFINITY;
+    tmax = fmaxf(tmax, xs[i]);
+  }
+  tmax = max_xor32(max_xor16(tmax));
+  if (g == 0) smax[wid][c16] = tmax;
+  lds_barrier();
+  const float m_new = fmaxf(S.m_run, fmaxf(fmaxf(smax[0][c16], smax[1][c16]), fmaxf(smax[2][c16], smax[3][c16])));
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2f(S.m_run - m_use);
+  S.m_run = m_new;
+  {
+    float psum = 0.f;
+    uint32_t hbits[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const bool valid = 32 * rh + 16 * rb + 4 * g + i < nvalid;
-      xs[rb][i] = valid ? acc[rb][i] * P.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, xs[rb][i]);
+      const float pv = exp2f(xs[i] - m_use);
+      psum += pv;
+      const uint32_t bits = __float_as_uint(pv);
+      hbits[i] = (bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16;  // round to nearest even
     }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  if (g == 0) smax[rh][16 * hb + c16] = tmax;
-  lds_barrier();
-  {
-    const int h = 16 * hb + c16;
-    const float m_new = fmaxf(S.m_s, fmaxf(smax[0][h], smax[1][h]));
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(S.m_s - m_use);
-    S.m_s = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-      uint32_t hbits[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float pv = exp2f(xs[rb][i] - m_use);
-        psum += pv;
-        const uint32_t bits = __float_as_uint(pv);
-        hbits[i] = (bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16;  // round to nearest even
-      }
-      u32x2 pk;
-      pk[0] = hbits[0] | (hbits[1] << 16);
-      pk[1] = hbits[2] | (hbits[3] << 16);
-      *(u32x2*)(pbuf + h * MH_PS + 32 * rh + 16 * rb + 4 * g) = pk;
-    }
+    u32x2 pk;
+    pk[0] = hbits[0] | (hbits[1] << 16);
+    pk[1] = hbits[2] | (hbits[3] << 16);
+    *(u32x2*)(pbuf + c16 * MH_PS + 16 * wid + 4 * g) = pk;
     S.l_run = S.l_run * alpha + psum;
   }
-  // the output role's heads: their maxima moved the same way
-  float alpha_o[2];
-#pragma unroll
-  for (int x = 0; x < 2; x++) {
-    const int h = 32 * hp + 16 * x + c16;
-    const float m_new = fmaxf(S.m_o[x], fmaxf(smax[0][h], smax[1][h]));
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    alpha_o[x] = exp2f(S.m_o[x] - m_use);
-    S.m_o[x] = m_new;
-  }
   lds_barrier();
-  // rescale O (heads 32 hp + 16 x + 4g + i) when a running max moved
-  if (__any(alpha_o[0] != 1.0f || alpha_o[1] != 1.0f)) {
+  // rescale O (this lane's head) when its running max moved
+  if (alpha != 1.0f) {
 #pragma unroll
-    for (int x = 0; x < 2; x++) {
-      float al[4];
+    for (int nt = 0; nt < 8; nt++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) al[i] = __shfl(alpha_o[x], 4 * g + i);
-#pragma unroll
-      for (int nt = 0; nt < 8; nt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) S.o[x][nt][i] *= al[i];
-    }
+      for (int i = 0; i < 4; i++) S.o[nt][i] *= alpha;
   }
   // O += P V over the 64 rows (two K-steps of 32, eight 16-dim blocks each);
-  // the V operands of step it + 2 are read while step it multiplies
-  const uint16_t* vbase = T.v + (8 * g + (c16 >> 2)) * MH_RS + 128 * qt + 4 * (c16 & 3);
+  // the V operands of step it + VD are read while step it multiplies
+  const uint16_t* vbase = T.v + (8 * g + (c16 >> 2)) * MH_RS + 128 * wid + 4 * (c16 & 3);
   auto vld = [&](int it) {
     const uint16_t* vb = vbase + 32 * (it >> 3) * MH_RS + 16 * (it & 7);
     const s16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4v*)vb);
@@ -727,39 +694,38 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
     return bv;
   };
   bf16x8 pa[2];
-  u32x4 va = vld(0), vbn = vld(1);
+#pragma unroll
+  for (int kk = 0; kk < 2; kk++) pa[kk] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pbuf + c16 * MH_PS + 32 * kk + 8 * g));
+  constexpr int VD = 4;  // transposed reads in flight ahead of the multiply
+  u32x4 vq[VD];
+#pragma unroll
+  for (int it = 0; it < VD; it++) vq[it] = vld(it);
 #pragma unroll
   for (int it = 0; it < 16; it++) {
-    const int kk = it >> 3, nt = it & 7;
-    if (nt == 0)
-#pragma unroll
-      for (int x = 0; x < 2; x++)
-        pa[x] = __builtin_bit_cast(bf16x8, *(const u32x4*)(pbuf + (32 * hp + 16 * x + c16) * MH_PS + 32 * kk + 8 * g));
-    u32x4 vc = va;
-    if (it + 2 < 16) vc = vld(it + 2);
-#pragma unroll
-    for (int x = 0; x < 2; x++)
-      S.o[x][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[x], __builtin_bit_cast(bf16x8, va), S.o[x][nt], 0, 0, 0);
-    va = vbn;
-    vbn = vc;
+    const u32x4 va = vq[it % VD];
+    if (it + VD < 16) vq[it % VD] = vld(it + VD);
+    S.o[it & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pa[it >> 3], S.o[it & 7], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   __shared__ MhTile TA, TB;
-  __shared__ __align__(16) uint16_t pbuf[64 * MH_PS];
+  __shared__ __align__(16) uint16_t pbuf[MH_HEADS * MH_PS];
   __shared__ __align__(16) int rows_all[MH_ROWS_CAP];  // the slice's rows, or a ring of 4 tiles for long dense slices
   __shared__ uint32_t dup[LIT_MAX_WINDOW / 32];
-  __shared__ float smax[2][64];
-  __shared__ float ssum[2][64];
+  __shared__ float smax[MH_WAVES][16];
+  __shared__ float ssum[MH_WAVES][16];
   __shared__ int part[16];
-  const int b = blockIdx.x / P.splits, s = blockIdx.x % P.splits;
+  const int HG = (P.Hq + MH_HEADS - 1) / MH_HEADS;
+  int u, hg;
+  if (!decode_unit(blockIdx.x, HG, P.B * P.splits, &u, &hg)) return;
+  const int b = u / P.splits, s = u % P.splits;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15, hb = wid & 3, rh = wid >> 2, hp = wid & 1, qt = wid >> 1;
+  const int g = lane >> 4, c16 = lane & 15;
   const int Hq = P.Hq;
   // the queries travel first, into the second tile buffer, while the row list is built
-  mh_issue_q(P, b, TB);
+  mh_issue_q(P, b, hg, TB);
 
   RowList RL;
   RL.dense = P.ids == nullptr;
@@ -798,32 +764,35 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   const bool all_rows = nrows <= MH_ROWS_CAP;
   int n = nrows;  // attended rows of the slice
   if (all_rows) {
-    int r[MH_ROWS_CAP / MH_THREADS + 1];
+    constexpr int PER = (MH_ROWS_CAP + MH_THREADS - 1) / MH_THREADS;
+    int r[PER];
     int cnt = 0;
 #pragma unroll
-    for (int k = 0; k < MH_ROWS_CAP / MH_THREADS + 1; k++) {
+    for (int k = 0; k < PER; k++) {
       const int i = tid + MH_THREADS * k;
       r[k] = i < nrows ? RL.row(p0 + i) : -1;
       cnt += r[k] >= 0;
     }
-    int pos = block_excl_scan1<MH_THREADS / 64>(cnt, part, &n);
+    int pos = block_excl_scan1<MH_WAVES>(cnt, part, &n);
 #pragma unroll
-    for (int k = 0; k < MH_ROWS_CAP / MH_THREADS + 1; k++)
+    for (int k = 0; k < PER; k++)
       if (r[k] >= 0) rows_all[pos++] = r[k];
     lds_barrier();
     const int upto = (n + MH_TR - 1) / MH_TR * MH_TR;
     for (int i = n + tid; i < upto; i += MH_THREADS) rows_all[i] = -1;
-  } else if (tid < 2 * MH_TR) {
-    const int p = p0 + tid;
-    rows_all[tid] = p < p1 ? p : -1;
+  } else {
+    for (int i = tid; i < 2 * MH_TR; i += MH_THREADS) {
+      const int p = p0 + i;
+      rows_all[i] = p < p1 ? p : -1;
+    }
   }
-  // the queries of head block hb as B operands, from the second tile buffer:
-  // K-step j, lane (g, c16) holds dims 32j + 8g .. +7 of head 16 hb + c16
+  // the queries as B operands, from the second tile buffer: K-step j, lane
+  // (g, c16) holds dims 32j + 8g .. +7 of head c16 of the group
   wait_vm0();
   lds_barrier();
   u32x4 qreg[16];
 #pragma unroll
-  for (int j = 0; j < 16; j++) qreg[j] = *(const u32x4*)(TB.v + (16 * hb + c16) * MH_RS + 32 * j + 8 * g);
+  for (int j = 0; j < 16; j++) qreg[j] = *(const u32x4*)(TB.v + c16 * MH_RS + 32 * j + 8 * g);
   lds_barrier();
   const size_t seq_rows = (size_t)b * P.N;
   // (one LDS array, so that the compiler can tell its reads from the tile loads in flight)
@@ -833,12 +802,8 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
 
   MhState S;
 #pragma unroll
-  for (int x = 0; x < 2; x++) {
-#pragma unroll
-    for (int nt = 0; nt < 8; nt++) S.o[x][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    S.m_o[x] = -INFINITY;
-  }
-  S.m_s = -INFINITY;
+  for (int nt = 0; nt < 8; nt++) S.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  S.m_run = -INFINITY;
   S.l_run = 0.f;
 
   // tile t uses buffer t & 1; tile t + 2 is issued into the same buffer once
@@ -865,43 +830,36 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
     }
   }
 
-  // l per head: the two row halves of the scoring role
-  {
-    float lw = S.l_run;
-    lw += __shfl_xor(lw, 16);
-    lw += __shfl_xor(lw, 32);
-    if (g == 0) ssum[rh][16 * hb + c16] = lw;
-  }
+  // l per head: the four waves' rows
+  const float lw = sum_xor32(sum_xor16(S.l_run));  // every lane takes part in the lane swaps
+  if (g == 0) ssum[wid][c16] = lw;
   lds_barrier();
+  const int hh = MH_HEADS * hg + c16;
+  const float Ls = (ssum[0][c16] + ssum[1][c16]) + (ssum[2][c16] + ssum[3][c16]);
+  if (hh < Hq) {
+    if (P.splits == 1) {
+      float* oh = P.out + ((size_t)b * Hq + hh) * LIT_KV_DIM + 128 * wid + 4 * g;
+      const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
-  for (int x = 0; x < 2; x++)
+      for (int nt = 0; nt < 8; nt++) *(f32x4*)(oh + 16 * nt) = S.o[nt] * inv;
+      if (P.lse && wid == 0 && g == 0) P.lse[(size_t)b * Hq + hh] = Ls > 0.f ? S.m_run * LN2 + logf(Ls) : -INFINITY;
+    } else {
+      float* ph = P.part + (((size_t)b * P.splits + s) * Hq + hh) * PART;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int hh = 32 * hp + 16 * x + 4 * g + i;
-      const float Ls = ssum[0][hh] + ssum[1][hh];
-      const float Ms = __shfl(S.m_o[x], 4 * g + i);
-      if (hh >= Hq) continue;
-      if (P.splits == 1) {
-        float* oh = P.out + ((size_t)b * Hq + hh) * LIT_KV_DIM + 128 * qt;
-        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-#pragma unroll
-        for (int nt = 0; nt < 8; nt++) oh[16 * nt + c16] = S.o[x][nt][i] * inv;
-        if (P.lse && qt == 0 && c16 == 0) P.lse[(size_t)b * Hq + hh] = Ls > 0.f ? Ms * LN2 + logf(Ls) : -INFINITY;
-      } else {
-        float* ph = P.part + (((size_t)b * P.splits + s) * Hq + hh) * PART;
-#pragma unroll
-        for (int nt = 0; nt < 8; nt++) ph[128 * qt + 16 * nt + c16] = S.o[x][nt][i];
-        if (qt == 0 && c16 == 0) {
-          ph[512] = Ms;
-          ph[513] = Ls;
-        }
+      for (int nt = 0; nt < 8; nt++) *(f32x4*)(ph + 128 * wid + 16 * nt + 4 * g) = S.o[nt];
+      if (wid == 0 && g == 0) {
+        ph[512] = S.m_run;
+        ph[513] = Ls;
       }
     }
+  }
 }
 
-void plan_mh(int B, int rows_max, bool sparse, int* splits, int* rows_per_split) {
+// Slices of the row list per sequence: enough workgroups (slices x head groups)
+// to fill the chip, and selection slices (sparse) no longer than MH_ROWS_CAP rows.
+void plan_mh(int B, int HG, int rows_max, bool sparse, int* splits, int* rows_per_split) {
   const int tiles = std::max(1, (rows_max + MH_TR - 1) / MH_TR);
-  const int want = std::max(1, (MH_TARGET + B - 1) / B);
+  const int want = std::max(1, (MH_TARGET + B * HG - 1) / (B * HG));
   int s = std::min(tiles, want);
   if (sparse) s = std::max(s, (tiles * MH_TR + MH_ROWS_CAP - 1) / MH_ROWS_CAP);
   const int tiles_per = (tiles + s - 1) / s;
@@ -929,9 +887,10 @@ extern "C" size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
   int s1, s2, rps;
   plan_splits(B, (Hq + HG_HEADS - 1) / HG_HEADS, N + LIT_MAX_WINDOW, &s1, &rps);
-  plan_mh(B, N + LIT_MAX_WINDOW, true, &s2, &rps);
+  const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
+  plan_mh(B, HGm, N + LIT_MAX_WINDOW, true, &s2, &rps);
   int s3;
-  plan_mh(B, N, false, &s3, &rps);
+  plan_mh(B, HGm, N, false, &s3, &rps);
   s2 = std::max(s2, s3);
   const int s = std::max(s1, s2);
   if (s <= 1) return 256;
@@ -977,9 +936,9 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   const int rows_max = ids ? (k_cap + Wc) : N;
   AttnParams P;
   const int HG = (Hq + HG_HEADS - 1) / HG_HEADS;
-  const bool mh = kv->dtype == LIT_BF16;  // BF16 rows: all heads per workgroup
+  const bool mh = kv->dtype == LIT_BF16;  // BF16 rows: the direct-to-LDS kernel
   if (mh)
-    plan_mh(B, rows_max, ids != nullptr, &P.splits, &P.rows_per_split);
+    plan_mh(B, (Hq + MH_HEADS - 1) / MH_HEADS, rows_max, ids != nullptr, &P.splits, &P.rows_per_split);
   else
     plan_splits(B, HG, rows_max, &P.splits, &P.rows_per_split);
   P.B = B;
@@ -1008,7 +967,8 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   dim3 grid((unsigned)(((U + 7) / 8) * 8 * HG));
   const size_t lds = sizeof(AttnLds);
   if (mh) {
-    attn_mh_kernel<<<dim3((unsigned)U), dim3(MH_THREADS), 0, st>>>(P);
+    const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
+    attn_mh_kernel<<<dim3((unsigned)(((U + 7) / 8) * 8 * HGm)), dim3(MH_THREADS), 0, st>>>(P);
   } else {
     lit_status ls = allow_lds((const void*)attn_hg_kernel<1>, lds, who);
     if (ls != LIT_OK) return ls;
