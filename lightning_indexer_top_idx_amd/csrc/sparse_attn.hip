@@ -400,53 +400,60 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
 }
 
 // Log-sum-exp merge of the row slices of one (sequence, head): 128 threads,
-// four dims each. Every slice's (m, l) and partial output are requested at
-// once (no load waits on another), then merged in slice order.
-constexpr int COMBINE_MAX = 8;  // slices merged per pass (all of a pass requested at once)
+// four dims each. Up to SM slices are merged per pass; every load of a pass
+// (each slice's m, l and four partial dims) is requested before any is used.
+template <int SM>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int splits, int Hq,
                                                            float* __restrict__ out, float* __restrict__ lse) {
   const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d4 = threadIdx.x;
   const float* base = part + ((size_t)b * splits * Hq + h) * PART;
   const size_t stride = (size_t)Hq * PART;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < splits; s0 += COMBINE_MAX) {
-    float mv[COMBINE_MAX];
-#pragma unroll
-    for (int i = 0; i < COMBINE_MAX; i++) mv[i] = s0 + i < splits ? base[(s0 + i) * stride + 512] : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < COMBINE_MAX; i++) M = fmaxf(M, mv[i]);
-  }
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < splits; s0 += COMBINE_MAX) {
-      f32x4 ov[COMBINE_MAX];
-      float ml[COMBINE_MAX][2];
+  for (int s0 = 0; s0 < splits; s0 += SM) {
+    f32x4 ov[SM];
+    float mv[SM], lv[SM];
 #pragma unroll
-      for (int i = 0; i < COMBINE_MAX; i++) {
-        const bool in = s0 + i < splits;
-        const float* ps = base + (size_t)(in ? s0 + i : 0) * stride;
-        ov[i] = *(const f32x4*)(ps + 4 * d4);
-        ml[i][0] = in ? ps[512] : -INFINITY;
-        ml[i][1] = ps[513];
-      }
+    for (int i = 0; i < SM; i++) {
+      const float* ps = base + (size_t)min(s0 + i, splits - 1) * stride;
+      ov[i] = *(const f32x4*)(ps + 4 * d4);
+      mv[i] = s0 + i < splits ? ps[512] : -INFINITY;
+      lv[i] = ps[513];
+    }
+    float Mp = M;
 #pragma unroll
-      for (int i = 0; i < COMBINE_MAX; i++) {
-        const float wgt = exp2f(ml[i][0] - M);  // empty slices and padding have m = -inf -> 0
-        if (wgt > 0.f) {
-          L += wgt * ml[i][1];
+    for (int i = 0; i < SM; i++) Mp = fmaxf(Mp, mv[i]);
+    if (Mp == -INFINITY) continue;
+    const float r = exp2f(M - Mp);  // earlier passes, rescaled (0 when M was -inf)
+    L *= r;
 #pragma unroll
-          for (int j = 0; j < 4; j++) acc[j] += wgt * ov[i][j];
-        }
+    for (int j = 0; j < 4; j++) acc[j] *= r;
+#pragma unroll
+    for (int i = 0; i < SM; i++) {
+      const float wgt = exp2f(mv[i] - Mp);  // empty slices and padding have m = -inf -> 0
+      if (wgt > 0.f) {
+        L += wgt * lv[i];
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[j] += wgt * ov[i][j];
       }
     }
+    M = Mp;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  f32x4 o;
-#pragma unroll
-  for (int j = 0; j < 4; j++) o[j] = acc[j] * inv;
-  *(f32x4*)(out + ((size_t)b * Hq + h) * LIT_KV_DIM + 4 * d4) = o;
+  *(f32x4*)(out + ((size_t)b * Hq + h) * LIT_KV_DIM + 4 * d4) = acc * inv;
   if (lse && d4 == 0) lse[(size_t)b * Hq + h] = L > 0.f ? M * LN2 + logf(L) : -INFINITY;
+}
+
+void launch_combine(const float* part, int B, int splits, int Hq, float* out, float* lse, hipStream_t st) {
+  const dim3 grid((unsigned)(B * Hq)), block(128);
+  if (splits <= 2)
+    attn_combine_kernel<2><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+  else if (splits <= 4)
+    attn_combine_kernel<4><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+  else if (splits <= 8)
+    attn_combine_kernel<8><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+  else
+    attn_combine_kernel<16><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
 }
 
 // FP32 rows and queries: one workgroup per (sequence, head), fp32 VALU with an
@@ -976,7 +983,7 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   }
   LIT_CHECK_LAUNCH(who);
   if (P.splits > 1) {
-    attn_combine_kernel<<<dim3((unsigned)(B * Hq)), dim3(128), 0, st>>>((const float*)ws, P.splits, Hq, out, lse);
+    launch_combine((const float*)ws, B, P.splits, Hq, out, lse, st);
     LIT_CHECK_LAUNCH(who);
   }
   return LIT_OK;
