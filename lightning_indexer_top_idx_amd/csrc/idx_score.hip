@@ -30,6 +30,7 @@ namespace lit {
 namespace {
 
 constexpr int CHUNK = LIT_KNORM_CHUNK;  // 256 entries: 4 waves x 64
+constexpr int KEY_RING = 4;             // key register buffers per wave (half-steps of 32 entries)
 static_assert(CHUNK == 256, "kernel tiling assumes 256-entry chunks");
 
 // Per-lane weights of the heads this lane's accumulators hold.
@@ -42,44 +43,37 @@ __device__ __forceinline__ void load_lane_weights(const float* wlds, float (&wr)
     for (int i = 0; i < 4; i++) wr[mt][i] = wlds[16 * mt + 4 * g + i];
 }
 
+// max(x, 0) as an integer max on the bits: negative values (and -0) become +0.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Epilogue shared by both dtypes: weighted ReLU over the lane's heads, summed
-// across the four 16-lane groups (which hold the other heads of the same entry).
+// across the four 16-lane groups (which hold the other heads of the same
+// entry) by lane swaps; every lane of the entry ends with the same sum.
 template <int MT>
 __device__ __forceinline__ float weighted_relu(const f32x4 (&acc)[MT], const float (&wr)[MT][4]) {
   float p = 0.f;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) p = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), p);
-  p += __shfl_xor(p, 16);
-  p += __shfl_xor(p, 32);
-  return p;
-}
-
-// Sum of squares of eight bf16 values (exact products, fp32 adds).
-__device__ __forceinline__ float sumsq_bf16x8(u32x4 v, float s) {
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const float a = bf16_lo(v[i]), b = bf16_hi(v[i]);
-    s = fmaf(a, a, s);
-    s = fmaf(b, b, s);
-  }
-  return s;
+    for (int i = 0; i < 4; i++) p = fmaf(wr[mt][i], relu_bits(acc[mt][i]), p);
+  return sum_xor32(sum_xor16(p));
 }
 
 // Upper bound of a key norm from a computed sum of squares m of 128 values:
 // 128 x 2^-126 covers any product lost below the normal range, and the factor
-// the fp32 rounding of the sum (<= 128 x 2^-24 relative) and of the sqrt.
-__device__ __forceinline__ float norm_bound(float m) { return sqrtf(m + 0x1p-119f) * (1.0f + 0x1p-16f); }
+// the fp32 rounding of the sum (<= 128 x 2^-24 relative for sequential adds,
+// taken four times over for the matrix cores' accumulation, as for the scores)
+// and of the sqrt.
+__device__ __forceinline__ float norm_bound(float m) { return sqrtf(m + 0x1p-119f) * (1.0f + 0x1p-14f); }
 
-// Loads the keys of 64 entries (4 column groups of 16) as B operands. Entries
+// Loads the keys of 32 entries (2 column groups of 16) as B operands. Entries
 // at or past N load row N-1 instead (in bounds; their scores are never stored
 // and a real row's norm keeps the chunk bound valid), so no load sits in a
-// branch and the next step's loads can stay in flight during this step's math.
-__device__ __forceinline__ void load_keys_bf16(const uint16_t* kb, int base, int N, int g, int c,
-                                               u32x4 (&kr)[4][4]) {
+// branch and later half-steps' loads stay in flight during this one's math.
+__device__ __forceinline__ void load_keys_half(const uint16_t* kb, int base, int N, int g, int c,
+                                               u32x4 (&kr)[2][4]) {
 #pragma unroll
-  for (int G = 0; G < 4; G++) {
+  for (int G = 0; G < 2; G++) {
     const int e = min(base + 16 * G + c, N - 1);
 #pragma unroll
     for (int j = 0; j < 4; j++)
@@ -89,7 +83,8 @@ __device__ __forceinline__ void load_keys_bf16(const uint16_t* kb, int base, int
 
 // Scores of the lane's entry (lane = 16 g + c holds entry base + lane): the
 // allowed mask applied, the score stored, and the group maximum returned in
-// every lane of the 16-lane group (entries at or past N count as -inf).
+// the group's last lane (c = 15; a running maximum along the 16-lane row on
+// DPP shifts; entries at or past N count as -inf).
 __device__ __forceinline__ float store_score(float v, int e, int N, const uint8_t* ab, float* sb) {
   if (e < N) {
     if (ab && ab[e] == 0) v = -INFINITY;
@@ -97,20 +92,26 @@ __device__ __forceinline__ float store_score(float v, int e, int N, const uint8_
   } else {
     v = -INFINITY;
   }
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+  constexpr uint32_t NEG_INF = 0xff800000u;
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x111>(NEG_INF, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x112>(NEG_INF, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x114>(NEG_INF, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x118>(NEG_INF, __float_as_uint(v))));
   return v;
 }
 
-template <int MT, int S>
+// A wave works through its 64 entries of each chunk in two half-steps of 32
+// (two column groups); its keys pass through a ring of NB register buffers, so
+// NB - 1 half-steps (NB - 1 times 8 KB per wave) are in flight while one is
+// multiplied.
+template <int MT, int S, int NB>
 __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ w,
                                                              const uint16_t* __restrict__ k,
                                                              const uint8_t* __restrict__ allowed, int H,
                                                              int N, int nchunks, float* __restrict__ scores,
                                                              float* __restrict__ hints, int hints_len) {
+  constexpr int NH = 2 * S;  // half-steps per wave
   __shared__ u32x4 qlds[MT * 4 * 64];
   __shared__ float wlds[64];
   __shared__ float nmax[4][S];
@@ -119,10 +120,13 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   const int g = lane >> 4, c = lane & 15;
   const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
   const int wg_base = blockIdx.x * (S * CHUNK);
-  // the first step's keys are in flight while q is staged; later steps'
-  // keys are loaded one step ahead (two register buffers)
-  u32x4 kr[2][4][4];
-  load_keys_bf16(kb, wg_base + wid * 64, N, g, c, kr[0]);
+  // half-step h: entries hbase(h) .. +31 of chunk h/2
+  auto hbase = [&](int h) { return wg_base + (h >> 1) * CHUNK + wid * 64 + 32 * (h & 1); };
+  // the first NB - 1 half-steps' keys are in flight while q is staged
+  u32x4 kr[NB][2][4];
+#pragma unroll
+  for (int h = 0; h < NB - 1; h++)
+    if (h < NH) load_keys_half(kb, hbase(h), N, g, c, kr[h]);
 
   // Stage q as MFMA A operands: operand (mt, j) lane (hh + 16*gg) holds head
   // 16*mt + hh, dims 8*gg + 32*j .. +7.
@@ -143,14 +147,16 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   float* sb = scores + (size_t)b * N;
   float* gm = hints ? hints + (size_t)b * hints_len + nchunks : nullptr;
 
+  float my_score = 0.f, my_n2 = 0.f;
 #pragma unroll
-  for (int s = 0; s < S; s++) {
-    const int base = wg_base + s * CHUNK + wid * 64;
-    if (s + 1 < S) load_keys_bf16(kb, base + CHUNK, N, g, c, kr[(s + 1) & 1]);
-    const u32x4 (&kc)[4][4] = kr[s & 1];
-    f32x4 acc[4][MT];
+  for (int h = 0; h < NH; h++) {
+    if (h + NB - 1 < NH) load_keys_half(kb, hbase(h + NB - 1), N, g, c, kr[(h + NB - 1) % NB]);
+    // keep the loads ahead of this half-step's math (the scheduler would sink them)
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x4 (&kc)[2][4] = kr[h % NB];
+    f32x4 acc[2][MT];
 #pragma unroll
-    for (int G = 0; G < 4; G++)
+    for (int G = 0; G < 2; G++)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) acc[G][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -159,30 +165,40 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
       for (int j = 0; j < 4; j++) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, qlds[(mt * 4 + j) * 64 + lane]);
 #pragma unroll
-        for (int G = 0; G < 4; G++)
+        for (int G = 0; G < 2; G++)
           acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kc[G][j]),
                                                                acc[G][mt], 0, 0, 0);
       }
-    float my_score = 0.f, my_n2 = 0.f;
+    // key norms: the 16 x 16 Gram matrix of each column group on the matrix
+    // cores (A = B = the group's key registers). Its largest entry is its
+    // largest diagonal entry (Cauchy-Schwarz), the largest squared norm.
+    f32x4 gram[2];
 #pragma unroll
-    for (int G = 0; G < 4; G++) {
-      const float p = weighted_relu<MT>(acc[G], wr);
-      float n2 = 0.f;
+    for (int G = 0; G < 2; G++) {
+      gram[G] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; j++) n2 = sumsq_bf16x8(kc[G][j], n2);
-      n2 += __shfl_xor(n2, 16);
-      n2 += __shfl_xor(n2, 32);
-      if (G == g) {
-        my_score = p;
-        my_n2 = n2;
-      }
+      for (int j = 0; j < 4; j++)
+        gram[G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[G][j]),
+                                                          __builtin_bit_cast(bf16x8, kc[G][j]), gram[G], 0, 0, 0);
     }
-    // lane = 16*g + c holds entry base + lane
-    const int e = base + lane;
-    const float gmax = store_score(my_score, e, N, ab, sb);
-    if (gm && c == 0 && base + 16 * g < N) gm[(base + 16 * g) / 16] = gmax;
-    const float m = wave_max(my_n2);
-    if (lane == 0) nmax[wid][s] = m;
+#pragma unroll
+    for (int G = 0; G < 2; G++) {
+      const float p = weighted_relu<MT>(acc[G], wr);
+      if (2 * (h & 1) + G == g) my_score = p;  // the column group that holds this lane's entry
+#pragma unroll
+      for (int i = 0; i < 4; i++) my_n2 = fmaxf(my_n2, gram[G][i]);
+    }
+    if (h & 1) {
+      // chunk h/2 done: lane = 16*g + c holds entry base + lane
+      const int s = h >> 1;
+      const int base = wg_base + s * CHUNK + wid * 64;
+      const int e = base + lane;
+      const float gmax = store_score(my_score, e, N, ab, sb);
+      if (gm && c == 15 && base + 16 * g < N) gm[(base + 16 * g) / 16] = gmax;
+      const float m = wave_max(my_n2);
+      if (lane == 0) nmax[wid][s] = m;
+      my_n2 = 0.f;
+    }
   }
   __syncthreads();
   if (hints && tid < S) {
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
   }
   const int e = base + lane;
   const float gmax = store_score(my_score, e, N, ab, sb);
-  if (hints && c == 0 && base + 16 * g < N) hints[(size_t)b * hints_len + nchunks + (base + 16 * g) / 16] = gmax;
+  if (hints && c == 15 && base + 16 * g < N) hints[(size_t)b * hints_len + nchunks + (base + 16 * g) / 16] = gmax;
   const float m = wave_max(my_n2);
   if (lane == 0) nmax[wid] = m;
   __syncthreads();
@@ -335,11 +351,11 @@ static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, 
   const uint16_t* q = (const uint16_t*)in->q;
   const uint16_t* k = (const uint16_t*)in->k;
   if (S == 4)
-    idx_score_bf16_kernel<MT, 4><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
+    idx_score_bf16_kernel<MT, 4, KEY_RING><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
   else if (S == 2)
-    idx_score_bf16_kernel<MT, 2><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
+    idx_score_bf16_kernel<MT, 2, KEY_RING><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
   else
-    idx_score_bf16_kernel<MT, 1><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
+    idx_score_bf16_kernel<MT, 1, KEY_RING><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
 }
 
 template <int MT>
