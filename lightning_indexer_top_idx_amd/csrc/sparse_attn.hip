@@ -575,30 +575,6 @@ struct MhTile {
 
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 
-// Wave w issues the loads of its share of the tile rows (one instruction per row).
-// Rows that are not attended (-1) load row 0 instead: their weight is 0, and a
-// finite value keeps 0 * value = 0.
-__device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, const int* rws, MhTile& T) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  // the row ids first: no LDS read sits between the loads
-  int rid[MH_ROWS_PER_WAVE];
-#pragma unroll
-  for (int v = 0; v < MH_ROWS_PER_WAVE / 4; v++) {
-    const u32x4 r4 = *(const u32x4*)(rws + MH_ROWS_PER_WAVE * wid + 4 * v);
-#pragma unroll
-    for (int i = 0; i < 4; i++) rid[4 * v + i] = __builtin_amdgcn_readfirstlane((int)r4[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) {
-    const int slot = MH_ROWS_PER_WAVE * wid + i;
-    const int r = rid[i];
-    const size_t rr = seq_rows + (size_t)(r >= 0 ? r : 0);
-    const uint16_t* src = (const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane;
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(T.v + slot * MH_RS), 16, 0, 0);
-  }
-}
-
 // The 16 query rows of head group hg of sequence b into rows 0..15 of a tile
 // buffer (heads past Hq repeat the last head: their outputs are never written).
 __device__ __forceinline__ void mh_issue_q(const AttnParams& P, int b, int hg, MhTile& T) {
@@ -613,10 +589,7 @@ __device__ __forceinline__ void mh_issue_q(const AttnParams& P, int b, int hg, M
   }
 }
 
-// vmcnt waits: the loads of one tile (of this wave) allowed to stay in flight, or none.
-static_assert(MH_ROWS_PER_WAVE == 16, "wait_tile encodes vmcnt(16)");
-__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(0x4F70); }  // vmcnt(16): bits [15:14] = 1
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 struct MhState {
   f32x4 o[8];   // O[head c16][dim 128 w + 16 nt + 4g + i]
@@ -624,9 +597,44 @@ struct MhState {
   float l_run;  // this lane's share of head c16's sum (its wave's rows)
 };
 
+// The row ids of this wave's share of a tile (wave-uniform), read before any
+// of their loads is issued.
+__device__ __forceinline__ void mh_row_ids(const int* rws, int (&rid)[MH_ROWS_PER_WAVE]) {
+  const int wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int v = 0; v < MH_ROWS_PER_WAVE / 4; v++) {
+    const u32x4 r4 = *(const u32x4*)(rws + MH_ROWS_PER_WAVE * wid + 4 * v);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rid[4 * v + i] = __builtin_amdgcn_readfirstlane((int)r4[i]);
+  }
+}
+
+// One tile row (slot i of this wave's share) straight into LDS. A row that is
+// not attended (-1) loads row 0 instead: its weight is 0, and a finite value
+// keeps 0 * value = 0.
+__device__ __forceinline__ void mh_issue_row(const AttnParams& P, size_t seq_rows, int r, int i, MhTile& T) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const size_t rr = seq_rows + (size_t)(r >= 0 ? r : 0);
+  const uint16_t* src = (const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane;
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)(T.v + (MH_ROWS_PER_WAVE * wid + i) * MH_RS),
+                                   16, 0, 0);
+}
+
+// This wave's share of a whole tile.
+__device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, const int* rws, MhTile& T) {
+  int rid[MH_ROWS_PER_WAVE];
+  mh_row_ids(rws, rid);
+#pragma unroll
+  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) mh_issue_row(P, seq_rows, rid[i], i, T);
+}
+
 // nvalid: rows 0 .. nvalid-1 of the tile are attended, the rest are padding.
+// When NT is given, this wave's loads of that next tile (rows nrid) are issued
+// one per K-step of the scores, so that their issue overlaps the multiplies.
 __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, int nvalid, const u32x4 (&qreg)[16],
-                                        MhState& S, float (*smax)[16], uint16_t* pbuf) {
+                                        MhState& S, float (*smax)[16], uint16_t* pbuf, MhTile* NT, size_t seq_rows,
+                                        const int (&nrid)[MH_ROWS_PER_WAVE]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   // S^T: rows 16w + 4g + i, head c16. K-step j accumulates into chain j % 4;
@@ -635,6 +643,7 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
   f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const uint16_t* krow = T.v + (16 * wid + c16) * MH_RS + 8 * g;
   constexpr int KD = 4;  // operand reads in flight ahead of the multiply
+  static_assert(MH_ROWS_PER_WAVE == 16, "one next-tile row per K-step");
   u32x4 kq[KD];
 #pragma unroll
   for (int j = 0; j < KD; j++) kq[j] = *(const u32x4*)(krow + 32 * j);
@@ -642,6 +651,7 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
   for (int j = 0; j < 16; j++) {
     const u32x4 ka = kq[j % KD];
     if (j + KD < 16) kq[j % KD] = *(const u32x4*)(krow + 32 * (j + KD));
+    if (NT) mh_issue_row(P, seq_rows, nrid[j], j, *NT);
     acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qreg[j]),
                                                          acc[j & 3], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -805,7 +815,6 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   // (one LDS array, so that the compiler can tell its reads from the tile loads in flight)
   auto tile_rows = [&](int tt) -> const int* { return rows_all + MH_TR * (all_rows ? tt : (tt & 3)); };
   if (0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
-  if (MH_TR < n) mh_issue(P, seq_rows, tile_rows(1), TB);
 
   MhState S;
 #pragma unroll
@@ -813,8 +822,9 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   S.m_run = -INFINITY;
   S.l_run = 0.f;
 
-  // tile t uses buffer t & 1; tile t + 2 is issued into the same buffer once
-  // every wave is done with tile t
+  // tile t uses buffer t & 1; the loads of tile t + 1 go into the other
+  // buffer (free since the barrier that ended tile t - 1) during tile t's
+  // score multiplies, so each tile waits only for its own loads
 #pragma unroll 1
   for (int t = 0; MH_TR * t < n; t += 2) {
 #pragma unroll
@@ -822,18 +832,18 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
       const int tt = t + ab;
       const int q0 = MH_TR * tt;
       if (q0 >= n) break;
-      if (q0 + MH_TR < n)
-        wait_tile();  // tile tt + 1 may stay in flight
-      else
-        wait_vm0();
+      wait_vm0();
       if (!all_rows && tid < MH_TR) {
         const int p = p0 + q0 + 2 * MH_TR + tid;
         rows_all[MH_TR * ((tt + 2) & 3) + tid] = p < p1 ? p : -1;
       }
       lds_barrier();
-      mh_tile(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf);
+      const bool more = q0 + MH_TR < n;
+      int nrid[MH_ROWS_PER_WAVE];
+      if (more) mh_row_ids(tile_rows(tt + 1), nrid);
+      mh_tile(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf, more ? (ab == 0 ? &TB : &TA) : nullptr, seq_rows,
+              nrid);
       lds_barrier();
-      if (q0 + 2 * MH_TR < n) mh_issue(P, seq_rows, tile_rows(tt + 2), ab == 0 ? TA : TB);
     }
   }
 
