@@ -558,7 +558,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
 //           a lane's output column is the head whose softmax it keeps; the V^T
 //           operand is read transposed by ds_read_b64_tr_b16 (lane (g, s) points
 //           at row 8g + s/4 (+4), dims 4(s % 4) .. +3 of the 16-dim block).
-// The four waves agree on each head's running maximum through LDS.
+// The four waves post their tile maxima to LDS; P is taken against the shared
+// running reference and retaken only when a maximum outgrows it by 2^8.
 constexpr int MH_THREADS = 256;
 constexpr int MH_WAVES = MH_THREADS / 64;
 constexpr int MH_TR = 64;                           // rows per tile
@@ -667,12 +668,9 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
   }
   tmax = max_xor32(max_xor16(tmax));
   if (g == 0) smax[wid][c16] = tmax;
-  lds_barrier();
-  const float m_new = fmaxf(S.m_run, fmaxf(fmaxf(smax[0][c16], smax[1][c16]), fmaxf(smax[2][c16], smax[3][c16])));
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = exp2f(S.m_run - m_use);
-  S.m_run = m_new;
-  {
+  // P = exp2(x - m) for the tile's rows, rounded to bf16 into pbuf; returns the
+  // lane's share of sum P
+  auto write_p = [&](float m_use) {
     float psum = 0.f;
     uint32_t hbits[4];
 #pragma unroll
@@ -686,10 +684,40 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
     pk[0] = hbits[0] | (hbits[1] << 16);
     pk[1] = hbits[2] | (hbits[3] << 16);
     *(u32x2*)(pbuf + c16 * MH_PS + 16 * wid + 4 * g) = pk;
-    S.l_run = S.l_run * alpha + psum;
+    return psum;
+  };
+  auto tile_max = [&]() {
+    return fmaxf(S.m_run, fmaxf(fmaxf(smax[0][c16], smax[1][c16]), fmaxf(smax[2][c16], smax[3][c16])));
+  };
+  // The running max m_run is only a reference point: P is taken against the
+  // one every wave already holds, and the four waves' tile maxima (posted to
+  // smax) are checked after the barrier that publishes P. Only when some
+  // head's maximum passed m_run + 8 (weights above 2^8) is P taken again
+  // against the new maximum and the running state rescaled; the first tile
+  // (m_run = -inf in every lane) always takes that path.
+  float alpha = 1.f;
+  if (__any(S.m_run == -INFINITY)) {
+    lds_barrier();
+    const float m_new = tile_max();
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    alpha = exp2f(S.m_run - m_use);
+    S.m_run = m_new;
+    S.l_run = S.l_run * alpha + write_p(m_use);
+    lds_barrier();
+  } else {
+    const float psum = write_p(S.m_run);
+    lds_barrier();
+    const float m_new = tile_max();
+    if (__any(m_new > S.m_run + 8.f)) {  // the same verdict in every wave: all read the same smax
+      alpha = exp2f(S.m_run - m_new);
+      S.m_run = m_new;
+      S.l_run = S.l_run * alpha + write_p(m_new);
+      lds_barrier();
+    } else {
+      S.l_run += psum;
+    }
   }
-  lds_barrier();
-  // rescale O (this lane's head) when its running max moved
+  // rescale O (this lane's head) when its reference moved
   if (alpha != 1.0f) {
 #pragma unroll
     for (int nt = 0; nt < 8; nt++)
@@ -843,7 +871,8 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
       if (more) mh_row_ids(tile_rows(tt + 1), nrid);
       mh_tile(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf, more ? (ab == 0 ? &TB : &TA) : nullptr, seq_rows,
               nrid);
-      lds_barrier();
+      // no barrier here: the next tile's opening barrier orders this tile's
+      // reads of its buffer, pbuf and smax before anything rewrites them
     }
   }
 
