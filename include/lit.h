@@ -69,6 +69,8 @@ extern "C" {
 #define LIT_KNORM_CHUNK 256
 /* Entries per group of the score-maximum part of lit_idx_score's hints. */
 #define LIT_HINT_GROUP 16
+/* Floats at the end of each sequence's hints holding the query-side bound sums. */
+#define LIT_HINT_QBOUND 4
 /* Limits. */
 #define LIT_MAX_IDX_HEADS 64
 #define LIT_MAX_Q_HEADS 64
@@ -151,7 +153,11 @@ const char* lit_last_error(void);
  *           is an upper bound of the largest Euclidean key norm among entries
  *           c*LIT_KNORM_CHUNK ... +LIT_KNORM_CHUNK-1; hints[b][ceil(N/LIT_KNORM_CHUNK) + j]
  *           is the largest of the scores written for entries LIT_HINT_GROUP*j ...
- *           +LIT_HINT_GROUP-1 (-inf when none is allowed). */
+ *           +LIT_HINT_GROUP-1 (-inf when none is allowed); the last
+ *           LIT_HINT_QBOUND floats hold two fp64 values as little-endian word
+ *           pairs: sum_h |w[b][h]| * ||q[b][h]|| and sum_h |w[b][h]| (each
+ *           within a relative 2^-40 of the exact sum), which scale the
+ *           rounding bound of the exact selection. */
 int32_t lit_idx_hints_len(int32_t N);
 lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
                          float* scores, float* hints, void* stream);

@@ -66,6 +66,26 @@ __device__ __forceinline__ float weighted_relu(const f32x4 (&acc)[MT], const flo
 // and of the sqrt.
 __device__ __forceinline__ float norm_bound(float m) { return sqrtf(m + 0x1p-119f) * (1.0f + 0x1p-14f); }
 
+// The two sums the exact selection scales its rounding bound by, written
+// after the key-norm bounds and group maxima: sum_h |w_h| * ||q_h|| and
+// sum_h |w_h|, in fp64 (the squares of bf16 or fp32 values are exact there),
+// each as the two 32-bit words of a double. One wave reads the per-head terms
+// (lanes past the staged heads count 0).
+__device__ __forceinline__ void write_q_bounds(const double* qn, const double* wa, int nheads, float* hb) {
+  const int lane = threadIdx.x & 63;
+  double q = lane < nheads ? qn[lane] : 0.0, a = lane < nheads ? wa[lane] : 0.0;
+  q = wave_sum_f64_dpp(q);
+  a = wave_sum_f64_dpp(a);
+  if (lane == 0) {
+    uint32_t* u = reinterpret_cast<uint32_t*>(hb);
+    const uint64_t qb = (uint64_t)__double_as_longlong(q), ab = (uint64_t)__double_as_longlong(a);
+    u[0] = (uint32_t)qb;
+    u[1] = (uint32_t)(qb >> 32);
+    u[2] = (uint32_t)ab;
+    u[3] = (uint32_t)(ab >> 32);
+  }
+}
+
 // Loads the keys of 32 entries (2 column groups of 16) as B operands. Entries
 // at or past N load row N-1 instead (in bounds; their scores are never stored
 // and a real row's norm keeps the chunk bound valid), so no load sits in a
@@ -115,11 +135,13 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   __shared__ u32x4 qlds[MT * 4 * 64];
   __shared__ float wlds[64];
   __shared__ float nmax[4][S];
+  __shared__ double qterm[2][MT * 16];  // |w_h| ||q_h||, |w_h| (first workgroup of a sequence)
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
   const int wg_base = blockIdx.x * (S * CHUNK);
+  const bool bounds = hints && blockIdx.x == 0;
   // half-step h: entries hbase(h) .. +31 of chunk h/2
   auto hbase = [&](int h) { return wg_base + (h >> 1) * CHUNK + wid * 64 + 32 * (h & 1); };
   // the first NB - 1 half-steps' keys are in flight while q is staged
@@ -132,14 +154,34 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   // 16*mt + hh, dims 8*gg + 32*j .. +7.
   const uint16_t* qb = q + (size_t)b * H * LIT_IDX_DIM;
   for (int idx = tid; idx < MT * 16 * 16; idx += 256) {
-    const int h = idx >> 4, d8 = idx & 15;
+    const int h = idx >> 4, d8 = idx & 15;  // the 16 lanes of a row hold one head
     u32x4 v = {0u, 0u, 0u, 0u};
     if (h < H) v = *(const u32x4*)(qb + h * LIT_IDX_DIM + d8 * 8);
     const int mt = h >> 4, hh = h & 15, gg = d8 & 3, j = d8 >> 2;
     qlds[(mt * 4 + j) * 64 + hh + 16 * gg] = v;
+    if (bounds) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const double lo = (double)bf16_lo(v[i]), hi = (double)bf16_hi(v[i]);
+        ss += lo * lo;
+        ss += hi * hi;
+      }
+      ss += dpp_f64<0x111>(ss);
+      ss += dpp_f64<0x112>(ss);
+      ss += dpp_f64<0x114>(ss);
+      ss += dpp_f64<0x118>(ss);
+      if (d8 == 15) {
+        const double a = h < H ? fabs((double)w[(size_t)b * H + h]) : 0.0;
+        qterm[0][h] = a * sqrt(ss);
+        qterm[1][h] = a;
+      }
+    }
   }
   if (tid < 64) wlds[tid] = tid < H ? w[(size_t)b * H + tid] : 0.f;
   lds_barrier();
+  if (bounds && wid == 0)
+    write_q_bounds(qterm[0], qterm[1], MT * 16, hints + (size_t)b * hints_len + nchunks + (N + LIT_HINT_GROUP - 1) / LIT_HINT_GROUP);
   float wr[MT][4];
   load_lane_weights<MT>(wlds, wr);
 
@@ -234,6 +276,20 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
   }
   if (tid < 64) wlds[tid] = tid < H ? w[(size_t)b * H + tid] : 0.f;
   __syncthreads();
+  if (hints && blockIdx.x == 0 && wid == 0) {
+    // lane h: its head's squared norm from the staged operands (fp64, exact squares)
+    __shared__ double qterm[2][64];
+    double ss = 0.0;
+    if (lane < MT * 16)
+      for (int d = 0; d < LIT_IDX_DIM; d++) {
+        const double x = (double)qlds[((lane >> 4) * 32 + (d & 31)) * 64 + (lane & 15) + 16 * (d >> 5)];
+        ss += x * x;
+      }
+    const double a = lane < H ? fabs((double)wlds[lane]) : 0.0;
+    qterm[0][lane] = a * sqrt(ss);
+    qterm[1][lane] = a;
+    write_q_bounds(qterm[0], qterm[1], 64, hints + (size_t)b * hints_len + nchunks + (N + LIT_HINT_GROUP - 1) / LIT_HINT_GROUP);
+  }
   float wr[MT][4];
   load_lane_weights<MT>(wlds, wr);
 
@@ -367,7 +423,7 @@ static void launch_f32(dim3 grid, hipStream_t st, const lit_idx_in* in, const ui
 
 extern "C" int32_t lit_idx_hints_len(int32_t N) {
   if (N < 1) return 0;
-  return (int32_t)(cdiv(N, LIT_KNORM_CHUNK) + cdiv(N, LIT_HINT_GROUP));
+  return (int32_t)(cdiv(N, LIT_KNORM_CHUNK) + cdiv(N, LIT_HINT_GROUP) + LIT_HINT_QBOUND);
 }
 
 extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,

@@ -919,13 +919,16 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   }
   const int qh = tid >> 4, d8 = tid & 15;
   // exact mode: indices clamped into range so that no load sits in a branch
-  float knorm = 0.f, w_h = 0.f, w_q = 0.f;
+  float knorm = 0.f, w_h = 0.f;
   u32x4 qraw[2];
+  u32x4 qbw = {0u, 0u, 0u, 0u};  // sum_h |w_h| ||q_h|| and sum_h |w_h| (fp64 word pairs) from the hints
   if (P.exact) {
     const int H = P.H;
     knorm = P.hints[(size_t)b * P.hints_len + min(tid, P.nchunks - 1)];
+    const uint32_t* qb = reinterpret_cast<const uint32_t*>(P.hints + (size_t)b * P.hints_len + P.hints_len) - LIT_HINT_QBOUND;
+#pragma unroll
+    for (int i = 0; i < 4; i++) qbw[i] = qb[i];
     w_h = P.w[(size_t)b * H + min(lane, H - 1)];
-    w_q = P.w[(size_t)b * H + min(qh, H - 1)];
     const size_t off = ((size_t)b * H + min(qh, H - 1)) * LIT_IDX_DIM + 8 * d8;
     if (BF16) {
       qraw[0] = *(const u32x4*)((const uint16_t*)P.q + off);
@@ -940,20 +943,17 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
 #pragma unroll
   for (int i = 0; i < GROUP; i++) kv[i] = score_key(sv[i / 4][i % 4]) & (e0 + i < N ? 0xffffffffu : 0u);
 
-  // 1. count, min and max of the selectable keys; exact mode also stages q,
-  //    and reduces sum_h |w_h| |q_h|, sum_h |w_h| and the largest key norm
-  int ns = 0;
+  // 1. min and max of the selectable keys (the histogram's range); exact mode
+  //    also stages q for the band rescoring, and wave 0 (which holds the
+  //    chunk bounds: at most 64 chunks here) takes the largest key norm
   uint32_t kmin = 0xffffffffu, kmx = 0u;
 #pragma unroll
   for (int i = 0; i < GROUP; i++)
     if (kv[i]) {
-      ns++;
       kmin = min(kmin, kv[i]);
       kmx = max(kmx, kv[i]);
     }
-  double qn = 0.0, wa = 0.0;
   if (P.exact) {
-    if (tid >= P.nchunks) knorm = 0.f;
     if (lane >= P.H) w_h = 0.f;
     float x[8];
 #pragma unroll
@@ -967,80 +967,45 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
       }
     }
     if (qh >= P.H) {
-      w_q = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; i++) x[i] = 0.f;
     }
-    double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      L.qP[qh * QP_STRIDE + 8 * d8 + i] = x[i];
-      ss += (double)x[i] * (double)x[i];
-    }
-    // 16 lanes per head: their sum of squares lands in the head's d8 == 15 lane
-    ss += dpp_f64<0x111>(ss);
-    ss += dpp_f64<0x112>(ss);
-    ss += dpp_f64<0x114>(ss);
-    ss += dpp_f64<0x118>(ss);
-    if (d8 == 15) {
-      wa = fabs((double)w_q);
-      qn = wa * sqrt(ss);
-    }
+    for (int i = 0; i < 8; i++) L.qP[qh * QP_STRIDE + 8 * d8 + i] = x[i];
   }
   {
-    const int s_w = wave_sum_dpp(ns);
     const uint32_t mn_w = wave_min_dpp(kmin), mx_w = wave_max_dpp(kmx);
-    const uint32_t kn_w = wave_max_dpp(__float_as_uint(knorm));  // non-negative floats order as integers
-    double qn_w = 0.0, wa_w = 0.0;
-    if (P.exact) {
-      qn_w = wave_sum_f64_dpp(qn);
-      wa_w = wave_sum_f64_dpp(wa);
-    }
     if (lane == 0) {
-      L.part[0][wid] = s_w;
       L.red_u[0][wid] = mn_w;
       L.red_u[1][wid] = mx_w;
-      L.red_u[2][wid] = kn_w;
-      L.red_d[0][wid] = qn_w;
-      L.red_d[1][wid] = wa_w;
+    }
+    if (P.exact && wid == 0) {
+      const uint32_t kn_w = wave_max_dpp(__float_as_uint(tid < P.nchunks ? knorm : 0.f));  // non-negative floats order as integers
+      if (lane == 0) L.red_u[2][0] = kn_w;
     }
   }
   lds_barrier();
   // the per-wave values, one per lane of each row, reduced across the row
   const int slot = lane & 15;
-  ns = __builtin_amdgcn_readlane(row_incl_scan_dpp(L.part[0][slot]), 15);
-  uint32_t kn_u;
+  uint32_t kn_u = 0u;
   {
-    uint32_t mn = L.red_u[0][slot], mx = L.red_u[1][slot], kn = L.red_u[2][slot];
+    uint32_t mn = L.red_u[0][slot], mx = L.red_u[1][slot];
     mn = min(mn, dpp_u32<0x111>(~0u, mn));
-    mn = min(mn, dpp_u32<0x112>(~0u, mn));
-    mn = min(mn, dpp_u32<0x114>(~0u, mn));
-    mn = min(mn, dpp_u32<0x118>(~0u, mn));
     mx = max(mx, dpp_u32<0x111>(0u, mx));
+    mn = min(mn, dpp_u32<0x112>(~0u, mn));
     mx = max(mx, dpp_u32<0x112>(0u, mx));
+    mn = min(mn, dpp_u32<0x114>(~0u, mn));
     mx = max(mx, dpp_u32<0x114>(0u, mx));
+    mn = min(mn, dpp_u32<0x118>(~0u, mn));
     mx = max(mx, dpp_u32<0x118>(0u, mx));
-    kn = max(kn, dpp_u32<0x111>(0u, kn));
-    kn = max(kn, dpp_u32<0x112>(0u, kn));
-    kn = max(kn, dpp_u32<0x114>(0u, kn));
-    kn = max(kn, dpp_u32<0x118>(0u, kn));
     kmin = (uint32_t)__builtin_amdgcn_readlane((int)mn, 15);
     kmx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 15);
-    kn_u = (uint32_t)__builtin_amdgcn_readlane((int)kn, 15);
+    if (P.exact) kn_u = L.red_u[2][0];
   }
   double Q = 0.0, Wa = 0.0;
   if (P.exact) {
-    double q = L.red_d[0][slot], a = L.red_d[1][slot];
-    q += dpp_f64<0x111>(q);
-    a += dpp_f64<0x111>(a);
-    q += dpp_f64<0x112>(q);
-    a += dpp_f64<0x112>(a);
-    q += dpp_f64<0x114>(q);
-    a += dpp_f64<0x114>(a);
-    q += dpp_f64<0x118>(q);
-    a += dpp_f64<0x118>(a);
-    Q = readlane_f64(q, 15);
-    Wa = readlane_f64(a, 15);
+    Q = __longlong_as_double((long long)(((uint64_t)qbw[1] << 32) | qbw[0]));
+    Wa = __longlong_as_double((long long)(((uint64_t)qbw[3] << 32) | qbw[2]));
   }
 
   // selected: key > hi (bits in `mine`, taken as soon as hi is known so that
@@ -1052,21 +1017,23 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
     return m;
   };
   uint32_t mine;
-  if (ns <= k) {
+  // 2. one histogram of all keys over the bits below their common prefix (the
+  //    key that is never selected, 0, goes to a bin of its own); its total is
+  //    the number of selectable entries
+  const uint32_t diff = kmin ^ kmx;
+  const int hb = diff ? 31 - __clz((int)diff) : 0;
+  const int shift = hb > 10 ? hb - 10 : 0;
+  const uint32_t prefix = kmx & ~((2u << hb) - 1u);
+  auto binof = [&](uint32_t kk) -> uint32_t { return (kk - prefix) >> shift; };
+#pragma unroll
+  for (int i = 0; i < GROUP; i++) atomicAdd(&L.hist2k[kv[i] ? binof(kv[i]) : 2048u], 1u);
+  lds_barrier();
+  const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
+  int tot;
+  const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.part[1], &tot);
+  if (tot <= k) {
     mine = keys_above(0u);  // every selectable entry
   } else {
-    // 2. one histogram of all keys over the bits below their common prefix
-    const uint32_t diff = kmin ^ kmx;
-    const int hb = diff ? 31 - __clz((int)diff) : 0;
-    const int shift = hb > 10 ? hb - 10 : 0;
-    const uint32_t prefix = kmx & ~((2u << hb) - 1u);
-    auto binof = [&](uint32_t kk) -> uint32_t { return (kk - prefix) >> shift; };
-#pragma unroll
-    for (int i = 0; i < GROUP; i++) atomicAdd(&L.hist2k[kv[i] ? binof(kv[i]) : 2048u], 1u);
-    lds_barrier();
-    const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
-    int tot;
-    const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.part[1], &tot);
     if (ab < k && k <= ab + c0) {
       L.misc[0] = 2047 - 2 * tid;
       L.misc[1] = ab;

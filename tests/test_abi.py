@@ -135,3 +135,10 @@ def test_binding_fails_loudly_without_library(tmp_path):
             lit.load(str(tmp_path / "missing.so"))
     finally:
         lit._lib = saved
+
+
+def test_hints_length_layout(L):
+    # key-norm chunk bounds, per-16 score maxima, then two fp64 bound sums (4 floats)
+    for n in (1, 15, 16, 17, 255, 256, 257, 16384, 125000):
+        assert L.lit_idx_hints_len(n) == -(-n // 256) + -(-n // 16) + 4
+    assert L.lit_idx_hints_len(0) == 0

@@ -126,7 +126,17 @@ def test_score_and_exact_topk(name, wl, B, N, k):
     sc = scores.cpu()
     gpad = (-Nn) % 16
     gref = torch.nn.functional.pad(sc, (0, gpad), value=float("-inf")).reshape(sc.shape[0], -1, 16).amax(-1)
-    assert torch.equal(hints.cpu()[:, nch:], gref)
+    ng = gref.shape[1]
+    assert hints.shape[1] == nch + ng + 4
+    assert torch.equal(hints.cpu()[:, nch:nch + ng], gref)
+    # the query-side bound sums, fp64 word pairs at the end: sum |w| ||q|| and sum |w|
+    qb = np.ascontiguousarray(hints.cpu()[:, nch + ng:].numpy()).view(np.float64)
+    q64 = inp.q_idx.double().cpu()
+    w64 = inp.w.double().cpu().abs()
+    qref = (w64 * q64.norm(dim=-1)).sum(-1).numpy()
+    wref = w64.sum(-1).numpy()
+    assert np.allclose(qb[:, 0], qref, rtol=2.0 ** -40, atol=0), (qb[:, 0], qref)
+    assert np.allclose(qb[:, 1], wref, rtol=2.0 ** -40, atol=0), (qb[:, 1], wref)
     check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, name)
 
 
