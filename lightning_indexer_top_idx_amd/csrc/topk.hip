@@ -83,7 +83,9 @@ struct FullLds {
 };
 
 constexpr int QP_STRIDE = LIT_IDX_DIM + 4;  // fp32 q row stride in LDS (spreads banks)
-constexpr int RS = 2;                       // entries rescored together by one wave
+
+constexpr int BW = 4;        // band entries per wave and round of the broadcast rescoring
+constexpr int PSUM_LD = 66;  // fp64 row stride of the head terms (rows on distinct banks)
 
 struct FastLds {
   SelectScratch sc;
@@ -92,8 +94,7 @@ struct FastLds {
   double qn[64];
   double wa[64];
   float qP[64 * QP_STRIDE];
-  float krow[NWAVES][RS][LIT_IDX_DIM];
-  double psum[NWAVES][RS][64];
+  double psum[NWAVES][BW][PSUM_LD];  // head terms of the rescoring waves
   double band_s[FBAND_CAP];
   int32_t band_n[FBAND_CAP];
   uint32_t band_k[FBAND_CAP];
@@ -198,6 +199,121 @@ __device__ void report_violation(const TopkParams& P, int b, int32_t* ids, uint8
     for (int i = threadIdx.x; i < P.N; i += TK_THREADS) mask[i] = 0;
   if (threadIdx.x == 0) P.count[b] = -1;
 }
+
+// acc[j] += KA[j] of lane N of this lane's 16-lane row (DPP row_newbcast) * QA,
+// then acc[j] += KB[j] (same lane) * QB, for the wave's BW entries: v_fmac_f64
+// rounds once, and the product of two values upcast from fp32/bf16 is exact,
+// so each step is the oracle's add. s_nop 1 first: two wait states between a
+// VALU write of a K register and its DPP read. Volatile: the blocks keep their
+// place between the surrounding memory operations and exec-mask updates.
+#define LIT_FMAC_LINE(I, KI, QI, N) \
+  "v_fmac_f64_dpp %" #I ", %" #KI ", %" #QI " row_newbcast:" #N " row_mask:0xf bank_mask:0xf\n\t"
+#define LIT_FMAC_BCAST(N, A, KA, KB, QA, QB)                                                              \
+  asm volatile("s_nop 1\n\t" LIT_FMAC_LINE(0, 4, 12, N) LIT_FMAC_LINE(1, 5, 12, N) LIT_FMAC_LINE(2, 6, 12, N) \
+                   LIT_FMAC_LINE(3, 7, 12, N) LIT_FMAC_LINE(0, 8, 13, N) LIT_FMAC_LINE(1, 9, 13, N)              \
+                       LIT_FMAC_LINE(2, 10, 13, N) LIT_FMAC_LINE(3, 11, 13, N)                                   \
+               : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3])                                                  \
+               : "v"(KA[0]), "v"(KA[1]), "v"(KA[2]), "v"(KA[3]), "v"(KB[0]), "v"(KB[1]), "v"(KB[2]), "v"(KB[3]), \
+                 "v"(QA), "v"(QB))
+
+// One dim pair (32c + 2N, 32c + 2N + 1) of the running dot products: lane N of
+// each row holds those two key values of every entry (kA, kB).
+#define LIT_BAND_STEP(N)                                                 \
+  {                                                                      \
+    const double q0 = (double)qv[((N) >> 1) & 1][2 * ((N)&1)];           \
+    const double q1 = (double)qv[((N) >> 1) & 1][2 * ((N)&1) + 1];       \
+    LIT_FMAC_BCAST(N, acc, kA, kB, q0, q1);                              \
+  }
+// the q values of dims 32c + 8u .. +7 (quarter u of block c) were loaded into
+// qn; they move to qv and the next quarter's are requested
+#define LIT_BAND_QUARTER(U, S0, S1, S2, S3)                                             \
+  {                                                                                     \
+    qv[0] = qn[0];                                                                      \
+    qv[1] = qn[1];                                                                      \
+    if (32 * c + 8 * (U) + 8 < LIT_IDX_DIM) {                                           \
+      qn[0] = *(const f32x4*)(qr + 32 * c + 8 * (U) + 8);                               \
+      qn[1] = *(const f32x4*)(qr + 32 * c + 8 * (U) + 12);                              \
+    }                                                                                   \
+    LIT_BAND_STEP(S0) LIT_BAND_STEP(S1) LIT_BAND_STEP(S2) LIT_BAND_STEP(S3)             \
+  }
+
+// fp64 canonical scores of up to BW band entries by one wave: entry j is
+// band_n[e0 + es * j] (entries at or past M, M >= 1, are computed on the row
+// of entry 0 and dropped). Lane h owns head h: its q row is read from qP, and the key values
+// come to it by DPP broadcast from the lanes of its row, each of which loaded
+// one dim pair per 32-dim block. Every dot product runs in dim order, the head
+// terms w_h * max(acc, 0) go through psum, and lane j adds entry j's terms in
+// head order (lanes h >= H post +0.0, which leaves a sum that starts at +0.0
+// unchanged).
+template <bool BF16>
+__device__ __forceinline__ void band_scores_bcast(const TopkParams& P, int b, const float* qP, float w_h,
+                                                  const int32_t* band_n, int M, int e0, int es,
+                                                  double (*psum)[PSUM_LD], double* band_s) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63, nl = lane & 15;
+  const float* qr = qP + lane * QP_STRIDE;
+  // the sequence's keys (a wave-uniform base) and 32-bit element offsets in it
+  // (N * 128 < 2^32 on the paths that call this)
+  const size_t kbase = (size_t)b * P.N * LIT_IDX_DIM;
+  uint32_t roff[BW];
+#pragma unroll
+  for (int j = 0; j < BW; j++) {
+    const int e = e0 + es * j;
+    roff[j] = (uint32_t)band_n[e < M ? e : 0] * LIT_IDX_DIM + 2 * nl;  // M >= 1; band_n[>= M] is unset
+  }
+  const uint16_t* kb16 = (const uint16_t*)P.kidx + kbase;
+  const float* kb32 = (const float*)P.kidx + kbase;
+  uint32_t kr[BW];  // bf16 key pairs of the next block (one dword per block)
+  if constexpr (BF16) {
+#pragma unroll
+    for (int j = 0; j < BW; j++) kr[j] = *(const uint32_t*)(kb16 + roff[j]);
+  }
+  double acc[BW];
+#pragma unroll
+  for (int j = 0; j < BW; j++) acc[j] = 0.0;
+  f32x4 qv[2], qn[2];
+  qn[0] = *(const f32x4*)qr;
+  qn[1] = *(const f32x4*)(qr + 4);
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    double kA[BW], kB[BW];
+#pragma unroll
+    for (int j = 0; j < BW; j++) {
+      float2 kp;
+      if constexpr (BF16) {
+        kp = make_float2(bf16_lo(kr[j]), bf16_hi(kr[j]));
+        if (c + 1 < 4) kr[j] = *(const uint32_t*)(kb16 + roff[j] + 32 * (c + 1));
+      } else {
+        kp = *(const float2*)(kb32 + roff[j] + 32 * c);
+      }
+      kA[j] = (double)kp.x;
+      kB[j] = (double)kp.y;
+    }
+    LIT_BAND_QUARTER(0, 0, 1, 2, 3)
+    LIT_BAND_QUARTER(1, 4, 5, 6, 7)
+    LIT_BAND_QUARTER(2, 8, 9, 10, 11)
+    LIT_BAND_QUARTER(3, 12, 13, 14, 15)
+  }
+#pragma unroll
+  for (int j = 0; j < BW; j++) {
+    const double a = acc[j] > 0.0 ? acc[j] : 0.0;
+    psum[j][lane] = lane < P.H ? (double)w_h * a : 0.0;
+  }
+  wave_sync();
+  {
+    const double* pr = psum[lane & (BW - 1)];
+    double s = 0.0;
+#pragma unroll 16
+    for (int h = 0; h < 64; h++) s = s + pr[h];
+    const int e = e0 + es * lane;
+    if (lane < BW && e < M) band_s[e] = s;
+  }
+  wave_sync();  // psum is refilled by the next round
+}
+#undef LIT_BAND_QUARTER
+#undef LIT_BAND_STEP
+#undef LIT_FMAC_BCAST
+#undef LIT_FMAC_LINE
 
 // ---------------------------------------------------------------- fast path
 
@@ -358,81 +474,6 @@ __device__ int gather_range(const float* sb, int N, const uint32_t* gkey, uint16
   return total;
 }
 
-// One lane's share (dims 2*lane, 2*lane+1) of a key row, for the fp64 rescoring.
-__device__ __forceinline__ float2 key_pair(const TopkParams& P, int b, int n) {
-  const int lane = threadIdx.x & 63;
-  const size_t off = ((size_t)b * P.N + n) * LIT_IDX_DIM + 2 * lane;
-  if (P.dtype == LIT_BF16) {
-    const uint32_t v = *(const uint32_t*)((const uint16_t*)P.kidx + off);
-    return make_float2(bf16_lo(v), bf16_hi(v));
-  }
-  return *(const float2*)((const float*)P.kidx + off);
-}
-
-// fp64 canonical scores of NC entries by one wave, their chains interleaved:
-// lane h owns head h (q row in qP); each entry's key row is staged in krow[c]
-// from the lanes' pairs kp[c] and read back as broadcasts; the per-head
-// products go through psum[c] and are summed in head order. Every lane returns
-// the NC scores.
-template <int NC>
-__device__ __forceinline__ void rescore_multi(const float* qP, const float2 (&kp)[NC], float w_h, int H,
-                                              float (*krow)[LIT_IDX_DIM], double (*psum)[64], double (&out)[NC]) {
-#pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int c = 0; c < NC; c++) *(float2*)(krow[c] + 2 * lane) = kp[c];
-  wave_sync();
-  const float* qr = qP + lane * QP_STRIDE;
-  double acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; c++) acc[c] = 0.0;
-#pragma unroll 2
-  for (int d0 = 0; d0 < LIT_IDX_DIM; d0 += 8) {
-    const f32x4 qa = *(const f32x4*)(qr + d0), qb = *(const f32x4*)(qr + d0 + 4);
-    f32x4 ka[NC], kb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; c++) {
-      ka[c] = *(const f32x4*)(krow[c] + d0);
-      kb[c] = *(const f32x4*)(krow[c] + d0 + 4);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) acc[c] = fma((double)qa[j], (double)ka[c][j], acc[c]);
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) acc[c] = fma((double)qb[j], (double)kb[c][j], acc[c]);
-  }
-#pragma unroll
-  for (int c = 0; c < NC; c++) {
-    const double r = acc[c] > 0.0 ? acc[c] : 0.0;
-    psum[c][lane] = (double)w_h * r;
-    out[c] = 0.0;
-  }
-  wave_sync();
-  if (lane == 0) {
-    int h = 0;
-    for (; h + 8 <= H; h += 8) {
-      double t[NC][8];
-#pragma unroll
-      for (int c = 0; c < NC; c++)
-#pragma unroll
-        for (int i = 0; i < 8; i++) t[c][i] = psum[c][h + i];
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-#pragma unroll
-        for (int c = 0; c < NC; c++) out[c] = out[c] + t[c][i];
-    }
-    for (; h < H; h++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) out[c] = out[c] + psum[c][h];
-  }
-#pragma unroll
-  for (int c = 0; c < NC; c++) out[c] = __shfl(out[c], 0);
-  wave_sync();
-}
-
 // Returns false, having written nothing, when the sequence does not fit.
 __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -564,10 +605,17 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         const uint32_t ki = L.ckey[i];
         const int ni = L.cidx[i];
         int rank = 0;
-        for (int j = 0; j < m; j++) {
-          const int pj = L.binpos[j];
-          const uint32_t kj = L.ckey[pj];
-          rank += (kj > ki) || (kj == ki && L.cidx[pj] < ni);
+        for (int j0 = 0; j0 < m; j0 += 8) {  // reads 8 at a time (clamped in range)
+          uint32_t kj[8];
+          int nj[8];
+#pragma unroll
+          for (int u = 0; u < 8; u++) {
+            const int pj = L.binpos[min(j0 + u, m - 1)];
+            kj[u] = L.ckey[pj];
+            nj[u] = L.cidx[pj];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; u++) rank += j0 + u < m && ((kj[u] > ki) || (kj[u] == ki && nj[u] < ni));
         }
         L.cflag[i] = rank < r;
         if (rank == r - 1) L.sc.misc[4] = (int)ki;
@@ -637,18 +685,15 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         report_violation(P, b, ids, mask);
         return true;
       }
-      // fp64 rescoring: each wave takes RS entries at a time
+      // fp64 rescoring: BW entries per wave and round, key values broadcast
+      // across each row (eight waves up to 8 * BW entries, else sixteen)
       const float w_h = lane < P.H ? P.w[(size_t)b * P.H + lane] : 0.f;
-      for (int i0 = wid * RS; i0 < M; i0 += NWAVES * RS) {
-        float2 kp[RS];
-#pragma unroll
-        for (int c = 0; c < RS; c++) kp[c] = i0 + c < M ? key_pair(P, b, L.band_n[i0 + c]) : make_float2(0.f, 0.f);
-        double sc[RS];
-        rescore_multi<RS>(L.qP, kp, w_h, P.H, L.krow[wid], L.psum[wid], sc);
-        if (lane == 0)
-#pragma unroll
-          for (int c = 0; c < RS; c++)
-            if (i0 + c < M) L.band_s[i0 + c] = sc[c];
+      const int nwr = M <= 8 * BW ? 8 : NWAVES;
+      for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW) {
+        if (P.dtype == LIT_BF16)
+          band_scores_bcast<true>(P, b, L.qP, w_h, L.band_n, M, base + wid, nwr, L.psum[wid], L.band_s);
+        else
+          band_scores_bcast<false>(P, b, L.qP, w_h, L.band_n, M, base + wid, nwr, L.psum[wid], L.band_s);
       }
       for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
       lds_barrier();
@@ -656,9 +701,16 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         const double si = L.band_s[i];
         const int ni = L.band_n[i];
         int rank = 0;
-        for (int j = 0; j < M; j++) {
-          const double sj = L.band_s[j];
-          rank += (sj > si) || (sj == si && L.band_n[j] < ni);
+        for (int j0 = 0; j0 < M; j0 += 8) {  // reads 8 at a time (clamped in range)
+          double sj[8];
+          int nj[8];
+#pragma unroll
+          for (int u = 0; u < 8; u++) {
+            sj[u] = L.band_s[min(j0 + u, M - 1)];
+            nj[u] = L.band_n[min(j0 + u, M - 1)];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; u++) rank += j0 + u < M && ((sj[u] > si) || (sj[u] == si && nj[u] < ni));
         }
         if (rank < rr) atomicOr(&sel[ni >> 5], 1u << (ni & 31));
       }
@@ -700,8 +752,6 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
 // issued up front, reductions and scans run on DPP lane moves, and each step
 // costs one barrier.
 constexpr int SBIN_CAP = 2048;  // members of the k-th score's histogram bin
-constexpr int BW = 4;        // band entries per wave and round of the broadcast rescoring
-constexpr int PSUM_LD = 66;  // fp64 row stride of the head terms (rows on distinct banks)
 
 struct SmallLds {
   float qP[64 * QP_STRIDE];
@@ -718,179 +768,8 @@ struct SmallLds {
   int misc[4];
 };
 
-// fp64 canonical scores of NC entries by one wave, their chains interleaved:
-// lane h owns head h (q row in qP); each entry's key row is staged in krow[c]
-// from the lanes' pairs kp[c] and read back as broadcasts. The head terms go
-// through psum[c] and every lane adds them up in head order (lanes h >= H post
-// +0.0, which leaves a sum that starts at +0.0 unchanged), so all lanes return
-// the NC scores.
-template <int NC>
-__device__ __forceinline__ void rescore_lanes(const float* qP, const float2 (&kp)[NC], float w_h, int H,
-                                              float (*krow)[LIT_IDX_DIM], double (*psum)[64], double (&out)[NC]) {
-#pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int c = 0; c < NC; c++) *(float2*)(krow[c] + 2 * lane) = kp[c];
-  wave_sync();
-  const float* qr = qP + lane * QP_STRIDE;
-  double acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; c++) acc[c] = 0.0;
-#pragma unroll 2
-  for (int d0 = 0; d0 < LIT_IDX_DIM; d0 += 8) {
-    const f32x4 qa = *(const f32x4*)(qr + d0), qb = *(const f32x4*)(qr + d0 + 4);
-    f32x4 ka[NC], kb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; c++) {
-      ka[c] = *(const f32x4*)(krow[c] + d0);
-      kb[c] = *(const f32x4*)(krow[c] + d0 + 4);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) acc[c] = fma((double)qa[j], (double)ka[c][j], acc[c]);
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) acc[c] = fma((double)qb[j], (double)kb[c][j], acc[c]);
-  }
-#pragma unroll
-  for (int c = 0; c < NC; c++) {
-    const double a = acc[c] > 0.0 ? acc[c] : 0.0;
-    psum[c][lane] = lane < H ? (double)w_h * a : 0.0;
-    out[c] = 0.0;
-  }
-  wave_sync();
-  for (int h0 = 0; h0 < H; h0 += 8) {
-    double t[NC][8];
-#pragma unroll
-    for (int c = 0; c < NC; c++)
-#pragma unroll
-      for (int i = 0; i < 8; i++) t[c][i] = psum[c][h0 + i];
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) out[c] = out[c] + t[c][i];
-  }
-  wave_sync();  // krow and psum are refilled by the next call
-}
-
 static_assert(sizeof(SmallLds) <= 160 * 1024, "LDS budget of a gfx950 CU");
 
-// acc[j] += KA[j] of lane N of this lane's 16-lane row (DPP row_newbcast) * QA,
-// then acc[j] += KB[j] (same lane) * QB, for the wave's BW entries: v_fmac_f64
-// rounds once, and the product of two values upcast from fp32/bf16 is exact,
-// so each step is the oracle's add. s_nop 1 first: two wait states between a
-// VALU write of a K register and its DPP read. Volatile: the blocks keep their
-// place between the surrounding memory operations and exec-mask updates.
-#define LIT_FMAC_LINE(I, KI, QI, N) \
-  "v_fmac_f64_dpp %" #I ", %" #KI ", %" #QI " row_newbcast:" #N " row_mask:0xf bank_mask:0xf\n\t"
-#define LIT_FMAC_BCAST(N, A, KA, KB, QA, QB)                                                              \
-  asm volatile("s_nop 1\n\t" LIT_FMAC_LINE(0, 4, 12, N) LIT_FMAC_LINE(1, 5, 12, N) LIT_FMAC_LINE(2, 6, 12, N) \
-                   LIT_FMAC_LINE(3, 7, 12, N) LIT_FMAC_LINE(0, 8, 13, N) LIT_FMAC_LINE(1, 9, 13, N)              \
-                       LIT_FMAC_LINE(2, 10, 13, N) LIT_FMAC_LINE(3, 11, 13, N)                                   \
-               : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3])                                                  \
-               : "v"(KA[0]), "v"(KA[1]), "v"(KA[2]), "v"(KA[3]), "v"(KB[0]), "v"(KB[1]), "v"(KB[2]), "v"(KB[3]), \
-                 "v"(QA), "v"(QB))
-
-// One dim pair (32c + 2N, 32c + 2N + 1) of the running dot products: lane N of
-// each row holds those two key values of every entry (kA, kB).
-#define LIT_BAND_STEP(N)                                                 \
-  {                                                                      \
-    const double q0 = (double)qv[((N) >> 1) & 1][2 * ((N)&1)];           \
-    const double q1 = (double)qv[((N) >> 1) & 1][2 * ((N)&1) + 1];       \
-    LIT_FMAC_BCAST(N, acc, kA, kB, q0, q1);                              \
-  }
-// the q values of dims 32c + 8u .. +7 (quarter u of block c) were loaded into
-// qn; they move to qv and the next quarter's are requested
-#define LIT_BAND_QUARTER(U, S0, S1, S2, S3)                                             \
-  {                                                                                     \
-    qv[0] = qn[0];                                                                      \
-    qv[1] = qn[1];                                                                      \
-    if (32 * c + 8 * (U) + 8 < LIT_IDX_DIM) {                                           \
-      qn[0] = *(const f32x4*)(qr + 32 * c + 8 * (U) + 8);                               \
-      qn[1] = *(const f32x4*)(qr + 32 * c + 8 * (U) + 12);                              \
-    }                                                                                   \
-    LIT_BAND_STEP(S0) LIT_BAND_STEP(S1) LIT_BAND_STEP(S2) LIT_BAND_STEP(S3)             \
-  }
-
-// fp64 canonical scores of up to BW band entries by one wave: entry j is
-// band_n[e0 + es * j] (entries at or past M, M >= 1, are computed on the row
-// of entry 0 and dropped). Lane h owns head h: its q row is read from qP, and the key values
-// come to it by DPP broadcast from the lanes of its row, each of which loaded
-// one dim pair per 32-dim block. Every dot product runs in dim order, the head
-// terms w_h * max(acc, 0) go through psum, and lane j adds entry j's terms in
-// head order (lanes h >= H post +0.0, which leaves a sum that starts at +0.0
-// unchanged).
-template <bool BF16>
-__device__ __forceinline__ void band_scores_bcast(const TopkParams& P, int b, const float* qP, float w_h,
-                                                  const int32_t* band_n, int M, int e0, int es,
-                                                  double (*psum)[PSUM_LD], double* band_s) {
-#pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63, nl = lane & 15;
-  const float* qr = qP + lane * QP_STRIDE;
-  // the sequence's keys (a wave-uniform base) and 32-bit element offsets in it
-  // (this path has N <= 16384)
-  const size_t kbase = (size_t)b * P.N * LIT_IDX_DIM;
-  uint32_t roff[BW];
-#pragma unroll
-  for (int j = 0; j < BW; j++) {
-    const int e = e0 + es * j;
-    roff[j] = (uint32_t)band_n[e < M ? e : 0] * LIT_IDX_DIM + 2 * nl;  // M >= 1; band_n[>= M] is unset
-  }
-  const uint16_t* kb16 = (const uint16_t*)P.kidx + kbase;
-  const float* kb32 = (const float*)P.kidx + kbase;
-  uint32_t kr[BW];  // bf16 key pairs of the next block (one dword per block)
-  if constexpr (BF16) {
-#pragma unroll
-    for (int j = 0; j < BW; j++) kr[j] = *(const uint32_t*)(kb16 + roff[j]);
-  }
-  double acc[BW];
-#pragma unroll
-  for (int j = 0; j < BW; j++) acc[j] = 0.0;
-  f32x4 qv[2], qn[2];
-  qn[0] = *(const f32x4*)qr;
-  qn[1] = *(const f32x4*)(qr + 4);
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    double kA[BW], kB[BW];
-#pragma unroll
-    for (int j = 0; j < BW; j++) {
-      float2 kp;
-      if constexpr (BF16) {
-        kp = make_float2(bf16_lo(kr[j]), bf16_hi(kr[j]));
-        if (c + 1 < 4) kr[j] = *(const uint32_t*)(kb16 + roff[j] + 32 * (c + 1));
-      } else {
-        kp = *(const float2*)(kb32 + roff[j] + 32 * c);
-      }
-      kA[j] = (double)kp.x;
-      kB[j] = (double)kp.y;
-    }
-    LIT_BAND_QUARTER(0, 0, 1, 2, 3)
-    LIT_BAND_QUARTER(1, 4, 5, 6, 7)
-    LIT_BAND_QUARTER(2, 8, 9, 10, 11)
-    LIT_BAND_QUARTER(3, 12, 13, 14, 15)
-  }
-#pragma unroll
-  for (int j = 0; j < BW; j++) {
-    const double a = acc[j] > 0.0 ? acc[j] : 0.0;
-    psum[j][lane] = lane < P.H ? (double)w_h * a : 0.0;
-  }
-  wave_sync();
-  {
-    const double* pr = psum[lane & (BW - 1)];
-    double s = 0.0;
-#pragma unroll 16
-    for (int h = 0; h < 64; h++) s = s + pr[h];
-    const int e = e0 + es * lane;
-    if (lane < BW && e < M) band_s[e] = s;
-  }
-  wave_sync();  // psum is refilled by the next round
-}
-#undef LIT_BAND_QUARTER
-#undef LIT_BAND_STEP
-#undef LIT_FMAC_BCAST
-#undef LIT_FMAC_LINE
 
 // Returns false, having written nothing, when a capacity is exceeded. BF16:
 // the index q and keys are bf16 (else fp32; unused without exact mode).
