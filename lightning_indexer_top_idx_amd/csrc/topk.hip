@@ -686,9 +686,10 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         return true;
       }
       // fp64 rescoring: BW entries per wave and round, key values broadcast
-      // across each row (eight waves up to 8 * BW entries, else sixteen)
+      // across each row; as many waves as the band needs, a multiple of four
+      // (one more per SIMD), at least eight
       const float w_h = lane < P.H ? P.w[(size_t)b * P.H + lane] : 0.f;
-      const int nwr = M <= 8 * BW ? 8 : NWAVES;
+      const int nwr = min(NWAVES, max(8, ((M + BW - 1) / BW + 3) & ~3));  // 8, 12 or 16 waves
       for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW) {
         if (P.dtype == LIT_BF16)
           band_scores_bcast<true>(P, b, L.qP, w_h, L.band_n, M, base + wid, nwr, L.psum[wid], L.band_s);
@@ -986,9 +987,9 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
         return true;
       }
       // exact scores of the band, BW entries per wave and round (each wave
-      // reads its q rows once per round): eight waves, two per SIMD, for up
-      // to 8 * BW entries, else all sixteen
-      const int nwr = M <= 8 * BW ? 8 : NWAVES;
+      // reads its q rows once per round): as many waves as the band needs, a
+      // multiple of four (one more per SIMD), at least eight
+      const int nwr = min(NWAVES, max(8, ((M + BW - 1) / BW + 3) & ~3));  // 8, 12 or 16 waves
       for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW)
         band_scores_bcast<BF16>(P, b, L.qP, w_h, L.band_n, M, base + wid, nwr, L.psum[wid], L.band_s);
       lds_barrier();
