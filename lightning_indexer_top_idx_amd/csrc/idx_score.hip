@@ -130,18 +130,29 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
                                                              const uint16_t* __restrict__ k,
                                                              const uint8_t* __restrict__ allowed, int H,
                                                              int N, int nchunks, float* __restrict__ scores,
-                                                             float* __restrict__ hints, int hints_len) {
+                                                             float* __restrict__ hints, int hints_len, int seq_xcd) {
   constexpr int NH = 2 * S;  // half-steps per wave
   __shared__ u32x4 qlds[MT * 4 * 64];
   __shared__ float wlds[64];
   __shared__ float nmax[4][S];
   __shared__ double qterm[2][MT * 16];  // |w_h| ||q_h||, |w_h| (first workgroup of a sequence)
-  const int b = blockIdx.y;
+  // seq_xcd: a 1-D grid in which sequence b's workgroups all have ids equal to
+  // b modulo 8, i.e. run on XCD b % 8, where the selection of sequence b (one
+  // workgroup, id b) then finds its scores in that XCD's L2
+  int b, bx;
+  if (seq_xcd) {
+    const int nx = (nchunks + S - 1) / S, slot = (int)blockIdx.x >> 3;
+    bx = slot % nx;
+    b = (slot / nx) * 8 + ((int)blockIdx.x & 7);
+  } else {
+    b = blockIdx.y;
+    bx = blockIdx.x;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
-  const int wg_base = blockIdx.x * (S * CHUNK);
-  const bool bounds = hints && blockIdx.x == 0;
+  const int wg_base = bx * (S * CHUNK);
+  const bool bounds = hints && bx == 0;
   // half-step h: entries hbase(h) .. +31 of chunk h/2
   auto hbase = [&](int h) { return wg_base + (h >> 1) * CHUNK + wid * 64 + 32 * (h & 1); };
   // the first NB - 1 half-steps' keys are in flight while q is staged
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   }
   __syncthreads();
   if (hints && tid < S) {
-    const int chunk = blockIdx.x * S + tid;
+    const int chunk = bx * S + tid;
     if (chunk < nchunks) {
       const float m = fmaxf(fmaxf(nmax[0][tid], nmax[1][tid]), fmaxf(nmax[2][tid], nmax[3][tid]));
       hints[(size_t)b * hints_len + chunk] = norm_bound(m);
@@ -406,12 +417,15 @@ static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, 
                         int nchunks, float* scores, float* hints, int hl) {
   const uint16_t* q = (const uint16_t*)in->q;
   const uint16_t* k = (const uint16_t*)in->k;
+  // batches that fill the 8 XCDs evenly keep each sequence on one XCD
+  const int seq_xcd = grid.y % 8 == 0;
+  const dim3 g = seq_xcd ? dim3(grid.x * grid.y) : grid;
   if (S == 4)
-    idx_score_bf16_kernel<MT, 4, KEY_RING><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
+    idx_score_bf16_kernel<MT, 4, KEY_RING><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
   else if (S == 2)
-    idx_score_bf16_kernel<MT, 2, KEY_RING><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
+    idx_score_bf16_kernel<MT, 2, KEY_RING><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
   else
-    idx_score_bf16_kernel<MT, 1, KEY_RING><<<grid, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl);
+    idx_score_bf16_kernel<MT, 1, KEY_RING><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
 }
 
 template <int MT>

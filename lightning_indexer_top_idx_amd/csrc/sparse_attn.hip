@@ -122,6 +122,21 @@ __device__ __forceinline__ bool decode_unit(int X, int HG, int U, int* u, int* h
   return *u < U;
 }
 
+// Unit u (XCD u % 8) -> sequence and slice. When the batch is a multiple of 8
+// every slice of sequence b gets a unit equal to b modulo 8, so its rows, ids
+// and the selection that wrote them meet on XCD b % 8; otherwise slices of a
+// sequence are consecutive units.
+__device__ __forceinline__ void unit_seq(int u, int B, int splits, int* b, int* s) {
+  if (B % 8 == 0) {
+    const int t = u >> 3;
+    *s = t % splits;
+    *b = (t / splits) * 8 + (u & 7);
+  } else {
+    *b = u / splits;
+    *s = u % splits;
+  }
+}
+
 // Register-staged gather of one 64-row tile: BF16 rows are 64 chunks of 16 B;
 // FP8 rows 28 chunks of 16 E4M3 bytes (dequantised on the store) + 8 chunks of
 // RoPE BF16.
@@ -209,7 +224,8 @@ __global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
   const int U = P.B * P.splits;
   int u, hg;
   if (!decode_unit(blockIdx.x, HG, U, &u, &hg)) return;
-  const int b = u / P.splits, s = u % P.splits;
+  int b, s;
+  unit_seq(u, P.B, P.splits, &b, &s);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int Hq = P.Hq;
@@ -765,7 +781,8 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   const int HG = (P.Hq + MH_HEADS - 1) / MH_HEADS;
   int u, hg;
   if (!decode_unit(blockIdx.x, HG, P.B * P.splits, &u, &hg)) return;
-  const int b = u / P.splits, s = u % P.splits;
+  int b, s;
+  unit_seq(u, P.B, P.splits, &b, &s);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int Hq = P.Hq;
