@@ -31,6 +31,7 @@ namespace {
 
 constexpr int CHUNK = LIT_KNORM_CHUNK;  // 256 entries: 4 waves x 64
 constexpr int KEY_RING = 4;             // key register buffers per wave (half-steps of 32 entries)
+constexpr bool KEY_CONTIG = true;       // whole-line key loads, turned into operands through LDS
 static_assert(CHUNK == 256, "kernel tiling assumes 256-entry chunks");
 
 // Per-lane weights of the heads this lane's accumulators hold.
@@ -101,6 +102,33 @@ __device__ __forceinline__ void load_keys_half(const uint16_t* kb, int base, int
   }
 }
 
+// Contiguous form: the 32 rows of a half-step are one 8 KB block; instruction i
+// reads its 1 KB (rows 4i .. 4i+3, lane l: row 4i + l/16, dims 8(l%16) .. +7),
+// so every request covers whole cache lines. Rows at or past N read row N-1.
+__device__ __forceinline__ void load_keys_contig(const uint16_t* kb, int base, int N, int lane, u32x4 (&kr)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int e = min(base + 4 * i + (lane >> 4), N - 1);
+    kr[i] = __builtin_nontemporal_load((const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 8 * (lane & 15)));
+  }
+}
+
+// Wave-private LDS slab for turning the contiguous block into B operands:
+// 32 rows of 16 pieces of 16 bytes plus one pad piece (272-byte rows, so that
+// the 16 lanes reading one piece of 16 rows hit distinct banks).
+constexpr int KT_LD = 17;
+__device__ __forceinline__ void keys_to_operands(u32x4* slab, const u32x4 (&kr)[8], int lane, int g, int c,
+                                                 u32x4 (&op)[2][4]) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) slab[(4 * i + (lane >> 4)) * KT_LD + (lane & 15)] = kr[i];
+  // operand (G, j), lane (g, c): row 16G + c, piece g + 4j (dims 8g + 32j .. +7);
+  // LDS keeps one wave's accesses in order, so the reads see the writes
+#pragma unroll
+  for (int G = 0; G < 2; G++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) op[G][j] = slab[(16 * G + c) * KT_LD + g + 4 * j];
+}
+
 // Scores of the lane's entry (lane = 16 g + c holds entry base + lane): the
 // allowed mask applied, the score stored, and the group maximum returned in
 // the group's last lane (c = 15; a running maximum along the 16-lane row on
@@ -124,7 +152,7 @@ __device__ __forceinline__ float store_score(float v, int e, int N, const uint8_
 // (two column groups); its keys pass through a ring of NB register buffers, so
 // NB - 1 half-steps (NB - 1 times 8 KB per wave) are in flight while one is
 // multiplied.
-template <int MT, int S, int NB>
+template <int MT, int S, int NB, bool CONTIG>
 __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ w,
                                                              const uint16_t* __restrict__ k,
@@ -136,6 +164,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   __shared__ float wlds[64];
   __shared__ float nmax[4][S];
   __shared__ double qterm[2][MT * 16];  // |w_h| ||q_h||, |w_h| (first workgroup of a sequence)
+  __shared__ u32x4 kslab[CONTIG ? 4 : 1][CONTIG ? 32 * KT_LD : 1];
   // seq_xcd: a 1-D grid in which sequence b's workgroups all have ids equal to
   // b modulo 8, i.e. run on XCD b % 8, where the selection of sequence b (one
   // workgroup, id b) then finds its scores in that XCD's L2
@@ -157,9 +186,15 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   auto hbase = [&](int h) { return wg_base + (h >> 1) * CHUNK + wid * 64 + 32 * (h & 1); };
   // the first NB - 1 half-steps' keys are in flight while q is staged
   u32x4 kr[NB][2][4];
+  auto load_half = [&](int h, u32x4 (&dst)[2][4]) {
+    if (CONTIG)
+      load_keys_contig(kb, hbase(h), N, lane, reinterpret_cast<u32x4(&)[8]>(dst));
+    else
+      load_keys_half(kb, hbase(h), N, g, c, dst);
+  };
 #pragma unroll
   for (int h = 0; h < NB - 1; h++)
-    if (h < NH) load_keys_half(kb, hbase(h), N, g, c, kr[h]);
+    if (h < NH) load_half(h, kr[h]);
 
   // Stage q as MFMA A operands: operand (mt, j) lane (hh + 16*gg) holds head
   // 16*mt + hh, dims 8*gg + 32*j .. +7.
@@ -203,10 +238,12 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   float my_score = 0.f, my_n2 = 0.f;
 #pragma unroll
   for (int h = 0; h < NH; h++) {
-    if (h + NB - 1 < NH) load_keys_half(kb, hbase(h + NB - 1), N, g, c, kr[(h + NB - 1) % NB]);
+    if (h + NB - 1 < NH) load_half(h + NB - 1, kr[(h + NB - 1) % NB]);
     // keep the loads ahead of this half-step's math (the scheduler would sink them)
     __builtin_amdgcn_sched_barrier(0);
-    const u32x4 (&kc)[2][4] = kr[h % NB];
+    u32x4 kt[2][4];
+    if (CONTIG) keys_to_operands(kslab[wid], reinterpret_cast<const u32x4(&)[8]>(kr[h % NB]), lane, g, c, kt);
+    const u32x4 (&kc)[2][4] = CONTIG ? kt : kr[h % NB];
     f32x4 acc[2][MT];
 #pragma unroll
     for (int G = 0; G < 2; G++)
@@ -421,11 +458,11 @@ static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, 
   const int seq_xcd = grid.y % 8 == 0;
   const dim3 g = seq_xcd ? dim3(grid.x * grid.y) : grid;
   if (S == 4)
-    idx_score_bf16_kernel<MT, 4, KEY_RING><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 4, KEY_RING, KEY_CONTIG><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
   else if (S == 2)
-    idx_score_bf16_kernel<MT, 2, KEY_RING><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 2, KEY_RING, KEY_CONTIG><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
   else
-    idx_score_bf16_kernel<MT, 1, KEY_RING><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 1, KEY_RING, KEY_CONTIG><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
 }
 
 template <int MT>
