@@ -30,7 +30,7 @@ namespace lit {
 namespace {
 
 constexpr int CHUNK = LIT_KNORM_CHUNK;  // 256 entries: 4 waves x 64
-constexpr int KEY_RING = 4;             // key register buffers per wave (half-steps of 32 entries)
+constexpr int KEY_RING = 3;             // key register buffers per wave (half-steps of 32 entries)
 constexpr bool KEY_CONTIG = true;       // whole-line key loads, turned into operands through LDS
 static_assert(CHUNK == 256, "kernel tiling assumes 256-entry chunks");
 
@@ -151,7 +151,8 @@ __device__ __forceinline__ float store_score(float v, int e, int N, const uint8_
 // A wave works through its 64 entries of each chunk in two half-steps of 32
 // (two column groups); its keys pass through a ring of NB register buffers, so
 // NB - 1 half-steps (NB - 1 times 8 KB per wave) are in flight while one is
-// multiplied.
+// multiplied (three buffers measured fastest: a fourth adds registers, not
+// bandwidth).
 template <int MT, int S, int NB, bool CONTIG>
 __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ w,
