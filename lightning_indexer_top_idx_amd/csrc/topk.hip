@@ -47,8 +47,22 @@ constexpr int GM_CAP = 8192;                   // group maxima in LDS: N <= 1310
 constexpr int CAND_CAP = 2048;                 // candidates >= L in LDS
 constexpr int FBAND_CAP = 1024;                // exact band in LDS
 constexpr int SEL_WORDS = GM_CAP * GROUP / 32;  // selection bitmap
-// Safety factor on the rounding bound (2 already covers truncating adds).
-constexpr double ERR_SAFETY = 4.0;
+
+// Bound delta on |fp32 score - fp64 canonical score| for an entry whose key
+// norm is at most kmax. On the way to a score, every fp32 operation of
+// lit_idx_score is an add or multiply rounded at least faithfully (relative
+// error below 2^-23, truncation included): per head 128 adds of the dot product
+// (bf16 products are exact in fp32; fp32 products add one rounding each, 128
+// more), one multiply by w_h, then H - 1 adds over the heads. Each rounded
+// quantity is bounded by |w_h| ||q_h|| ||k|| (Cauchy-Schwarz), so the error is
+// below 2^-23 * nr * sum_h |w_h| ||q_h|| * kmax with nr >= the roundings on
+// any path. Flushed subnormals lose less than 2^-126 each: 128 per head scaled
+// by |w_h|, at most 2H - 1 unscaled. The factor 1 + 2^-10 covers the
+// second-order terms and the rounding of the fp64 canonical value itself.
+__device__ __forceinline__ double score_err_bound(bool bf16_in, int H, double Q, double kmax, double Wa) {
+  const double nr = (double)((bf16_in ? 1 : 2) * LIT_IDX_DIM + H + 2);
+  return (0x1p-23 * nr * Q * kmax + 0x1p-126 * (nr * Wa + 2.0 * H + 2.0)) * (1.0 + 0x1p-10);
+}
 
 __device__ __forceinline__ int padi(int i) { return i + (i >> 5); }
 
@@ -158,9 +172,7 @@ __device__ void exact_band(const TopkParams& P, int b, uint32_t tkey, float (*kr
   if (tid == 0) {
     float m = 0.f;
     for (int i = 0; i < NWAVES; i++) m = fmaxf(m, krow[0][i]);
-    const double terms = (double)(LIT_IDX_DIM + P.H + 2);
-    const double delta = (ERR_SAFETY * 0x1p-24 * terms * dmisc[0] * (double)m +
-                          ERR_SAFETY * terms * 0x1p-126 * dmisc[1]) * (1.0 + 0x1p-20);
+    const double delta = score_err_bound(P.dtype == LIT_BF16, P.H, dmisc[0], (double)m, dmisc[1]);
     const double t = (double)key_score(tkey);
     dmisc[2] = t - 2.0 * delta;
     dmisc[3] = t + 2.0 * delta;
@@ -639,9 +651,7 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
           Q += L.qn[h];
           Wa += L.wa[h];
         }
-        const double terms = (double)(LIT_IDX_DIM + P.H + 2);
-        const double delta = (ERR_SAFETY * 0x1p-24 * terms * Q * (double)knorm +
-                              ERR_SAFETY * terms * 0x1p-126 * Wa) * (1.0 + 0x1p-20);
+        const double delta = score_err_bound(P.dtype == LIT_BF16, P.H, Q, (double)knorm, Wa);
         const double t = (double)key_score(T);
         L.dmisc[2] = t - 2.0 * delta;
         L.dmisc[3] = t + 2.0 * delta;
@@ -746,59 +756,93 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
 // ---------------------------------------------------------------- small path
 
 // N <= 16 * 1024 has a kernel of its own (its own register budget): thread t
-// keeps the scores of entries 16t .. 16t+15 in registers. One histogram of all
-// keys finds the bin of the k-th score, whose few members are ranked exactly;
-// exact mode rescores the band around that score; the output is written from
-// the registers in thread order, which is index order. Every global read is
-// issued up front, reductions and scans run on DPP lane moves, and each step
-// costs one barrier.
-constexpr int SBIN_CAP = 2048;  // members of the k-th score's histogram bin
+// keeps the scores of entries 16t .. 16t+15 in registers. With four waves per
+// SIMD the workgroup's time goes mostly to issuing per-entry vector
+// instructions, so the entries are swept three times only: (1) their keys,
+// largest and smallest; (2) a histogram of the keys at or above a lower bound
+// of the k-th score, over the bits below the common prefix of that bound and
+// the largest key, which finds the bin of the k-th score; (3) a bitmask of the
+// candidates, the keys from that bin up (less the exact-mode margin of
+// 2 delta), compacted into a list of about k entries in index order. The rest
+// works on the list, one entry per thread: the bin's members are ranked
+// exactly, exact mode rescores the band around the k-th score in fp64, and the
+// selected entries are written in list order, which is index order. The lower
+// bound is the smallest of the per-16-entry score maxima of the hints (each
+// group holds an entry that large, so with k <= N/16 groups the k-th score is
+// at least that), else the smallest selectable key. Reductions and scans run
+// on DPP lane moves; each step costs one barrier.
+constexpr int SBIN_CAP = 2048;                    // members of the k-th score's histogram bin
+constexpr int SLIST_CAP = 4096;                   // candidates: k, the bin and the exact margin
+constexpr int SLIST_PT = SLIST_CAP / TK_THREADS;  // list entries per thread, at most
 
-struct SmallLds {
+struct SmallRescore {
   float qP[64 * QP_STRIDE];
   double psum[NWAVES][BW][PSUM_LD];  // head terms of the rescoring waves
+};
+struct SmallBand {
   double band_s[FBAND_CAP];
   int32_t band_n[FBAND_CAP];
-  uint32_t hist2k[2048 + 1];  // + a slot for the keys that are never selected
+};
+
+struct SmallLds {
+  union {  // the keys are dead once the candidates are listed
+    uint32_t keys[TK_THREADS * GROUP];
+    SmallRescore rs;
+  };
+  union {  // the histogram is dead once the k-th score's bin is known
+    uint32_t hist2k[2048];
+    SmallBand bd;
+  };
+  int32_t lidx[SLIST_CAP];
   uint32_t bkey[SBIN_CAP];
   int32_t bidx[SBIN_CAP];
   uint32_t sel[TK_THREADS * GROUP / 32];
   int part[6][NWAVES];  // one per block scan
-  uint32_t red_u[3][NWAVES];
-  double red_d[2][NWAVES];
+  uint32_t red_u[4][NWAVES];
   int misc[4];
 };
 
 static_assert(sizeof(SmallLds) <= 160 * 1024, "LDS budget of a gfx950 CU");
 
-
-// Returns false, having written nothing, when a capacity is exceeded. BF16:
-// the index q and keys are bf16 (else fp32; unused without exact mode).
+// Returns false, having written nothing, when a capacity is exceeded (or the
+// hints do not belong to these scores). BF16: the index q and keys are bf16
+// (else fp32; unused without exact mode).
 template <bool BF16>
 __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // every kernel argument this path reads, in SGPRs at once: their scalar
+  // loads then go out together instead of one round trip per use
+  asm volatile("" ::"s"(P.scores), "s"(P.hints), "s"(P.q), "s"(P.w), "s"(P.ids), "s"(P.mask), "s"(P.N), "s"(P.k),
+               "s"(P.exact), "s"(P.H), "s"(P.hints_len), "s"(P.nchunks));
   const int N = P.N, k = P.k;
   const float* sb = P.scores + (size_t)b * N;
   int32_t* ids = P.ids + (size_t)b * k;
   uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
   const int e0 = GROUP * tid;
+  const int G = (N + GROUP - 1) / GROUP;  // score groups, one maximum each in the hints
+  const bool full = e0 + GROUP <= N;
 
-  // 0. every global read up front: my 16 scores; in exact mode the key-norm
-  //    bounds, w and this thread's 8-dim piece of q (head tid/16)
-  //    (loads at clamped addresses, masked afterwards: nothing waits on a
-  //    branch before the next load is issued)
+  // 0. every global read up front: my 16 scores, my group's maximum; in exact
+  //    mode the key-norm bounds, w and this thread's 8-dim piece of q (head
+  //    tid/16) (loads at clamped addresses, masked afterwards: nothing waits
+  //    on a branch before the next load is issued)
   f32x4 sv[GROUP / 4];
-  if (e0 + GROUP <= N && (reinterpret_cast<uintptr_t>(sb) & 15u) == 0) {
+  if (full && (reinterpret_cast<uintptr_t>(sb) & 15u) == 0) {
 #pragma unroll
-    for (int c = 0; c < GROUP / 4; c++) sv[c] = __builtin_nontemporal_load((const f32x4*)(sb + e0 + 4 * c));
+    for (int c = 0; c < GROUP / 4; c++) sv[c] = *(const f32x4*)(sb + e0 + 4 * c);
   } else {
 #pragma unroll
     for (int c = 0; c < GROUP / 4; c++)
 #pragma unroll
       for (int i = 0; i < 4; i++) sv[c][i] = sb[min(e0 + 4 * c + i, N - 1)];
   }
+  // (loaded unconditionally, from the scores when there are no hints: a load
+  // inside a branch gets its wait placed in that branch, which would hold the
+  // loads below until the scores have arrived)
+  const bool gm_ok = P.hints != nullptr;
+  const float* gmp = gm_ok ? P.hints + (size_t)b * P.hints_len + P.nchunks : sb;
+  const float gmax = gmp[min(tid, G - 1)];
   const int qh = tid >> 4, d8 = tid & 15;
-  // exact mode: indices clamped into range so that no load sits in a branch
   float knorm = 0.f, w_h = 0.f;
   u32x4 qraw[2];
   u32x4 qbw = {0u, 0u, 0u, 0u};  // sum_h |w_h| ||q_h|| and sum_h |w_h| (fp64 word pairs) from the hints
@@ -817,47 +861,34 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
       qraw[1] = *(const u32x4*)((const float*)P.q + off + 4);
     }
   }
-  for (int i = tid; i < 2048 + 1; i += TK_THREADS) L.hist2k[i] = 0u;
+  for (int i = tid; i < 2048; i += TK_THREADS) L.hist2k[i] = 0u;
   for (int i = tid; i < TK_THREADS * GROUP / 32; i += TK_THREADS) L.sel[i] = 0u;
   uint32_t kv[GROUP];
+  if (full) {
 #pragma unroll
-  for (int i = 0; i < GROUP; i++) kv[i] = score_key(sv[i / 4][i % 4]) & (e0 + i < N ? 0xffffffffu : 0u);
+    for (int i = 0; i < GROUP; i++) kv[i] = score_key(sv[i / 4][i % 4]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) kv[i] = e0 + i < N ? score_key(sv[i / 4][i % 4]) : 0u;
+  }
 
-  // 1. min and max of the selectable keys (the histogram's range); exact mode
-  //    also stages q for the band rescoring, and wave 0 (which holds the
-  //    chunk bounds: at most 64 chunks here) takes the largest key norm
-  uint32_t kmin = 0xffffffffu, kmx = 0u;
+  // 1. largest key, smallest selectable key (key - 1 taken modulo 2^32, so
+  //    that the never-selected key 0 comes last) and smallest group-maximum key;
+  //    wave 0 (which holds the chunk bounds: at most 64 chunks here) takes the
+  //    largest key norm
+  uint32_t kmx = 0u, kmn1 = ~0u;
 #pragma unroll
-  for (int i = 0; i < GROUP; i++)
-    if (kv[i]) {
-      kmin = min(kmin, kv[i]);
-      kmx = max(kmx, kv[i]);
-    }
-  if (P.exact) {
-    if (lane >= P.H) w_h = 0.f;
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if (BF16) {
-        x[2 * i] = bf16_lo(qraw[0][i]);
-        x[2 * i + 1] = bf16_hi(qraw[0][i]);
-      } else {
-        x[i] = __uint_as_float(qraw[0][i]);
-        x[4 + i] = __uint_as_float(qraw[1][i]);
-      }
-    }
-    if (qh >= P.H) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) x[i] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++) L.qP[qh * QP_STRIDE + 8 * d8 + i] = x[i];
+  for (int i = 0; i < GROUP; i++) {
+    kmx = max(kmx, kv[i]);
+    kmn1 = min(kmn1, kv[i] - 1u);
   }
   {
-    const uint32_t mn_w = wave_min_dpp(kmin), mx_w = wave_max_dpp(kmx);
+    const uint32_t gk = gm_ok && tid < G ? score_key(gmax) : ~0u;
+    const uint32_t mn_w = wave_min_dpp(kmn1), mx_w = wave_max_dpp(kmx), gk_w = wave_min_dpp(gk);
     if (lane == 0) {
       L.red_u[0][wid] = mn_w;
       L.red_u[1][wid] = mx_w;
+      L.red_u[3][wid] = gk_w;
     }
     if (P.exact && wid == 0) {
       const uint32_t kn_w = wave_max_dpp(__float_as_uint(tid < P.nchunks ? knorm : 0.f));  // non-negative floats order as integers
@@ -866,54 +897,66 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   }
   lds_barrier();
   // the per-wave values, one per lane of each row, reduced across the row
-  const int slot = lane & 15;
-  uint32_t kn_u = 0u;
+  uint32_t kn_u = 0u, glo;
   {
-    uint32_t mn = L.red_u[0][slot], mx = L.red_u[1][slot];
+    const int slot = lane & 15;
+    uint32_t mn = L.red_u[0][slot], mx = L.red_u[1][slot], gm = L.red_u[3][slot];
     mn = min(mn, dpp_u32<0x111>(~0u, mn));
     mx = max(mx, dpp_u32<0x111>(0u, mx));
+    gm = min(gm, dpp_u32<0x111>(~0u, gm));
     mn = min(mn, dpp_u32<0x112>(~0u, mn));
     mx = max(mx, dpp_u32<0x112>(0u, mx));
+    gm = min(gm, dpp_u32<0x112>(~0u, gm));
     mn = min(mn, dpp_u32<0x114>(~0u, mn));
     mx = max(mx, dpp_u32<0x114>(0u, mx));
+    gm = min(gm, dpp_u32<0x114>(~0u, gm));
     mn = min(mn, dpp_u32<0x118>(~0u, mn));
     mx = max(mx, dpp_u32<0x118>(0u, mx));
-    kmin = (uint32_t)__builtin_amdgcn_readlane((int)mn, 15);
+    gm = min(gm, dpp_u32<0x118>(~0u, gm));
+    kmn1 = (uint32_t)__builtin_amdgcn_readlane((int)mn, 15);
     kmx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 15);
+    glo = (uint32_t)__builtin_amdgcn_readlane((int)gm, 15);
     if (P.exact) kn_u = L.red_u[2][0];
   }
-  double Q = 0.0, Wa = 0.0;
+  double Q = 0.0, Wa = 0.0, delta = 0.0;
   if (P.exact) {
     Q = __longlong_as_double((long long)(((uint64_t)qbw[1] << 32) | qbw[0]));
     Wa = __longlong_as_double((long long)(((uint64_t)qbw[3] << 32) | qbw[2]));
+    // fp32 scores are within delta of their fp64 canonical values
+    delta = score_err_bound(BF16, P.H, Q, (double)__uint_as_float(kn_u), Wa);
   }
+  // lower bound of the k-th key: the smallest group maximum when every group
+  // has a selectable entry and k <= G, else the smallest selectable key (at
+  // least 1: key 0 is never selected)
+  const uint32_t kmin = kmn1 + 1u;
+  const bool useL = gm_ok && k <= G && glo > 0u;
+  uint32_t Lb = useL ? max(glo, kmin) : kmin;
+  Lb = Lb > 1u ? Lb : 1u;
 
-  // selected: key > hi (bits in `mine`, taken as soon as hi is known so that
-  // the keys die early), or a band or bin member marked in sel
-  auto keys_above = [&](uint32_t hi) {
-    uint32_t m = 0u;
-#pragma unroll
-    for (int i = 0; i < GROUP; i++) m |= (uint32_t)(kv[i] > hi) << i;
-    return m;
-  };
-  uint32_t mine;
-  // 2. one histogram of all keys over the bits below their common prefix (the
-  //    key that is never selected, 0, goes to a bin of its own); its total is
-  //    the number of selectable entries
-  const uint32_t diff = kmin ^ kmx;
+  // 2. histogram of the keys >= Lb over the bits below the common prefix of
+  //    Lb and the largest key; the keys also go to LDS for the candidate list
+  const uint32_t diff = Lb ^ kmx;
   const int hb = diff ? 31 - __clz((int)diff) : 0;
   const int shift = hb > 10 ? hb - 10 : 0;
   const uint32_t prefix = kmx & ~((2u << hb) - 1u);
   auto binof = [&](uint32_t kk) -> uint32_t { return (kk - prefix) >> shift; };
 #pragma unroll
-  for (int i = 0; i < GROUP; i++) atomicAdd(&L.hist2k[kv[i] ? binof(kv[i]) : 2048u], 1u);
+  for (int i = 0; i < GROUP; i++)
+    if (kv[i] >= Lb) atomicAdd(&L.hist2k[binof(kv[i])], 1u);
+#pragma unroll
+  for (int c = 0; c < GROUP / 4; c++) {  // chunk-major: a wave's stores are contiguous
+    const u32x4 kq = {kv[4 * c], kv[4 * c + 1], kv[4 * c + 2], kv[4 * c + 3]};
+    *(u32x4*)&L.keys[c * (4 * TK_THREADS) + 4 * tid] = kq;
+  }
   lds_barrier();
   const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
   int tot;
-  const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.part[1], &tot);
-  if (tot <= k) {
-    mine = keys_above(0u);  // every selectable entry
-  } else {
+  const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.part[0], &tot);
+  if (useL && tot < k) return false;  // hints of other scores
+  // every histogrammed entry is selected (exact mode with the group bound
+  // still ranks: entries below the bound may rank above in fp64)
+  const bool all = tot <= k && !(P.exact && useL);
+  if (!all) {
     if (ab < k && k <= ab + c0) {
       L.misc[0] = 2047 - 2 * tid;
       L.misc[1] = ab;
@@ -921,103 +964,178 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
       L.misc[0] = 2046 - 2 * tid;
       L.misc[1] = ab + c0;
     }
-    lds_barrier();
+  }
+  lds_barrier();
+  // the k-th key's bin holds keys mlo .. blast (the histogrammed ones); r of
+  // them are selected
+  uint32_t mlo = Lb, blast = 0u, L0 = Lb, band_hi = 0u;
+  int r = 0;
+  if (!all) {
     const uint32_t bin_t = (uint32_t)L.misc[0];
-    const int r = k - L.misc[1];  // members of bin_t that are selected
-    // 3. the members of bin_t, in index order, ranked exactly
-    int nb = 0;
+    r = k - L.misc[1];
+    const uint32_t binlo = prefix + (bin_t << shift);
+    blast = binlo + ((1u << shift) - 1u);
+    mlo = max(binlo, Lb);
+    L0 = mlo;
+    if (P.exact) {
+      // the k-th fp32 key T lies in mlo .. blast; the k-th fp64 score is within
+      // delta of T, so entries above blast + 2 delta are in, entries below
+      // mlo - 2 delta out, and the band between is rescored (it holds
+      // T - 2 delta .. T + 2 delta and the rest of the bin)
+      const double s_lo = (double)key_score(max(mlo, 0x00800000u));
+      const double s_hi = (double)key_score(min(blast, 0xff800000u));
+      const uint32_t l0 = score_key(__double2float_rd(s_lo - 2.0 * delta));
+      L0 = l0 > 1u ? l0 : 1u;
+      band_hi = score_key(__double2float_ru(s_hi + 2.0 * delta));
+    }
+  }
+
+  // 3. candidates (keys >= L0) listed in index order
+  uint32_t cm = 0u;
 #pragma unroll
-    for (int i = 0; i < GROUP; i++) nb += kv[i] && binof(kv[i]) == bin_t;
+  for (int i = 0; i < GROUP; i++) cm |= (uint32_t)(kv[i] >= L0) << i;
+  int nlist;
+  int cpos = block_excl_scan1<NWAVES>(__popc(cm), L.part[1], &nlist);
+  if (nlist > SLIST_CAP) return false;
+  while (cm) {
+    L.lidx[cpos++] = e0 + __ffs(cm) - 1;
+    cm &= cm - 1u;
+  }
+  lds_barrier();
+  // thread t owns list entries per*t .. per*t + per - 1 (index order kept)
+  const int per = (nlist + TK_THREADS - 1) / TK_THREADS;
+  const int la = min(nlist, per * tid), ln = min(nlist, la + per) - la;
+  uint32_t lk[SLIST_PT];
+  int li[SLIST_PT];
+#pragma unroll
+  for (int j = 0; j < SLIST_PT; j++) {
+    li[j] = j < ln ? L.lidx[la + j] : 0;
+    lk[j] = j < ln ? L.keys[((li[j] >> 2) & 3) * (4 * TK_THREADS) + (li[j] >> 4) * 4 + (li[j] & 3)] : 0u;
+  }
+
+  uint32_t hi_sel = 0u;  // list entries with a key above this are selected
+  if (!all && !P.exact) {
+    // 4. the members of the k-th key's bin, in index order, ranked exactly
+    int nm = 0;
+#pragma unroll
+    for (int j = 0; j < SLIST_PT; j++) nm += j < ln && lk[j] >= mlo && lk[j] <= blast;
     int m;
-    int bp = block_excl_scan1<NWAVES>(nb, L.part[2], &m);
+    int mp = block_excl_scan1<NWAVES>(nm, L.part[2], &m);
     if (m > SBIN_CAP) return false;
 #pragma unroll
-    for (int i = 0; i < GROUP; i++)
-      if (kv[i] && binof(kv[i]) == bin_t) {
-        L.bkey[bp] = kv[i];
-        L.bidx[bp] = e0 + i;
-        bp++;
+    for (int j = 0; j < SLIST_PT; j++)
+      if (j < ln && lk[j] >= mlo && lk[j] <= blast) {
+        L.bkey[mp] = lk[j];
+        L.bidx[mp] = li[j];
+        mp++;
       }
     lds_barrier();
-    for (int t = tid; t < m; t += TK_THREADS) {
-      const uint32_t ki = L.bkey[t];
+    // rank of member i: members before it in (key desc, index asc), counted
+    // by ballots over 64 members at a time; one wave per member
+    for (int i = wid; i < m; i += NWAVES) {
+      const uint32_t ki = L.bkey[i];
       int rank = 0;
-      for (int j = 0; j < m; j++) {
-        const uint32_t kj = L.bkey[j];
-        rank += (kj > ki) || (kj == ki && j < t);
+      for (int j0 = 0; j0 < m; j0 += 64) {
+        const int j = j0 + lane;
+        const uint32_t kj = j < m ? L.bkey[j] : 0u;
+        rank += __popcll(__ballot(j < m && (kj > ki || (kj == ki && j < i))));
       }
-      if (!P.exact && rank < r) atomicOr(&L.sel[L.bidx[t] >> 5], 1u << (L.bidx[t] & 31));
-      if (rank == r - 1) L.misc[2] = (int)ki;
+      if (lane == 0 && rank < r) atomicOr(&L.sel[L.bidx[i] >> 5], 1u << (L.bidx[i] & 31));
+    }
+    hi_sel = blast;  // everything in higher bins, and the r marked members
+    lds_barrier();
+  } else if (!all) {
+    // 4. exact band: the list entries up to band_hi (all are >= its lower end)
+    int nd = 0, nbd = 0;
+#pragma unroll
+    for (int j = 0; j < SLIST_PT; j++) {
+      nd += j < ln && lk[j] > band_hi;
+      nbd += j < ln && lk[j] <= band_hi;
+    }
+    int tb;
+    int pos = block_excl_scan1<NWAVES>((nd << 16) | nbd, L.part[3], &tb);
+    pos &= 0xffff;
+    const int A = tb >> 16, M = tb & 0xffff;
+    if (M > FBAND_CAP) return false;
+#pragma unroll
+    for (int j = 0; j < SLIST_PT; j++)
+      if (j < ln && lk[j] <= band_hi) L.bd.band_n[pos++] = li[j];
+    {
+      // the keys are dead (read before the scan's barrier): q goes to LDS for
+      // the band rescoring (w_h passes an empty asm first, which keeps its use,
+      // and so the wait for its load, from being hoisted to the load)
+      asm volatile("" : "+v"(w_h));
+      if (lane >= P.H) w_h = 0.f;
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (BF16) {
+          x[2 * i] = bf16_lo(qraw[0][i]);
+          x[2 * i + 1] = bf16_hi(qraw[0][i]);
+        } else {
+          x[i] = __uint_as_float(qraw[0][i]);
+          x[4 + i] = __uint_as_float(qraw[1][i]);
+        }
+      }
+      if (qh >= P.H) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) x[i] = 0.f;
+      }
+      *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8] = f32x4{x[0], x[1], x[2], x[3]};
+      *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
     }
     lds_barrier();
-    const uint32_t T = (uint32_t)L.misc[2];
-    if (!P.exact) {
-      mine = 0u;  // everything in higher bins
-#pragma unroll
-      for (int i = 0; i < GROUP; i++) mine |= (uint32_t)(kv[i] != 0u && binof(kv[i]) > bin_t) << i;
-    } else {
-      // 4. exact band around T: fp32 scores are within delta of their fp64
-      //    values, so entries above T + 2 delta are in, below T - 2 delta out
-      const double terms = (double)(LIT_IDX_DIM + P.H + 2);
-      const double delta = (ERR_SAFETY * 0x1p-24 * terms * Q * (double)__uint_as_float(kn_u) +
-                            ERR_SAFETY * terms * 0x1p-126 * Wa) * (1.0 + 0x1p-20);
-      const double t = (double)key_score(T);
-      const uint32_t lo0 = score_key(__double2float_rd(t - 2.0 * delta));
-      const uint32_t lo = lo0 > 1u ? lo0 : 1u;
-      const uint32_t hi = score_key(__double2float_ru(t + 2.0 * delta));
-      mine = keys_above(hi);
-      int nd = 0, nbd = 0;
-#pragma unroll
-      for (int i = 0; i < GROUP; i++) {
-        nd += kv[i] > hi;
-        nbd += kv[i] >= lo && kv[i] <= hi;
-      }
-      int tb;
-      int pos = block_excl_scan1<NWAVES>((nd << 16) | nbd, L.part[3], &tb);
-      pos &= 0xffff;
-      const int A = tb >> 16, M = tb & 0xffff;
-      if (M > FBAND_CAP) return false;
-#pragma unroll
-      for (int i = 0; i < GROUP; i++)
-        if (kv[i] >= lo && kv[i] <= hi) L.band_n[pos++] = e0 + i;
-      lds_barrier();
-      const int rr = k - A;
-      if (rr < 1 || rr > M) {
-        report_violation(P, b, ids, mask);
-        return true;
-      }
-      // exact scores of the band, BW entries per wave and round (each wave
-      // reads its q rows once per round): as many waves as the band needs, a
-      // multiple of four (one more per SIMD), at least eight
-      const int nwr = min(NWAVES, max(8, ((M + BW - 1) / BW + 3) & ~3));  // 8, 12 or 16 waves
-      for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW)
-        band_scores_bcast<BF16>(P, b, L.qP, w_h, L.band_n, M, base + wid, nwr, L.psum[wid], L.band_s);
-      lds_barrier();
-      for (int i = tid; i < M; i += TK_THREADS) {
-        const double si = L.band_s[i];
-        int rank = 0;
-        for (int j = 0; j < M; j++) {
-          const double sj = L.band_s[j];
-          rank += (sj > si) || (sj == si && j < i);  // the band is in index order
-        }
-        if (rank < rr) atomicOr(&L.sel[L.band_n[i] >> 5], 1u << (L.band_n[i] & 31));
-      }
+    const int rr = k - A;
+    if (rr < 1 || rr > M) {
+      report_violation(P, b, ids, mask);
+      return true;
     }
+    // 5. exact scores of the band, BW entries per wave and round (each wave
+    //    reads its q rows once per round): as many waves as the band needs, a
+    //    multiple of four (one more per SIMD), at least eight
+    const int nwr = min(NWAVES, max(8, ((M + BW - 1) / BW + 3) & ~3));  // 8, 12 or 16 waves
+    for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW)
+      band_scores_bcast<BF16>(P, b, L.rs.qP, w_h, L.bd.band_n, M, base + wid, nwr, L.rs.psum[wid], L.bd.band_s);
+    lds_barrier();
+    // the rr best of the band by (score desc, index asc): ballots as above
+    for (int i = wid; i < M; i += NWAVES) {
+      const double si = L.bd.band_s[i];
+      int rank = 0;
+      for (int j0 = 0; j0 < M; j0 += 64) {
+        const int j = j0 + lane;
+        const double sj = j < M ? L.bd.band_s[j] : 0.0;
+        rank += __popcll(__ballot(j < M && (sj > si || (sj == si && j < i))));  // the band is in index order
+      }
+      if (lane == 0 && rank < rr) atomicOr(&L.sel[L.bd.band_n[i] >> 5], 1u << (L.bd.band_n[i] & 31));
+    }
+    hi_sel = band_hi;
     lds_barrier();
   }
 
-  // 5. output in thread order = index order
-  mine |= (L.sel[e0 >> 5] >> (e0 & 31)) & 0xffffu;
-  int total;
-  int opos = block_excl_scan1<NWAVES>(__popc(mine), L.part[4], &total);
+  // 6. output in list order = index order; the selection bitmap feeds the mask
+  uint32_t sm = 0u;
 #pragma unroll
-  for (int i = 0; i < GROUP; i++)
-    if ((mine >> i) & 1u) {
-      if (opos < k) ids[opos] = e0 + i;
+  for (int j = 0; j < SLIST_PT; j++)
+    if (j < ln) {
+      const uint32_t bit = 1u << (li[j] & 31);
+      if (lk[j] > hi_sel) {
+        sm |= 1u << j;
+        if (mask) atomicOr(&L.sel[li[j] >> 5], bit);
+      } else if (L.sel[li[j] >> 5] & bit) {
+        sm |= 1u << j;
+      }
+    }
+  int total;
+  int opos = block_excl_scan1<NWAVES>(__popc(sm), L.part[4], &total);
+#pragma unroll
+  for (int j = 0; j < SLIST_PT; j++)
+    if ((sm >> j) & 1u) {
+      if (opos < k) ids[opos] = li[j];
       opos++;
     }
   if (mask && e0 < N) {
-    if (e0 + GROUP <= N && (reinterpret_cast<uintptr_t>(mask) & 15u) == 0) {
+    const uint32_t mine = (L.sel[e0 >> 5] >> (e0 & 31)) & 0xffffu;
+    if (full && (reinterpret_cast<uintptr_t>(mask) & 15u) == 0) {
       u32x4 mv;
 #pragma unroll
       for (int w = 0; w < 4; w++)
@@ -1028,8 +1146,8 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
       for (int i = 0; i < GROUP && e0 + i < N; i++) mask[e0 + i] = (mine >> i) & 1u;
     }
   }
-  for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
-  if (tid == 0) P.count[b] = total;
+  for (int j = min(total, k) + tid; j < k; j += TK_THREADS) ids[j] = -1;
+  if (tid == 0) P.count[b] = min(total, k);
   return true;
 }
 
