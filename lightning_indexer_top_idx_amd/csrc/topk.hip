@@ -757,23 +757,26 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
 
 // N <= 16 * 1024 has a kernel of its own (its own register budget): thread t
 // keeps the scores of entries 16t .. 16t+15 in registers. With four waves per
-// SIMD the workgroup's time goes mostly to issuing per-entry vector
-// instructions, so the entries are swept three times only: (1) their keys,
-// largest and smallest; (2) a histogram of the keys at or above a lower bound
-// of the k-th score, over the bits below the common prefix of that bound and
-// the largest key, which finds the bin of the k-th score; (3) a bitmask of the
-// candidates, the keys from that bin up (less the exact-mode margin of
-// 2 delta), compacted into a list of about k entries in index order. The rest
-// works on the list, one entry per thread: the bin's members are ranked
-// exactly, exact mode rescores the band around the k-th score in fp64, and the
-// selected entries are written in list order, which is index order. The lower
-// bound is the smallest of the per-16-entry score maxima of the hints (each
-// group holds an entry that large, so with k <= N/16 groups the k-th score is
-// at least that), else the smallest selectable key. Reductions and scans run
-// on DPP lane moves; each step costs one barrier.
-constexpr int SBIN_CAP = 2048;                    // members of the k-th score's histogram bin
-constexpr int SLIST_CAP = 4096;                   // candidates: k, the bin and the exact margin
-constexpr int SLIST_PT = SLIST_CAP / TK_THREADS;  // list entries per thread, at most
+// SIMD the workgroup's time goes to issuing per-entry vector instructions and
+// to the barriers between its steps, so the entries are swept twice only, and
+// the steps are few:
+//   1. the range of the histogram comes from the hints alone (largest and
+//      smallest of the per-16-entry score maxima; each group holds an entry
+//      that large, so with k <= N/16 groups the k-th score is at least the
+//      smallest), reduced while the scores are still in flight; without
+//      usable hints, from the keys;
+//   2. a histogram of the keys in that range, over the bits below the common
+//      prefix of its ends, finds the bin of the k-th score;
+//   3. each entry is then "above" (selected for sure) or in the band (decided
+//      by rank) or out: the band is the bin itself (ranked by key and index),
+//      or in exact mode the bin widened by 2 delta both ways, whose entries
+//      are rescored in fp64; one scan gives every thread the number of above
+//      and band entries before its own;
+//   4. the output offset of a thread is the above entries before it plus the
+//      chosen band entries before its first band slot, so each thread writes
+//      its selected ids in index order with no further scan.
+// Reductions and scans run on DPP lane moves; each step costs one barrier.
+constexpr int SBIN_CAP = 2048;  // members of the k-th score's histogram bin (non-exact band)
 
 struct SmallRescore {
   float qP[64 * QP_STRIDE];
@@ -781,28 +784,36 @@ struct SmallRescore {
 };
 struct SmallBand {
   double band_s[FBAND_CAP];
-  int32_t band_n[FBAND_CAP];
+  int32_t band_n[SBIN_CAP];
 };
 
 struct SmallLds {
-  union {  // the keys are dead once the candidates are listed
-    uint32_t keys[TK_THREADS * GROUP];
-    SmallRescore rs;
-  };
+  SmallRescore rs;
   union {  // the histogram is dead once the k-th score's bin is known
     uint32_t hist2k[2048];
     SmallBand bd;
   };
-  int32_t lidx[SLIST_CAP];
-  uint32_t bkey[SBIN_CAP];
-  int32_t bidx[SBIN_CAP];
-  uint32_t sel[TK_THREADS * GROUP / 32];
-  int part[6][NWAVES];  // one per block scan
-  uint32_t red_u[4][NWAVES];
+  uint32_t bkey[SBIN_CAP];            // keys of the band (non-exact)
+  uint32_t chosen[SBIN_CAP / 32];     // band slots selected
+  int part[4][NWAVES];                // one per block scan
+  uint32_t red_u[6][NWAVES];
   int misc[4];
 };
 
 static_assert(sizeof(SmallLds) <= 160 * 1024, "LDS budget of a gfx950 CU");
+
+// the per-wave values red[0..15] reduced across a row of lanes (every lane
+// gets the result): min when MIN, else max
+template <bool MIN>
+__device__ __forceinline__ uint32_t row_reduce16(const uint32_t* red) {
+  const uint32_t id = MIN ? ~0u : 0u;
+  uint32_t v = red[threadIdx.x & 15];
+  v = MIN ? min(v, dpp_u32<0x111>(id, v)) : max(v, dpp_u32<0x111>(id, v));
+  v = MIN ? min(v, dpp_u32<0x112>(id, v)) : max(v, dpp_u32<0x112>(id, v));
+  v = MIN ? min(v, dpp_u32<0x114>(id, v)) : max(v, dpp_u32<0x114>(id, v));
+  v = MIN ? min(v, dpp_u32<0x118>(id, v)) : max(v, dpp_u32<0x118>(id, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+}
 
 // Returns false, having written nothing, when a capacity is exceeded (or the
 // hints do not belong to these scores). BF16: the index q and keys are bf16
@@ -822,12 +833,19 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   const int G = (N + GROUP - 1) / GROUP;  // score groups, one maximum each in the hints
   const bool full = e0 + GROUP <= N;
 
-  // 0. every global read up front: my 16 scores, my group's maximum; in exact
-  //    mode the key-norm bounds, w and this thread's 8-dim piece of q (head
-  //    tid/16) (loads at clamped addresses, masked afterwards: nothing waits
-  //    on a branch before the next load is issued)
+  // 0. every global read up front, the group maximum first (its reduction
+  //    runs while the scores are in flight); in exact mode the key-norm
+  //    bounds, w and this thread's 8-dim piece of q (head tid/16). Loads go to
+  //    clamped addresses and are masked afterwards, and none sits in a branch:
+  //    the compiler places a load's wait where the branch joins, which would
+  //    hold every load issued after it
+  const bool gm_ok = P.hints != nullptr;
+  const float* gmp = gm_ok ? P.hints + (size_t)b * P.hints_len + P.nchunks : sb;
+  const float gmax = gmp[min(tid, G - 1)];
   f32x4 sv[GROUP / 4];
   if (full && (reinterpret_cast<uintptr_t>(sb) & 15u) == 0) {
+    // (plain loads: the scores were just written and sit in L2, which
+    // non-temporal loads would pass by)
 #pragma unroll
     for (int c = 0; c < GROUP / 4; c++) sv[c] = *(const f32x4*)(sb + e0 + 4 * c);
   } else {
@@ -836,12 +854,6 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
 #pragma unroll
       for (int i = 0; i < 4; i++) sv[c][i] = sb[min(e0 + 4 * c + i, N - 1)];
   }
-  // (loaded unconditionally, from the scores when there are no hints: a load
-  // inside a branch gets its wait placed in that branch, which would hold the
-  // loads below until the scores have arrived)
-  const bool gm_ok = P.hints != nullptr;
-  const float* gmp = gm_ok ? P.hints + (size_t)b * P.hints_len + P.nchunks : sb;
-  const float gmax = gmp[min(tid, G - 1)];
   const int qh = tid >> 4, d8 = tid & 15;
   float knorm = 0.f, w_h = 0.f;
   u32x4 qraw[2];
@@ -862,7 +874,23 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
     }
   }
   for (int i = tid; i < 2048; i += TK_THREADS) L.hist2k[i] = 0u;
-  for (int i = tid; i < TK_THREADS * GROUP / 32; i += TK_THREADS) L.sel[i] = 0u;
+  if (tid < SBIN_CAP / 32) L.chosen[tid] = 0u;
+  if (tid == 0) L.misc[3] = 0;
+
+  // 1. largest and smallest group-maximum key; wave 0 (which holds the chunk
+  //    bounds: at most 64 chunks here) takes the largest key norm
+  {
+    const uint32_t gk = score_key(gmax);
+    const uint32_t mx_w = wave_max_dpp(tid < G ? gk : 0u), mn_w = wave_min_dpp(tid < G ? gk : ~0u);
+    if (lane == 0) {
+      L.red_u[0][wid] = mx_w;
+      L.red_u[1][wid] = mn_w;
+    }
+    if (P.exact && wid == 0) {
+      const uint32_t kn_w = wave_max_dpp(__float_as_uint(tid < P.nchunks ? knorm : 0.f));  // non-negative floats order as integers
+      if (lane == 0) L.red_u[2][0] = kn_w;
+    }
+  }
   uint32_t kv[GROUP];
   if (full) {
 #pragma unroll
@@ -871,84 +899,64 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
 #pragma unroll
     for (int i = 0; i < GROUP; i++) kv[i] = e0 + i < N ? score_key(sv[i / 4][i % 4]) : 0u;
   }
-
-  // 1. largest key, smallest selectable key (key - 1 taken modulo 2^32, so
-  //    that the never-selected key 0 comes last) and smallest group-maximum key;
-  //    wave 0 (which holds the chunk bounds: at most 64 chunks here) takes the
-  //    largest key norm
-  uint32_t kmx = 0u, kmn1 = ~0u;
-#pragma unroll
-  for (int i = 0; i < GROUP; i++) {
-    kmx = max(kmx, kv[i]);
-    kmn1 = min(kmn1, kv[i] - 1u);
-  }
-  {
-    const uint32_t gk = gm_ok && tid < G ? score_key(gmax) : ~0u;
-    const uint32_t mn_w = wave_min_dpp(kmn1), mx_w = wave_max_dpp(kmx), gk_w = wave_min_dpp(gk);
-    if (lane == 0) {
-      L.red_u[0][wid] = mn_w;
-      L.red_u[1][wid] = mx_w;
-      L.red_u[3][wid] = gk_w;
-    }
-    if (P.exact && wid == 0) {
-      const uint32_t kn_w = wave_max_dpp(__float_as_uint(tid < P.nchunks ? knorm : 0.f));  // non-negative floats order as integers
-      if (lane == 0) L.red_u[2][0] = kn_w;
-    }
-  }
   lds_barrier();
-  // the per-wave values, one per lane of each row, reduced across the row
-  uint32_t kn_u = 0u, glo;
-  {
-    const int slot = lane & 15;
-    uint32_t mn = L.red_u[0][slot], mx = L.red_u[1][slot], gm = L.red_u[3][slot];
-    mn = min(mn, dpp_u32<0x111>(~0u, mn));
-    mx = max(mx, dpp_u32<0x111>(0u, mx));
-    gm = min(gm, dpp_u32<0x111>(~0u, gm));
-    mn = min(mn, dpp_u32<0x112>(~0u, mn));
-    mx = max(mx, dpp_u32<0x112>(0u, mx));
-    gm = min(gm, dpp_u32<0x112>(~0u, gm));
-    mn = min(mn, dpp_u32<0x114>(~0u, mn));
-    mx = max(mx, dpp_u32<0x114>(0u, mx));
-    gm = min(gm, dpp_u32<0x114>(~0u, gm));
-    mn = min(mn, dpp_u32<0x118>(~0u, mn));
-    mx = max(mx, dpp_u32<0x118>(0u, mx));
-    gm = min(gm, dpp_u32<0x118>(~0u, gm));
-    kmn1 = (uint32_t)__builtin_amdgcn_readlane((int)mn, 15);
-    kmx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 15);
-    glo = (uint32_t)__builtin_amdgcn_readlane((int)gm, 15);
-    if (P.exact) kn_u = L.red_u[2][0];
+  uint32_t kmx = row_reduce16<false>(L.red_u[0]);
+  const uint32_t glo = row_reduce16<true>(L.red_u[1]);
+  const uint32_t kn_u = P.exact ? L.red_u[2][0] : 0u;
+  // the group bound holds when every group has a selectable entry and k <= G
+  const bool useL = gm_ok && k <= G && glo > 0u;
+  uint32_t Lb;
+  if (useL) {
+    Lb = glo;
+  } else {
+    // the smallest selectable key (key - 1 taken modulo 2^32, so that the
+    // never-selected key 0 comes last) and the largest, from the keys
+    uint32_t kx = 0u, kn1 = ~0u;
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) {
+      kx = max(kx, kv[i]);
+      kn1 = min(kn1, kv[i] - 1u);
+    }
+    kx = wave_max_dpp(kx);
+    kn1 = wave_min_dpp(kn1);
+    if (lane == 0) {
+      L.red_u[3][wid] = kx;
+      L.red_u[4][wid] = kn1;
+    }
+    lds_barrier();
+    kmx = row_reduce16<false>(L.red_u[3]);
+    Lb = row_reduce16<true>(L.red_u[4]) + 1u;  // 0 when nothing is selectable
+    Lb = Lb > 1u ? Lb : 1u;
   }
-  double Q = 0.0, Wa = 0.0, delta = 0.0;
+  double delta = 0.0;
   if (P.exact) {
-    Q = __longlong_as_double((long long)(((uint64_t)qbw[1] << 32) | qbw[0]));
-    Wa = __longlong_as_double((long long)(((uint64_t)qbw[3] << 32) | qbw[2]));
+    const double Q = __longlong_as_double((long long)(((uint64_t)qbw[1] << 32) | qbw[0]));
+    const double Wa = __longlong_as_double((long long)(((uint64_t)qbw[3] << 32) | qbw[2]));
     // fp32 scores are within delta of their fp64 canonical values
     delta = score_err_bound(BF16, P.H, Q, (double)__uint_as_float(kn_u), Wa);
   }
-  // lower bound of the k-th key: the smallest group maximum when every group
-  // has a selectable entry and k <= G, else the smallest selectable key (at
-  // least 1: key 0 is never selected)
-  const uint32_t kmin = kmn1 + 1u;
-  const bool useL = gm_ok && k <= G && glo > 0u;
-  uint32_t Lb = useL ? max(glo, kmin) : kmin;
-  Lb = Lb > 1u ? Lb : 1u;
 
-  // 2. histogram of the keys >= Lb over the bits below the common prefix of
-  //    Lb and the largest key; the keys also go to LDS for the candidate list
+  // 2. histogram of the keys in Lb .. kmx over the bits below the common
+  //    prefix of the two (a key above the hints' largest means hints of other
+  //    scores: no histogram then, and the path gives up)
   const uint32_t diff = Lb ^ kmx;
   const int hb = diff ? 31 - __clz((int)diff) : 0;
   const int shift = hb > 10 ? hb - 10 : 0;
   const uint32_t prefix = kmx & ~((2u << hb) - 1u);
-  auto binof = [&](uint32_t kk) -> uint32_t { return (kk - prefix) >> shift; };
+  {
+    uint32_t kr = kv[0];
 #pragma unroll
-  for (int i = 0; i < GROUP; i++)
-    if (kv[i] >= Lb) atomicAdd(&L.hist2k[binof(kv[i])], 1u);
+    for (int i = 1; i < GROUP; i++) kr = max(kr, kv[i]);
+    if (kr > kmx) {
+      L.misc[3] = 1;
+    } else {
 #pragma unroll
-  for (int c = 0; c < GROUP / 4; c++) {  // chunk-major: a wave's stores are contiguous
-    const u32x4 kq = {kv[4 * c], kv[4 * c + 1], kv[4 * c + 2], kv[4 * c + 3]};
-    *(u32x4*)&L.keys[c * (4 * TK_THREADS) + 4 * tid] = kq;
+      for (int i = 0; i < GROUP; i++)
+        if (kv[i] >= Lb) atomicAdd(&L.hist2k[(kv[i] - prefix) >> shift], 1u);
+    }
   }
   lds_barrier();
+  if (L.misc[3]) return false;
   const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
   int tot;
   const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.part[0], &tot);
@@ -966,138 +974,94 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
     }
   }
   lds_barrier();
-  // the k-th key's bin holds keys mlo .. blast (the histogrammed ones); r of
-  // them are selected
-  uint32_t mlo = Lb, blast = 0u, L0 = Lb, band_hi = 0u;
+
+  // 3. above (key > hi_sel) and band (blo <= key <= hi_sel) entries
+  uint32_t hi_sel = Lb - 1u, blo = Lb;  // all: every histogrammed key is above, no band
   int r = 0;
   if (!all) {
+    // the k-th key's bin holds keys mlo .. blast (the histogrammed ones); r of
+    // them are selected
     const uint32_t bin_t = (uint32_t)L.misc[0];
     r = k - L.misc[1];
     const uint32_t binlo = prefix + (bin_t << shift);
-    blast = binlo + ((1u << shift) - 1u);
-    mlo = max(binlo, Lb);
-    L0 = mlo;
+    const uint32_t blast = binlo + ((1u << shift) - 1u);
+    const uint32_t mlo = max(binlo, Lb);
+    hi_sel = blast;
+    blo = mlo;
     if (P.exact) {
-      // the k-th fp32 key T lies in mlo .. blast; the k-th fp64 score is within
-      // delta of T, so entries above blast + 2 delta are in, entries below
-      // mlo - 2 delta out, and the band between is rescored (it holds
-      // T - 2 delta .. T + 2 delta and the rest of the bin)
+      // the k-th fp32 key T lies in mlo .. blast and the k-th fp64 score is
+      // within delta of T: entries above blast + 2 delta are in, entries below
+      // mlo - 2 delta out, and the band between (which holds T - 2 delta ..
+      // T + 2 delta and the rest of the bin) is rescored
       const double s_lo = (double)key_score(max(mlo, 0x00800000u));
       const double s_hi = (double)key_score(min(blast, 0xff800000u));
       const uint32_t l0 = score_key(__double2float_rd(s_lo - 2.0 * delta));
-      L0 = l0 > 1u ? l0 : 1u;
-      band_hi = score_key(__double2float_ru(s_hi + 2.0 * delta));
+      blo = l0 > 1u ? l0 : 1u;
+      hi_sel = score_key(__double2float_ru(s_hi + 2.0 * delta));
     }
   }
-
-  // 3. candidates (keys >= L0) listed in index order
-  uint32_t cm = 0u;
+  uint32_t am = 0u, bm = 0u;
 #pragma unroll
-  for (int i = 0; i < GROUP; i++) cm |= (uint32_t)(kv[i] >= L0) << i;
-  int nlist;
-  int cpos = block_excl_scan1<NWAVES>(__popc(cm), L.part[1], &nlist);
-  if (nlist > SLIST_CAP) return false;
-  while (cm) {
-    L.lidx[cpos++] = e0 + __ffs(cm) - 1;
-    cm &= cm - 1u;
+  for (int i = 0; i < GROUP; i++) am |= (uint32_t)(kv[i] > hi_sel) << i;
+  if (!all) {
+    const uint32_t bw = hi_sel - blo;
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) bm |= (uint32_t)(kv[i] - blo <= bw) << i;
   }
-  lds_barrier();
-  // thread t owns list entries per*t .. per*t + per - 1 (index order kept)
-  const int per = (nlist + TK_THREADS - 1) / TK_THREADS;
-  const int la = min(nlist, per * tid), ln = min(nlist, la + per) - la;
-  uint32_t lk[SLIST_PT];
-  int li[SLIST_PT];
+  int tab;
+  const int pab = block_excl_scan1<NWAVES>((__popc(am) << 16) | __popc(bm), L.part[1], &tab);
+  const int A = tab >> 16, M = tab & 0xffff;     // above and band totals
+  const int apos = pab >> 16, bpos = pab & 0xffff;  // mine before me
+  if (M > (P.exact ? FBAND_CAP : SBIN_CAP)) return false;
+  if (bm) {
+    int p = bpos;
 #pragma unroll
-  for (int j = 0; j < SLIST_PT; j++) {
-    li[j] = j < ln ? L.lidx[la + j] : 0;
-    lk[j] = j < ln ? L.keys[((li[j] >> 2) & 3) * (4 * TK_THREADS) + (li[j] >> 4) * 4 + (li[j] & 3)] : 0u;
+    for (int i = 0; i < GROUP; i++)
+      if ((bm >> i) & 1u) {
+        L.bd.band_n[p] = e0 + i;
+        if (!P.exact) L.bkey[p] = kv[i];
+        p++;
+      }
   }
-
-  uint32_t hi_sel = 0u;  // list entries with a key above this are selected
-  if (!all && !P.exact) {
-    // 4. the members of the k-th key's bin, in index order, ranked exactly
-    int nm = 0;
+  int nsel = 0;  // band entries selected
+  if (!all && P.exact) {
+    // q goes to LDS for the rescoring (w_h passes an empty asm first, which
+    // keeps its use, and so the wait for its load, from being hoisted to the
+    // load)
+    asm volatile("" : "+v"(w_h));
+    if (lane >= P.H) w_h = 0.f;
+    float x[8];
 #pragma unroll
-    for (int j = 0; j < SLIST_PT; j++) nm += j < ln && lk[j] >= mlo && lk[j] <= blast;
-    int m;
-    int mp = block_excl_scan1<NWAVES>(nm, L.part[2], &m);
-    if (m > SBIN_CAP) return false;
-#pragma unroll
-    for (int j = 0; j < SLIST_PT; j++)
-      if (j < ln && lk[j] >= mlo && lk[j] <= blast) {
-        L.bkey[mp] = lk[j];
-        L.bidx[mp] = li[j];
-        mp++;
+    for (int i = 0; i < 4; i++) {
+      if (BF16) {
+        x[2 * i] = bf16_lo(qraw[0][i]);
+        x[2 * i + 1] = bf16_hi(qraw[0][i]);
+      } else {
+        x[i] = __uint_as_float(qraw[0][i]);
+        x[4 + i] = __uint_as_float(qraw[1][i]);
       }
-    lds_barrier();
-    // rank of member i: members before it in (key desc, index asc), counted
-    // by ballots over 64 members at a time; one wave per member
-    for (int i = wid; i < m; i += NWAVES) {
-      const uint32_t ki = L.bkey[i];
-      int rank = 0;
-      for (int j0 = 0; j0 < m; j0 += 64) {
-        const int j = j0 + lane;
-        const uint32_t kj = j < m ? L.bkey[j] : 0u;
-        rank += __popcll(__ballot(j < m && (kj > ki || (kj == ki && j < i))));
-      }
-      if (lane == 0 && rank < r) atomicOr(&L.sel[L.bidx[i] >> 5], 1u << (L.bidx[i] & 31));
     }
-    hi_sel = blast;  // everything in higher bins, and the r marked members
-    lds_barrier();
-  } else if (!all) {
-    // 4. exact band: the list entries up to band_hi (all are >= its lower end)
-    int nd = 0, nbd = 0;
+    if (qh >= P.H) {
 #pragma unroll
-    for (int j = 0; j < SLIST_PT; j++) {
-      nd += j < ln && lk[j] > band_hi;
-      nbd += j < ln && lk[j] <= band_hi;
+      for (int i = 0; i < 8; i++) x[i] = 0.f;
     }
-    int tb;
-    int pos = block_excl_scan1<NWAVES>((nd << 16) | nbd, L.part[3], &tb);
-    pos &= 0xffff;
-    const int A = tb >> 16, M = tb & 0xffff;
-    if (M > FBAND_CAP) return false;
-#pragma unroll
-    for (int j = 0; j < SLIST_PT; j++)
-      if (j < ln && lk[j] <= band_hi) L.bd.band_n[pos++] = li[j];
-    {
-      // the keys are dead (read before the scan's barrier): q goes to LDS for
-      // the band rescoring (w_h passes an empty asm first, which keeps its use,
-      // and so the wait for its load, from being hoisted to the load)
-      asm volatile("" : "+v"(w_h));
-      if (lane >= P.H) w_h = 0.f;
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        if (BF16) {
-          x[2 * i] = bf16_lo(qraw[0][i]);
-          x[2 * i + 1] = bf16_hi(qraw[0][i]);
-        } else {
-          x[i] = __uint_as_float(qraw[0][i]);
-          x[4 + i] = __uint_as_float(qraw[1][i]);
-        }
-      }
-      if (qh >= P.H) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) x[i] = 0.f;
-      }
-      *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8] = f32x4{x[0], x[1], x[2], x[3]};
-      *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
-    }
+    *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8] = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
     lds_barrier();
-    const int rr = k - A;
-    if (rr < 1 || rr > M) {
+    nsel = k - A;
+    if (nsel < 1 || nsel > M) {
       report_violation(P, b, ids, mask);
       return true;
     }
-    // 5. exact scores of the band, BW entries per wave and round (each wave
-    //    reads its q rows once per round): as many waves as the band needs, a
-    //    multiple of four (one more per SIMD), at least eight
+    // exact scores of the band, BW entries per wave and round (each wave
+    // reads its q rows once per round): as many waves as the band needs, a
+    // multiple of four (one more per SIMD), at least eight
     const int nwr = min(NWAVES, max(8, ((M + BW - 1) / BW + 3) & ~3));  // 8, 12 or 16 waves
     for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW)
       band_scores_bcast<BF16>(P, b, L.rs.qP, w_h, L.bd.band_n, M, base + wid, nwr, L.rs.psum[wid], L.bd.band_s);
     lds_barrier();
-    // the rr best of the band by (score desc, index asc): ballots as above
+    // the nsel best of the band by (score desc, index asc): the rank of slot i
+    // counted by ballots over 64 slots at a time, one wave per slot
     for (int i = wid; i < M; i += NWAVES) {
       const double si = L.bd.band_s[i];
       int rank = 0;
@@ -1106,48 +1070,66 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
         const double sj = j < M ? L.bd.band_s[j] : 0.0;
         rank += __popcll(__ballot(j < M && (sj > si || (sj == si && j < i))));  // the band is in index order
       }
-      if (lane == 0 && rank < rr) atomicOr(&L.sel[L.bd.band_n[i] >> 5], 1u << (L.bd.band_n[i] & 31));
+      if (lane == 0 && rank < nsel) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
     }
-    hi_sel = band_hi;
+    lds_barrier();
+  } else if (!all) {
+    lds_barrier();
+    // the r best members of the bin by (key desc, index asc), as above
+    nsel = r;
+    for (int i = wid; i < M; i += NWAVES) {
+      const uint32_t ki = L.bkey[i];
+      int rank = 0;
+      for (int j0 = 0; j0 < M; j0 += 64) {
+        const int j = j0 + lane;
+        const uint32_t kj = j < M ? L.bkey[j] : 0u;
+        rank += __popcll(__ballot(j < M && (kj > ki || (kj == ki && j < i))));
+      }
+      if (lane == 0 && rank < nsel) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
+    }
     lds_barrier();
   }
 
-  // 6. output in list order = index order; the selection bitmap feeds the mask
-  uint32_t sm = 0u;
-#pragma unroll
-  for (int j = 0; j < SLIST_PT; j++)
-    if (j < ln) {
-      const uint32_t bit = 1u << (li[j] & 31);
-      if (lk[j] > hi_sel) {
-        sm |= 1u << j;
-        if (mask) atomicOr(&L.sel[li[j] >> 5], bit);
-      } else if (L.sel[li[j] >> 5] & bit) {
-        sm |= 1u << j;
-      }
+  // 4. output in index order: my offset is the above entries before me plus
+  //    the chosen band slots before my first one
+  uint32_t sm = am;
+  int opos = apos;
+  if (!all) {
+    for (int w = 0; w < (bpos >> 5); w++) opos += __popc(L.chosen[w]);
+    if (bpos & 31) opos += __popc(L.chosen[bpos >> 5] & ((1u << (bpos & 31)) - 1u));
+    uint32_t rest = bm;
+    int p = bpos;
+    while (rest) {
+      const int i = __ffs(rest) - 1;
+      if ((L.chosen[p >> 5] >> (p & 31)) & 1u) sm |= 1u << i;
+      p++;
+      rest &= rest - 1u;
     }
-  int total;
-  int opos = block_excl_scan1<NWAVES>(__popc(sm), L.part[4], &total);
-#pragma unroll
-  for (int j = 0; j < SLIST_PT; j++)
-    if ((sm >> j) & 1u) {
-      if (opos < k) ids[opos] = li[j];
+  }
+  {
+    uint32_t rest = sm;
+    while (rest) {
+      const int i = __ffs(rest) - 1;
+      if (opos < k) ids[opos] = e0 + i;
       opos++;
+      rest &= rest - 1u;
     }
+  }
   if (mask && e0 < N) {
-    const uint32_t mine = (L.sel[e0 >> 5] >> (e0 & 31)) & 0xffffu;
     if (full && (reinterpret_cast<uintptr_t>(mask) & 15u) == 0) {
       u32x4 mv;
 #pragma unroll
       for (int w = 0; w < 4; w++)
-        mv[w] = ((mine >> (4 * w)) & 1u) | (((mine >> (4 * w + 1)) & 1u) << 8) | (((mine >> (4 * w + 2)) & 1u) << 16) |
-                (((mine >> (4 * w + 3)) & 1u) << 24);
+        mv[w] = ((sm >> (4 * w)) & 1u) | (((sm >> (4 * w + 1)) & 1u) << 8) | (((sm >> (4 * w + 2)) & 1u) << 16) |
+                (((sm >> (4 * w + 3)) & 1u) << 24);
       *(u32x4*)(mask + e0) = mv;
     } else {
-      for (int i = 0; i < GROUP && e0 + i < N; i++) mask[e0 + i] = (mine >> i) & 1u;
+      for (int i = 0; i < GROUP && e0 + i < N; i++) mask[e0 + i] = (sm >> i) & 1u;
     }
   }
-  for (int j = min(total, k) + tid; j < k; j += TK_THREADS) ids[j] = -1;
-  if (tid == 0) P.count[b] = min(total, k);
+  const int total = min(A + nsel, k);
+  for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
+  if (tid == 0) P.count[b] = total;
   return true;
 }
 
