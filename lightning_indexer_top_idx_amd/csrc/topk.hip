@@ -1008,6 +1008,21 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
 #pragma unroll
     for (int i = 0; i < GROUP; i++) bm |= (uint32_t)(kv[i] - blo <= bw) << i;
   }
+  // exact mode: the key rows of my first two band entries are requested now
+  // (a dword from each of their first two 128-byte lines), so that the
+  // rescoring finds them in L2 rather than waiting on HBM; the values only
+  // feed an empty asm at the end (and so are not waited for before it)
+  uint32_t touch[4] = {0u, 0u, 0u, 0u};
+  if (P.exact && bm) {
+    constexpr int RW = LIT_IDX_DIM * (BF16 ? 2 : 4) / 4;  // dwords per key row
+    const uint32_t* kb = reinterpret_cast<const uint32_t*>(P.kidx) + (size_t)b * N * RW;
+    const uint32_t bm2 = bm & (bm - 1u);
+    const int ea = e0 + __ffs(bm) - 1, eb = bm2 ? e0 + __ffs(bm2) - 1 : ea;
+    touch[0] = kb[(size_t)ea * RW];
+    touch[1] = kb[(size_t)ea * RW + 32];
+    touch[2] = kb[(size_t)eb * RW];
+    touch[3] = kb[(size_t)eb * RW + 32];
+  }
   int tab;
   const int pab = block_excl_scan1<NWAVES>((__popc(am) << 16) | __popc(bm), L.part[1], &tab);
   const int A = tab >> 16, M = tab & 0xffff;     // above and band totals
@@ -1130,6 +1145,7 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   const int total = min(A + nsel, k);
   for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
   if (tid == 0) P.count[b] = total;
+  asm volatile("" ::"v"(touch[0]), "v"(touch[1]), "v"(touch[2]), "v"(touch[3]));
   return true;
 }
 
