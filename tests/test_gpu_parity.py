@@ -199,6 +199,23 @@ def test_topk_with_hints_on_fp32_order():
         check_selection(ids, cnt, mask, rids, rcnt, rmask, None, f"fp32 order N={N} k={k}")
 
 
+def test_topk_with_hints_of_other_scores_falls_back():
+    # hints computed for other scores: their group maxima may lie below or above
+    # these scores' own; the selection detects that (a key above the hinted
+    # largest, or fewer than k entries above the hinted bound) and takes the
+    # full scan, so the result is still the exact top-k of the scores given
+    for N, k in ((16384, 512), (4000, 256)):
+        a = W.layer_inputs(W.CTX64K, 1, "cpu", B=2, N=N).idx
+        o = W.layer_inputs(W.CTX64K, 2, "cpu", B=2, N=N).idx
+        scores, _ = lit.idx_score(dev(a.q_idx), dev(a.w), dev(a.k_idx))
+        for scale in (0.25, 4.0):
+            _, hints = lit.idx_score(dev(o.q_idx), dev(o.w) * scale, dev(o.k_idx))
+            ids, cnt, mask = lit.topk_select(scores, k, hints=hints)
+            torch.cuda.synchronize()
+            rids, rcnt, rmask = oracle.topk(scores.double().cpu().numpy(), k)
+            check_selection(ids, cnt, mask, rids, rcnt, rmask, None, f"other hints N={N} x{scale}")
+
+
 def test_idx_score_exact_matches_oracle_bit_for_bit():
     for wl, B, N in ((W.TINY, None, None), (W.CTX64K, 2, 3001)):
         inp = W.layer_inputs(wl, 0, "cpu", B=B, N=N).idx
