@@ -11,6 +11,8 @@
  *   lit_golden_topp_vote top-p 0.6 per layer, then a cross-layer vote (labels)
  *   lit_recall           set overlap of two selections
  *   lit_lsa_gate         sigmoid chunk gate of FlashMemory/LSA (candidate set)
+ *   lit_pool_plan / lit_pool_gather / lit_pool_remap_ids
+ *                        the LSA cold-pool fetch: gated entries into a compact pool
  *
  * Pages cited (title, then the part of the page):
  *   [ARCH]  ai-muninn.com, "284B 塞得進 128GB、長 context 還跑得動:DeepSeek-V4-Flash
@@ -83,7 +85,8 @@ typedef enum {
   LIT_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
   LIT_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination */
   LIT_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
-  LIT_ERR_LAUNCH = 6     /* the HIP runtime refused a launch or query */
+  LIT_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch or query */
+  LIT_ERR_MEMORY = 7     /* host memory the device must read is not page-locked */
 } lit_status;
 
 typedef enum {
@@ -285,6 +288,49 @@ lit_status lit_lsa_gate(const lit_gate_layer* layers, int32_t n_layers, int32_t 
                         int32_t H, int32_t d_model, int32_t rank, double threshold,
                         uint8_t* gate, int32_t* gate_count, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* ---- NEXT: the LSA cold-pool fetch -------------------------------------------------
+ * [LSA] 2.2: every tau = 64 decode steps the gate's kept blocks are moved from a
+ * CPU "cold pool" to the GPU and the steps in between attend only inside the
+ * moved set, so that GPU memory follows the gate, not the context length; the
+ * later section of the same page notes that the swap engine was not published.
+ * The three calls below form one: plan the compact pool from the gate, gather
+ * each per-entry array (index keys, latent rows, their FP8 parts) into it, run
+ * lit_idx_score / lit_topk_select / lit_sparse_attn_decode on the compact pool
+ * (N = C, allowed = allowed_c, the same window), then map the selected ids back.
+ * The compact pool keeps the original order of the entries, so the selection and
+ * the attention output equal those of the same calls on the resident arrays
+ * with allowed = gate.
+ *
+ * lit_pool_plan: for sequence b the kept entries are
+ *     K_b = {n : gate[b][n] != 0}  union  {N - W' .. N - 1},  W' = min(window, N)
+ * in ascending order, right-aligned in C slots so that the window stays in the
+ * last W' slots:  map[b][C - |K_b| + i] = the i-th entry of K_b,  map[b][j] = -1
+ * before that;  allowed_c[b][j] = 1 where map[b][j] is a gated entry (window
+ * entries outside the gate get 0; allowed_c may be NULL);  count[b] = |K_b|.
+ * When |K_b| > C the pool is too small: map[b] is all -1, allowed_c[b] all 0, and
+ * count[b] = |K_b| tells the caller by how much.
+ * gate : [B][N] u8;  map : [B][C] int32 output;  count : [B] int32 output;
+ * allowed_c : [B][C] u8 output or NULL. */
+lit_status lit_pool_plan(const uint8_t* gate, int32_t B, int32_t N, int32_t window, int32_t C,
+                         int32_t* map, int32_t* count, uint8_t* allowed_c, void* stream);
+
+/* lit_pool_gather: dst[b][j][:] = src[b][map[b][j]][:] (row_bytes bytes), and zeros
+ * where map[b][j] is -1 or not below src_rows.
+ * src : [B][src_rows][row_bytes] bytes, either device memory or page-locked
+ *       (pinned) HOST memory, which the kernel reads in place over the host link;
+ *       pageable host memory returns LIT_ERR_MEMORY.
+ * map : [B][C] int32 (from lit_pool_plan);  dst : [B][C][row_bytes] device output.
+ * row_bytes is a multiple of 4 (1 MiB at most); src, dst and map 4-byte aligned. */
+lit_status lit_pool_gather(const void* src, int32_t src_rows, int64_t row_bytes, int32_t B,
+                           const int32_t* map, int32_t C, void* dst, void* stream);
+
+/* lit_pool_remap_ids: ids[b][j] = map[b][ids_c[b][j]] for j < count[b], -1 after
+ * (ids_c and count as lit_topk_select wrote them on the compact pool). Ascending
+ * compact ids give ascending original ids.
+ * ids_c, ids : [B][k] int32;  count : [B] int32;  map : [B][C] int32. */
+lit_status lit_pool_remap_ids(const int32_t* ids_c, const int32_t* count, int32_t B, int32_t k,
+                              const int32_t* map, int32_t C, int32_t* ids, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,7 @@ raises.
 
 Functions (same names as the C entry points, without the lit_ prefix):
   idx_score, topk_select, sparse_attn_decode, golden_topk, golden_topp_vote,
-  idx_score_exact, recall, lsa_gate.
+  idx_score_exact, recall, lsa_gate, pool_plan, pool_gather, pool_remap_ids.
 """
 from __future__ import annotations
 
@@ -28,13 +28,13 @@ KNORM_CHUNK = 256
 DEFAULT_SCALE = 1.0 / math.sqrt(KV_DIM)
 
 _STATUS = {0: "LIT_OK", 1: "LIT_ERR_NULL", 2: "LIT_ERR_SHAPE", 3: "LIT_ERR_ALIGN", 4: "LIT_ERR_DTYPE",
-           5: "LIT_ERR_WORKSPACE", 6: "LIT_ERR_LAUNCH"}
+           5: "LIT_ERR_WORKSPACE", 6: "LIT_ERR_LAUNCH", 7: "LIT_ERR_MEMORY"}
 
 EXPORTS = [
     "lit_abi_version", "lit_last_error", "lit_idx_hints_len", "lit_idx_score", "lit_topk_workspace_bytes", "lit_topk_select",
     "lit_attn_workspace_bytes", "lit_sparse_attn_decode", "lit_golden_workspace_bytes", "lit_golden_topk",
     "lit_topp_workspace_bytes", "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall",
-    "lit_gate_workspace_bytes", "lit_lsa_gate",
+    "lit_gate_workspace_bytes", "lit_lsa_gate", "lit_pool_plan", "lit_pool_gather", "lit_pool_remap_ids",
 ]
 
 
@@ -95,8 +95,12 @@ def load(path: str = LIB_PATH):
     L.lit_gate_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.lit_gate_workspace_bytes.restype = sz
     L.lit_lsa_gate.argtypes = [ctypes.POINTER(GateLayerDesc), i32, i32, i32, i32, i32, i32, f64, vp, vp, vp, sz, vp]
+    L.lit_pool_plan.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.lit_pool_gather.argtypes = [vp, i32, ctypes.c_int64, i32, vp, i32, vp, vp]
+    L.lit_pool_remap_ids.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
     for name in ("lit_idx_score", "lit_topk_select", "lit_sparse_attn_decode", "lit_golden_topk",
-                 "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall", "lit_lsa_gate"):
+                 "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall", "lit_lsa_gate", "lit_pool_plan",
+                 "lit_pool_gather", "lit_pool_remap_ids"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -317,3 +321,48 @@ def lsa_gate(layers: Sequence, threshold: float = 0.5, ws=None):
     _check(L.lit_lsa_gate(descs, len(layers), B, N, H, d_model, rank, float(threshold), gate.data_ptr(),
                           count.data_ptr(), ws.data_ptr(), ws.numel(), _stream(g0.h)))
     return gate, count
+
+
+def pool_plan(gate, window: int, C: int, want_allowed: bool = True):
+    """The compact pool of the LSA fetch: gate [B,N] u8 -> map [B,C] int32 (the
+    gated entries plus the window, ascending, right-aligned; -1 before them),
+    count [B] int32 (> C: the pool is too small), allowed_c [B,C] u8."""
+    torch = _torch()
+    _need_cuda(gate)
+    B, N = gate.shape
+    dev = gate.device
+    m = torch.empty(B, C, dtype=torch.int32, device=dev)
+    count = torch.empty(B, dtype=torch.int32, device=dev)
+    ac = torch.empty(B, C, dtype=torch.uint8, device=dev) if want_allowed else None
+    _check(load().lit_pool_plan(gate.data_ptr(), B, N, int(window), int(C), m.data_ptr(), count.data_ptr(), _ptr(ac),
+                                _stream(gate)))
+    return m, count, ac
+
+
+def pool_gather(src, m, out=None):
+    """Rows of src [B,src_rows,...] (a GPU tensor, or a pinned CPU tensor read in
+    place over the host link) through map m [B,C] -> [B,C,...] on the GPU
+    (zeros for empty slots)."""
+    torch = _torch()
+    _need_cuda(m)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    if not src.is_cuda and not src.is_pinned():
+        raise ValueError("a CPU src must be pinned (page-locked)")
+    B, C = m.shape
+    rows = src.shape[1]
+    row_bytes = src[0, 0].numel() * src.element_size() if src.dim() > 2 else src.element_size()
+    dst = out if out is not None else torch.empty((B, C) + tuple(src.shape[2:]), dtype=src.dtype, device=m.device)
+    _check(load().lit_pool_gather(src.data_ptr(), rows, row_bytes, B, m.data_ptr(), C, dst.data_ptr(), _stream(m)))
+    return dst
+
+
+def pool_remap_ids(ids_c, count, m):
+    """Selected compact ids [B,k] (with their count [B]) -> original entry ids [B,k]."""
+    torch = _torch()
+    _need_cuda(ids_c, count, m)
+    B, k = ids_c.shape
+    ids = torch.empty_like(ids_c)
+    _check(load().lit_pool_remap_ids(ids_c.data_ptr(), count.data_ptr(), B, k, m.data_ptr(), m.shape[1],
+                                     ids.data_ptr(), _stream(ids_c)))
+    return ids

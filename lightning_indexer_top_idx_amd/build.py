@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblit.so")
 ARCH = os.environ.get("LIT_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["capi.hip", "idx_score.hip", "topk.hip", "sparse_attn.hip", "recall.hip", "golden.hip", "lsa_gate.hip"]
+SOURCES = ["capi.hip", "idx_score.hip", "topk.hip", "sparse_attn.hip", "recall.hip", "golden.hip", "lsa_gate.hip",
+           "pool.hip"]
 HEADERS = ["lit_common.h", "exact.h", "select.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -270,6 +270,28 @@ def lsa_gate(layers, threshold: float = 0.5, return_z: bool = False):
     return (gate, count, zs) if return_z else (gate, count)
 
 
+def pool_plan(gate, window: int, C: int):
+    """The LSA cold-pool fetch ([LSA] 2.2: the kept blocks move to the GPU, the
+    steps in between attend only inside them). Per sequence the kept entries are
+    the gated ones and the last min(window, N) ones (the SWA window is always
+    attended), in ascending order, placed in the last |K| of C slots, -1 in the
+    slots before; allowed_c marks the gated ones. When |K| > C nothing fits: the
+    map is all -1. Returns map [B,C] int32, count [B] int32, allowed_c [B,C] u8."""
+    g = np.asarray(np_of(gate)) != 0
+    B, N = g.shape
+    W = min(window, N)
+    m = np.full((B, C), -1, np.int32)
+    ac = np.zeros((B, C), np.uint8)
+    cnt = np.zeros(B, np.int32)
+    for b in range(B):
+        kept = sorted(set(np.flatnonzero(g[b]).tolist()) | set(range(N - W, N)))
+        cnt[b] = len(kept)
+        if len(kept) <= C:
+            m[b, C - len(kept):] = kept
+            ac[b, C - len(kept):] = g[b, kept]
+    return m, cnt, ac
+
+
 def topp_vote(x, is_logits: bool, top_p: float = 0.6, min_votes: int = 3):
     """a9 ([LSA] 3.2): x [L,B,N] fp64 -> gold [B,N] u8, gold_count [B], votes [B,N]."""
     x = np.ascontiguousarray(np_of(x), np.float64)

@@ -475,3 +475,43 @@ def test_kv_cache_871_mib_reconstruction():
     hca = 20 * 512 * 512 * 4
     swa = 43 * 128 * 512 * 4
     assert (csa + hca + swa) / 2**20 == 870.75
+
+
+# ---------------------------------------------------------------- cold-pool plan
+
+
+def test_pool_plan_hand_worked_cases():
+    # nothing gated: only the window (the last W entries) is kept, right-aligned
+    m, c, a = oracle.pool_plan(np.zeros((1, 10), np.uint8), 3, 5)
+    assert m.tolist() == [[-1, -1, 7, 8, 9]] and c.tolist() == [3] and a.tolist() == [[0, 0, 0, 0, 0]]
+    # everything gated: every entry, all allowed
+    m, c, a = oracle.pool_plan(np.ones((1, 6), np.uint8), 2, 8)
+    assert m.tolist() == [[-1, -1, 0, 1, 2, 3, 4, 5]] and c.tolist() == [6]
+    assert a.tolist() == [[0, 0, 1, 1, 1, 1, 1, 1]]
+    # gated {0, 3, 7}, window {6, 7}: union {0, 3, 6, 7} fills C = 4 exactly;
+    # 6 is kept for the window only, so it is not a scoring candidate
+    g = np.array([[1, 0, 0, 1, 0, 0, 0, 1]], np.uint8)
+    m, c, a = oracle.pool_plan(g, 2, 4)
+    assert m.tolist() == [[0, 3, 6, 7]] and c.tolist() == [4] and a.tolist() == [[1, 1, 0, 1]]
+    # one slot short: nothing fits, the count says how many were needed
+    m, c, a = oracle.pool_plan(g, 2, 3)
+    assert m.tolist() == [[-1, -1, -1]] and c.tolist() == [4] and a.sum() == 0
+    # a window longer than the sequence keeps the whole sequence
+    m, c, _ = oracle.pool_plan(np.zeros((1, 3), np.uint8), 16, 3)
+    assert m.tolist() == [[0, 1, 2]] and c.tolist() == [3]
+    # no window: the gated entries alone
+    m, c, _ = oracle.pool_plan(g, 0, 5)
+    assert m.tolist() == [[-1, -1, 0, 3, 7]] and c.tolist() == [3]
+
+
+def test_pool_plan_invariants_on_random_gates():
+    g = (rng.random((5, 300)) < np.array([0.0, 0.05, 0.3, 0.9, 1.0])[:, None]).astype(np.uint8)
+    m, c, a = oracle.pool_plan(g, 32, 300)
+    for b in range(5):
+        kept = m[b][m[b] >= 0]
+        assert len(kept) == c[b] and (np.diff(kept) > 0).all()            # ascending, distinct
+        assert (m[b][: 300 - c[b]] == -1).all()                             # right-aligned
+        assert set(range(268, 300)) <= set(kept.tolist())                   # the window is in
+        assert set(np.flatnonzero(g[b]).tolist()) <= set(kept.tolist())     # every gated entry is in
+        assert (a[b][300 - c[b]:] == g[b][kept]).all() and a[b][: 300 - c[b]].sum() == 0
+        assert c[b] == len(set(np.flatnonzero(g[b]).tolist()) | set(range(268, 300)))
