@@ -14,7 +14,8 @@ the eager result) and replayed. Besides the headline line the JSON carries:
                  the stream it runs on, against the 8 TB/s HBM peak;
   cpu_baseline : the CPU oracle on a bounded sample of the same queries;
   others       : the 64K batch-1 latency and the 500K batch-4 step (distinct
-                 layers rotated so every replay streams from HBM).
+                 layers rotated so every replay streams from HBM), and the LSA
+                 cold-pool fetch at the gate workload's shapes.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 from __future__ import annotations
@@ -53,10 +54,10 @@ def idx_score_bytes_per_query(N, H):
 class Path:
     """Preallocated buffers of one layer of B sequences and the three C calls."""
 
-    def __init__(self, lit, L, k, window, scale, dev):
+    def __init__(self, lit, L, k, window, scale, dev, allowed=None):
         import torch
 
-        self.lit, self.L = lit, L
+        self.lit, self.L, self.allowed = lit, L, allowed
         self.B, self.N = L.idx.k_idx.shape[0], L.idx.k_idx.shape[1]
         self.H, self.Hq = L.idx.q_idx.shape[1], L.q.shape[1]
         self.k, self.window, self.scale = k, window, scale
@@ -75,8 +76,9 @@ class Path:
         self.C = C
 
     def score(self, stream):
-        st = self.C.lit_idx_score(ctypes.byref(self.idx_desc), None, self.B, self.N, self.scores.data_ptr(),
-                                  self.hints.data_ptr(), stream)
+        st = self.C.lit_idx_score(ctypes.byref(self.idx_desc),
+                                  None if self.allowed is None else self.allowed.data_ptr(), self.B, self.N,
+                                  self.scores.data_ptr(), self.hints.data_ptr(), stream)
         assert st == 0, self.lit.last_error()
 
     def select(self, stream):
@@ -354,7 +356,89 @@ def others(lit, W, dev, scale):
                          "hbm_frac": round(per_query * wl.B / csa_s / 1e9 / HBM_PEAK_GBS, 4),
                          "hca_layer_us": round(hca_s * 1e6, 2),
                          "hca_hbm_frac": round(wl.B * wl.hca_N * 1024 / hca_s / 1e9 / HBM_PEAK_GBS, 4)}
+    del gc, gh, csa_paths, hkvs
+    torch.cuda.empty_cache()
+    res["gate64k_offload"] = offload(lit, W, dev, scale)
     return res
+
+
+def offload(lit, W, dev, scale):
+    """The LSA cold-pool fetch at the gate workload's shapes (8 sequences, N =
+    16384, FP8 rows, top-1024, gate at layers 10/12/20): one CSA layer's index
+    keys and latent rows live in pinned host memory; the gate's kept entries
+    (plus the window) are gathered over the host link into a compact pool, and
+    the decode step runs on that pool. Reported: the fetch (per layer, and per
+    tau = 64 steps for the 21 CSA layers), the link rate it reaches next to a
+    plain pinned-to-device copy, and the step on the compact pool next to the
+    same step on the resident arrays with the gate as the allowed set (the two
+    are checked equal first)."""
+    import torch
+    from lightning_indexer_top_idx_amd import synth
+
+    wl = W.GATE64K
+    keys = [W.layer_inputs(wl, l, dev).idx.k_idx for l in W.GATE_LAYERS]
+    gl = [W.gate_layer(wl, l, kk, dev) for l, kk in zip(W.GATE_LAYERS, keys)]
+    gate, gcnt = lit.lsa_gate(gl, 0.5)
+    del gl, keys
+    L = W.layer_inputs(wl, 10, dev)
+    # the pool holds the largest kept set (a first plan at full size counts them)
+    _, pc, _ = lit.pool_plan(gate, wl.window, wl.N)
+    C = min(wl.N, int((pc.max().item() + 63) // 64 * 64))
+    m, pc, ac = lit.pool_plan(gate, wl.window, C)
+    host = [t.cpu().pin_memory() for t in (L.idx.k_idx, L.kv.data, L.kv.rope, L.kv.scale)]
+    bufs = [torch.empty((wl.B, C) + tuple(t.shape[2:]), dtype=t.dtype, device=dev) for t in host]
+    row_bytes = sum(t[0, 0].numel() * t.element_size() for t in host)
+
+    def fetch():
+        for t, o in zip(host, bufs):
+            lit.pool_gather(t, m, out=o)
+
+    fetch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        fetch()
+    e1.record()
+    torch.cuda.synchronize()
+    fetch_s = e0.elapsed_time(e1) / 1e3 / reps
+    link_bytes = int(pc.sum().item()) * row_bytes
+    # a plain copy of as many bytes from pinned memory (the runtime's DMA engines)
+    cp_src = torch.empty(link_bytes, dtype=torch.uint8).pin_memory()
+    cp_dst = torch.empty(link_bytes, dtype=torch.uint8, device=dev)
+    cp_dst.copy_(cp_src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        cp_dst.copy_(cp_src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 1e3 / reps
+    # the decode step, resident (gate as allowed) and on the compact pool
+    Pr = Path(lit, L, wl.k, wl.window, scale, dev, allowed=gate)
+    Lc = W.LayerInputs(synth.IndexerInputs(L.idx.q_idx, L.idx.w, bufs[0]), L.q,
+                       synth.KVRows("fp8", bufs[1], bufs[2], bufs[3]))
+    Pc = Path(lit, Lc, wl.k, wl.window, scale, dev, allowed=ac)
+    s0 = torch.cuda.current_stream().cuda_stream
+    Pr.run(s0)
+    Pc.run(s0)
+    ids_o = lit.pool_remap_ids(Pc.ids, Pc.count, m)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ids_o, Pr.ids) and torch.equal(Pc.count, Pr.count) and torch.equal(Pc.out, Pr.out))
+    gr, gcp = capture(Pr.run), capture(Pc.run)
+    resident_s = time_graph(gr, 20) / 20
+    compact_s = time_graph(gcp, 20) / 20
+    return {"sequences": wl.B, "entries": wl.N, "keep_frac": round(float(gcnt.float().mean().item()) / wl.N, 4),
+            "pool_rows": C, "row_bytes": row_bytes, "fetch_bytes_per_layer": link_bytes,
+            "fetch_us_per_layer": round(fetch_s * 1e6, 1), "link_GBs": round(link_bytes / fetch_s / 1e9, 2),
+            "pinned_copy_GBs": round(link_bytes / copy_s / 1e9, 2),
+            "fetch_ms_per_tau_21_layers": round(21 * fetch_s * 1e3, 2),
+            "fetch_us_per_step_amortized": round(21 * fetch_s * 1e6 / 64, 1),
+            "step_us_resident_gated": round(resident_s * 1e6, 2), "step_us_compact_pool": round(compact_s * 1e6, 2),
+            "compact_equals_resident": same,
+            "note": "one CSA layer's keys + FP8 rows (840 B per entry) fetched from pinned host memory by the "
+                    "gather kernel; per-tau and per-step figures scale it to the 21 CSA layers"}
 
 
 if __name__ == "__main__":

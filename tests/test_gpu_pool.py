@@ -88,7 +88,8 @@ def test_offload_step_equals_resident_gated_step():
     ids, cnt, _ = lit.topk_select(s, wl.k, exact=(q, w, kk), hints=h)
     out, lse = lit.sparse_attn_decode(L.q, L.kv, ids, cnt, wl.window, SCALE)
     # the cold pool, and the compact pool sized to the largest kept set
-    need = int(((gate.sum(1) + wl.window).max().item() + 63) // 64 * 64)
+    _, pc, _ = lit.pool_plan(gate, wl.window, wl.N)
+    need = min(wl.N, int((pc.max().item() + 63) // 64 * 64))
     m, pc, ac = lit.pool_plan(gate, wl.window, need)
     assert (pc.cpu() <= need).all()
     host = [t.cpu().pin_memory() for t in (kk, L.kv.data, L.kv.rope, L.kv.scale)]
