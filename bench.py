@@ -13,9 +13,11 @@ the eager result) and replayed. Besides the headline line the JSON carries:
                  launch / its average launch time, measured with HIP events on
                  the stream it runs on, against the 8 TB/s HBM peak;
   cpu_baseline : the CPU oracle on a bounded sample of the same queries;
-  others       : the 64K batch-1 latency and the 500K batch-4 step (distinct
-                 layers rotated so every replay streams from HBM), and the LSA
-                 cold-pool fetch at the gate workload's shapes.
+  others       : the whole attention step of a token (2 SWA + 21 CSA + 20
+                 HCA layers) at 64K and 500K, the 64K batch-1 latency, the
+                 500K batch-4 step (distinct layers rotated so every replay
+                 streams from HBM), and the LSA cold-pool fetch at the gate
+                 workload's shapes.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 from __future__ import annotations
@@ -49,55 +51,6 @@ def idx_score_bytes_per_query(N, H):
     and queries, the fp32 weights, the fp32 scores written and the hints written
     (one key-norm bound per 256 entries, one score maximum per 16 entries)."""
     return N * 128 * 2 + H * 128 * 2 + H * 4 + N * 4 + ((-(-N // 256)) + (-(-N // 16))) * 4
-
-
-class Path:
-    """Preallocated buffers of one layer of B sequences and the three C calls."""
-
-    def __init__(self, lit, L, k, window, scale, dev, allowed=None):
-        import torch
-
-        self.lit, self.L, self.allowed = lit, L, allowed
-        self.B, self.N = L.idx.k_idx.shape[0], L.idx.k_idx.shape[1]
-        self.H, self.Hq = L.idx.q_idx.shape[1], L.q.shape[1]
-        self.k, self.window, self.scale = k, window, scale
-        B, N = self.B, self.N
-        self.scores = torch.empty(B, N, dtype=torch.float32, device=dev)
-        self.hints = torch.empty(B, lit.hints_len(N), dtype=torch.float32, device=dev)
-        self.ids = torch.empty(B, k, dtype=torch.int32, device=dev)
-        self.count = torch.empty(B, dtype=torch.int32, device=dev)
-        self.out = torch.empty(B, self.Hq, 512, dtype=torch.float32, device=dev)
-        self.lse = torch.empty(B, self.Hq, dtype=torch.float32, device=dev)
-        C = lit.load()
-        self.ws_topk = torch.empty(C.lit_topk_workspace_bytes(B, N, k), dtype=torch.uint8, device=dev)
-        self.ws_attn = torch.empty(C.lit_attn_workspace_bytes(B, self.Hq, N), dtype=torch.uint8, device=dev)
-        self.idx_desc = lit.idx_in(L.idx.q_idx, L.idx.w, L.idx.k_idx)
-        self.kv_desc = lit.kv_desc(L.kv)
-        self.C = C
-
-    def score(self, stream):
-        st = self.C.lit_idx_score(ctypes.byref(self.idx_desc),
-                                  None if self.allowed is None else self.allowed.data_ptr(), self.B, self.N,
-                                  self.scores.data_ptr(), self.hints.data_ptr(), stream)
-        assert st == 0, self.lit.last_error()
-
-    def select(self, stream):
-        st = self.C.lit_topk_select(self.scores.data_ptr(), self.B, self.N, self.k, ctypes.byref(self.idx_desc),
-                                    self.hints.data_ptr(), self.ids.data_ptr(), self.count.data_ptr(), None,
-                                    self.ws_topk.data_ptr(), self.ws_topk.numel(), stream)
-        assert st == 0, self.lit.last_error()
-
-    def attend(self, stream):
-        st = self.C.lit_sparse_attn_decode(self.L.q.data_ptr(), self.lit.LIT_BF16, self.Hq, ctypes.byref(self.kv_desc),
-                                           self.B, self.ids.data_ptr(), self.count.data_ptr(), self.k, self.window,
-                                           self.scale, self.out.data_ptr(), self.lse.data_ptr(),
-                                           self.ws_attn.data_ptr(), self.ws_attn.numel(), stream)
-        assert st == 0, self.lit.last_error()
-
-    def run(self, stream):
-        self.score(stream)
-        self.select(stream)
-        self.attend(stream)
 
 
 def capture(fn):
@@ -213,6 +166,7 @@ def main():
 
     import lightning_indexer_top_idx_amd as lit
     from lightning_indexer_top_idx_amd import workloads as W
+    from lightning_indexer_top_idx_amd.step import CsaLayer
 
     lit.load()
     dev = torch.device("cuda:0")
@@ -233,7 +187,7 @@ def main():
     print(f"[bench] generating {wl.name}: {wl.layers} layers x {wl.B} sequences x N={wl.N}", file=sys.stderr,
           flush=True)
     layers = [W.layer_inputs(wl, l, dev) for l in range(wl.layers)]
-    paths = [Path(lit, L, wl.k, wl.window, scale, dev) for L in layers]
+    paths = [CsaLayer(L, wl.k, wl.window, scale, dev) for L in layers]
     torch.cuda.synchronize()
 
     def step(stream):
@@ -303,22 +257,62 @@ def main():
                                            threads, paths)
 
     if not args.no_others:
-        out["others"] = others(lit, W, dev, scale)
+        print("[bench] token step at 64K", file=sys.stderr, flush=True)
+        out["others"] = {"token_step_64k": token_step(W, dev, scale, paths, 65536)}
+        out["others"].update(others(lit, W, dev, scale))
 
     del g, gs
     print(json.dumps(out))
 
 
+def token_step(W, dev, scale, csa, T, hca_kv=None, reps=10):
+    """All 43 attention layers of one decode step ([ARCH] (A), the layer table):
+    SWA on layers 0-1 (the last 128 uncompressed rows), CSA on the even layers
+    2-42 (the `csa` layers given, reused in turn when fewer than 21), HCA on the
+    odd layers 3-41 (ceil(T/128) rows read densely; the rows of `hca_kv` =
+    (q, [rows...]) reused in turn when given). Returns the step time for the
+    CSA layers' B sequences and the tokens/s it gives."""
+    import torch
+    from lightning_indexer_top_idx_amd.step import DenseLayer, TokenSchedule, layer_kind
+
+    B, Hq = csa[0].B, csa[0].Hq
+    swa = [DenseLayer(*W.dense_layer_inputs(B, 128, Hq, l, dev), scale, dev) for l in range(2)]
+    if hca_kv is None:
+        hca = [DenseLayer(*W.dense_layer_inputs(B, -(-T // 128), Hq, l, dev), scale, dev) for l in range(3, 42, 2)]
+    else:
+        hca = [DenseLayer(hca_kv[0], hca_kv[1][i % len(hca_kv[1])], scale, dev) for i in range(20)]
+    order = []
+    for l in range(43):
+        kind = layer_kind(l)
+        order.append(swa[l] if kind == "swa" else csa[((l - 2) // 2) % len(csa)] if kind == "csa"
+                     else hca[(l - 3) // 2])
+    sched = TokenSchedule(order)
+    g = capture(sched.run)
+    g.replay()
+    sec = time_graph(g, reps) / reps
+    # the CSA layers alone, in the same order, for their share of the step
+    gc = capture(lambda s: [Ly.run(s) for l, Ly in enumerate(order) if layer_kind(l) == "csa"])
+    gc.replay()
+    csa_sec = time_graph(gc, reps) / reps
+    del g, gc, swa, hca
+    torch.cuda.empty_cache()
+    return {"sequences": B, "context_tokens": T, "layers": "2 SWA (128 rows) + 21 CSA + 20 HCA "
+                                                          f"({-(-T // 128)} rows)",
+            "token_step_us": round(sec * 1e6, 1), "tokens_per_s": round(B / sec, 1),
+            "csa_layers_us": round(csa_sec * 1e6, 1), "csa_share": round(csa_sec / sec, 3)}
+
+
 def others(lit, W, dev, scale):
     """Secondary figures: 64K batch-1 latency and the 500K batch-4 step."""
     import torch
+    from lightning_indexer_top_idx_amd.step import CsaLayer
 
     res = {}
     # 64K, batch 1: 32 independent layers rotated so the data exceeds the 256 MB cache
     wl = W.CTX64K
     n_rot = 32
     layers = [W.layer_inputs(wl, 100 + l, dev) for l in range(n_rot)]
-    paths = [Path(lit, L, wl.k, wl.window, scale, dev) for L in layers]
+    paths = [CsaLayer(L, wl.k, wl.window, scale, dev) for L in layers]
     g = capture(lambda s: [P.run(s) for P in paths])
     g.replay()
     sec = time_graph(g, 5)
@@ -333,7 +327,7 @@ def others(lit, W, dev, scale):
     # 256 MB cache.
     wl = W.CTX500K
     n_csa, n_hca = 3, 24
-    csa_paths = [Path(lit, W.layer_inputs(wl, l, dev), wl.k, wl.window, scale, dev) for l in range(n_csa)]
+    csa_paths = [CsaLayer(W.layer_inputs(wl, l, dev), wl.k, wl.window, scale, dev) for l in range(n_csa)]
     hq, hkv0 = W.hca_inputs(wl, dev)
     hkvs = [hkv0] + [type(hkv0)(hkv0.dtype, hkv0.data.clone()) for _ in range(n_hca - 1)]
     hout = torch.empty(wl.B, wl.Hq, 512, dtype=torch.float32, device=dev)
@@ -356,7 +350,12 @@ def others(lit, W, dev, scale):
                          "hbm_frac": round(per_query * wl.B / csa_s / 1e9 / HBM_PEAK_GBS, 4),
                          "hca_layer_us": round(hca_s * 1e6, 2),
                          "hca_hbm_frac": round(wl.B * wl.hca_N * 1024 / hca_s / 1e9 / HBM_PEAK_GBS, 4)}
-    del gc, gh, csa_paths, hkvs
+    del gc, gh, hout, hws
+    # the whole attention step of a token at 500K: the three CSA layers above
+    # in turn, the 24 copies of the HCA rows in turn
+    print("[bench] token step at 500K", file=sys.stderr, flush=True)
+    res["token_step_500k"] = token_step(W, dev, scale, csa_paths, 500000, hca_kv=(hq, hkvs))
+    del csa_paths, hkvs
     torch.cuda.empty_cache()
     res["gate64k_offload"] = offload(lit, W, dev, scale)
     return res
@@ -374,6 +373,7 @@ def offload(lit, W, dev, scale):
     are checked equal first)."""
     import torch
     from lightning_indexer_top_idx_amd import synth
+    from lightning_indexer_top_idx_amd.step import CsaLayer
 
     wl = W.GATE64K
     keys = [W.layer_inputs(wl, l, dev).idx.k_idx for l in W.GATE_LAYERS]
@@ -416,10 +416,10 @@ def offload(lit, W, dev, scale):
     torch.cuda.synchronize()
     copy_s = e0.elapsed_time(e1) / 1e3 / reps
     # the decode step, resident (gate as allowed) and on the compact pool
-    Pr = Path(lit, L, wl.k, wl.window, scale, dev, allowed=gate)
+    Pr = CsaLayer(L, wl.k, wl.window, scale, dev, allowed=gate)
     Lc = W.LayerInputs(synth.IndexerInputs(L.idx.q_idx, L.idx.w, bufs[0]), L.q,
                        synth.KVRows("fp8", bufs[1], bufs[2], bufs[3]))
-    Pc = Path(lit, Lc, wl.k, wl.window, scale, dev, allowed=ac)
+    Pc = CsaLayer(Lc, wl.k, wl.window, scale, dev, allowed=ac)
     s0 = torch.cuda.current_stream().cuda_stream
     Pr.run(s0)
     Pc.run(s0)

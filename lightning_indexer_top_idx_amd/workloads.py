@@ -127,3 +127,18 @@ def gate_layer(wl: Workload, layer: int, keys: torch.Tensor, device="cpu", d_mod
     g = synth.generator(device, wl.cid, 2000 + layer)
     h, wa, wb, wp = synth.make_gate_weights(keys.shape[0], H, d_model, rank, g, device)
     return synth.GateLayer(h, wa, wb, wp, keys)
+
+
+# The other attention layers of a decode step ([ARCH] (A), the layer table):
+# SWA on layers 0-1 keeps the last W uncompressed rows, HCA on the odd layers
+# 3-41 keeps ceil(T/128) rows read densely. Their inputs come from streams of
+# their own (config id 5), one per layer.
+SCHEDULE_CID = 5
+
+
+def dense_layer_inputs(B: int, rows: int, Hq: int, layer: int, device="cpu") -> Tuple[torch.Tensor, synth.KVRows]:
+    """Attention query [B,Hq,512] bf16 and bf16 rows [B,rows,512] of an SWA or HCA layer."""
+    g = synth.generator(device, SCHEDULE_CID, layer)
+    q = synth.make_q(B, Hq, "bf16", g, device)
+    kv = synth.make_kv(B, rows, "bf16", g, device)
+    return q, kv
