@@ -259,6 +259,8 @@ def main():
     if not args.no_others:
         print("[bench] token step at 64K", file=sys.stderr, flush=True)
         out["others"] = {"token_step_64k": token_step(W, dev, scale, paths, 65536)}
+        print("[bench] multi-query indexer: MTP at 64K", file=sys.stderr, flush=True)
+        out["others"]["mtp_64k_indexer"] = mtp(lit, W, dev, layers, paths, wl)
         out["others"].update(others(lit, W, dev, scale))
 
     del g, gs
@@ -300,6 +302,113 @@ def token_step(W, dev, scale, csa, T, hca_kv=None, reps=10):
                                                           f"({-(-T // 128)} rows)",
             "token_step_us": round(sec * 1e6, 1), "tokens_per_s": round(B / sec, 1),
             "csa_layers_us": round(csa_sec * 1e6, 1), "csa_share": round(csa_sec / sec, 3)}
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def mtp(lit, W, dev, layers, paths, wl):
+    """The multi-query indexer at depth-1 MTP (the current token and its draft,
+    Q = 2) on the timed workload's 21 layers: score both queries against the
+    keys in one pass, then each query's exact top-512. Next to it the same
+    layers' single-query indexer (score + select of the timed step). Query 0
+    of each sequence is the timed step's query, so its selection must equal
+    the timed step's ids (checked)."""
+    import torch
+
+    Q = W.MTP_Q
+    C = lit.load()
+    bufs = []
+    for l, (L, P) in enumerate(zip(layers, paths)):
+        q, w = W.extra_queries(L.idx, Q, l, dev)
+        d = lit.idx_in_mq(q, w, L.idx.k_idx)
+        B, N = P.B, P.N
+        sc = torch.empty(B, Q, N, dtype=torch.float32, device=dev)
+        hi = torch.empty(B, Q, lit.hints_len(N), dtype=torch.float32, device=dev)
+        ids = torch.empty(B, Q, wl.k, dtype=torch.int32, device=dev)
+        cnt = torch.empty(B, Q, dtype=torch.int32, device=dev)
+        ws = torch.empty(C.lit_topk_workspace_bytes(B * Q, N, wl.k), dtype=torch.uint8, device=dev)
+        bufs.append((q, w, d, sc, hi, ids, cnt, ws, B, N))
+
+    def score(s):
+        for (q, w, d, sc, hi, ids, cnt, ws, B, N) in bufs:
+            assert C.lit_idx_score_mq(ctypes.byref(d), Q, None, None, B, N, sc.data_ptr(), hi.data_ptr(), s) == 0, \
+                lit.last_error()
+
+    def select(s):
+        for (q, w, d, sc, hi, ids, cnt, ws, B, N) in bufs:
+            assert C.lit_topk_select_mq(sc.data_ptr(), B, Q, N, wl.k, ctypes.byref(d), hi.data_ptr(), ids.data_ptr(),
+                                        cnt.data_ptr(), None, ws.data_ptr(), ws.numel(), s) == 0, lit.last_error()
+
+    g2 = capture(lambda s: (score(s), select(s)))
+    g2.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(b[5][:, 0], P.ids) for b, P in zip(bufs, paths))
+    gs = capture(score)
+    g1 = capture(lambda s: [(P.score(s), P.select(s)) for P in paths])
+    reps = 10
+    t2 = time_graph(g2, reps) / (reps * len(paths))
+    ts = time_graph(gs, reps) / (reps * len(paths))
+    t1 = time_graph(g1, reps) / (reps * len(paths))
+    B, N = paths[0].B, paths[0].N
+    score_bytes = B * (N * 128 * 2 + Q * (wl.H * 128 * 2 + wl.H * 4) + Q * N * 4
+                       + Q * ((-(-N // 256)) + (-(-N // 16))) * 4)
+    del g2, gs, g1, bufs
+    torch.cuda.empty_cache()
+    return {"sequences": B, "queries_per_sequence": Q, "entries": N,
+            "indexer_us_per_layer_q2": round(t2 * 1e6, 2), "indexer_us_per_layer_q1": round(t1 * 1e6, 2),
+            "indexer_us_per_query_q2": round(t2 * 1e6 / (B * Q), 3),
+            "indexer_us_per_query_q1": round(t1 * 1e6 / B, 3),
+            "score_us_per_layer_q2": round(ts * 1e6, 2),
+            "score_hbm_frac_q2": round(score_bytes / ts / 1e9 / HBM_PEAK_GBS, 4),
+            "query0_equals_single_query_step": same,
+            "note": "score + exact top-512 of both queries per layer, 21 layers in one graph; the keys are read "
+                    "once for the two queries"}
+
+
+def prefill(lit, W, dev):
+    """The multi-query indexer on a prefill chunk: the last 2048 tokens of a 64K
+    prompt (one sequence, 16384 entries, 64 index heads), each token seeing the
+    entries complete before it (causal lengths). The scoring is a [2048*64 x
+    128] x [128 x 16384] product on the matrix cores; algorithmic flops count
+    the visible entries only. Then every token's exact top-512."""
+    import torch
+
+    wl = W.CTX64K
+    Q = W.PREFILL_Q
+    idx = W.mq_inputs(wl, Q, 0, dev)
+    q, w, k = idx.q_idx, idx.w, idx.k_idx
+    lengths = W.causal_lengths(1, Q, W.PREFILL_T - Q, dev)
+    C = lit.load()
+    d = lit.idx_in_mq(q, w, k)
+    N = wl.N
+    sc = torch.empty(1, Q, N, dtype=torch.float32, device=dev)
+    hi = torch.empty(1, Q, lit.hints_len(N), dtype=torch.float32, device=dev)
+    ids = torch.empty(1, Q, wl.k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, Q, dtype=torch.int32, device=dev)
+    ws = torch.empty(C.lit_topk_workspace_bytes(Q, N, wl.k), dtype=torch.uint8, device=dev)
+
+    def score(s):
+        assert C.lit_idx_score_mq(ctypes.byref(d), Q, lengths.data_ptr(), None, 1, N, sc.data_ptr(), hi.data_ptr(),
+                                  s) == 0, lit.last_error()
+
+    def select(s):
+        assert C.lit_topk_select_mq(sc.data_ptr(), 1, Q, N, wl.k, ctypes.byref(d), hi.data_ptr(), ids.data_ptr(),
+                                    cnt.data_ptr(), None, ws.data_ptr(), ws.numel(), s) == 0, lit.last_error()
+
+    gs, gt = capture(score), capture(select)
+    reps = 10
+    ts = time_graph(gs, reps) / reps
+    tt = time_graph(gt, reps) / reps
+    flops = 2.0 * wl.H * 128 * float(lengths.sum().item())
+    tflops = flops / ts / 1e12
+    ok = bool((cnt == wl.k).all().item())
+    del gs, gt
+    torch.cuda.empty_cache()
+    return {"queries": Q, "entries": N, "score_us": round(ts * 1e6, 1), "score_TFLOPs": round(tflops, 1),
+            "mfma_bf16_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "topk_us": round(tt * 1e6, 1),
+            "topk_us_per_query": round(tt * 1e6 / Q, 3), "tokens_per_s_indexer": round(Q / (ts + tt), 1),
+            "all_counts_k": ok}
 
 
 def others(lit, W, dev, scale):
@@ -358,6 +467,8 @@ def others(lit, W, dev, scale):
     del csa_paths, hkvs
     torch.cuda.empty_cache()
     res["gate64k_offload"] = offload(lit, W, dev, scale)
+    print("[bench] multi-query indexer: prefill chunk", file=sys.stderr, flush=True)
+    res["prefill_chunk_indexer"] = prefill(lit, W, dev)
     return res
 
 

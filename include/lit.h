@@ -13,6 +13,8 @@
  *   lit_lsa_gate         sigmoid chunk gate of FlashMemory/LSA (candidate set)
  *   lit_pool_plan / lit_pool_gather / lit_pool_remap_ids
  *                        the LSA cold-pool fetch: gated entries into a compact pool
+ *   lit_idx_score_mq / lit_topk_select_mq
+ *                        the indexer for several queries per sequence (MTP, prefill)
  *
  * Pages cited (title, then the part of the page):
  *   [ARCH]  ai-muninn.com, "284B 塞得進 128GB、長 context 還跑得動:DeepSeek-V4-Flash
@@ -77,6 +79,7 @@ extern "C" {
 #define LIT_MAX_IDX_HEADS 64
 #define LIT_MAX_Q_HEADS 64
 #define LIT_MAX_WINDOW 8192
+#define LIT_MAX_QUERIES 65536 /* queries per sequence of the multi-query calls */
 
 typedef enum {
   LIT_OK = 0,
@@ -331,6 +334,40 @@ lit_status lit_pool_gather(const void* src, int32_t src_rows, int64_t row_bytes,
  * ids_c, ids : [B][k] int32;  count : [B] int32;  map : [B][C] int32. */
 lit_status lit_pool_remap_ids(const int32_t* ids_c, const int32_t* count, int32_t B, int32_t k,
                               const int32_t* map, int32_t C, int32_t* ids, void* stream);
+
+/* ---- NEXT: the multi-query indexer ----------------------------------------------
+ * Several queries of one sequence scored against that sequence's compressed
+ * entries in one call: the draft token of depth-1 MTP speculative decoding
+ * ([ARCH], the series list at its end: Part 5) is verified together with the
+ * current token (Q = 2), and a prefill chunk ([ARCH] (A), the resident prefill
+ * cache) scores each of its tokens (Q = the chunk length). The keys are read
+ * once per group of queries, so the scoring turns from a key stream into a
+ * matrix product on the matrix cores.
+ *
+ * lit_idx_score_mq: for sequence b, query j (row r = b*Q + j) and entry n:
+ *     scores[r][n] = sum_h w[r][h] * max(0, sum_d q[r][h][d] * k[b][n][d])
+ * for n < lengths[r] (and allowed[b][n] != 0); -inf otherwise. A query sees
+ * the entries that existed when its token was decoded: lengths[r] (NULL: all N
+ * for every query); values above N act as N, values below 1 hide every entry.
+ * in      : q [B][Q][H][128], w [B][Q][H], k [B][N][128] (the lit_idx_in layout
+ *           with Q queries per sequence), LIT_BF16 or LIT_F32.
+ * lengths : [B][Q] int32 or NULL;  allowed : [B][N] u8 or NULL (shared by the
+ *           Q queries of a sequence).
+ * scores  : [B][Q][N] fp32 output;  hints : [B][Q][lit_idx_hints_len(N)] fp32
+ *           output or NULL, row r as lit_idx_score writes for one sequence.
+ * Q == 1 with lengths == NULL gives lit_idx_score's results bit for bit. */
+lit_status lit_idx_score_mq(const lit_idx_in* in, int32_t Q, const int32_t* lengths,
+                            const uint8_t* allowed, int32_t B, int32_t N, float* scores,
+                            float* hints, void* stream);
+
+/* lit_topk_select_mq: lit_topk_select on the B*Q rows of lit_idx_score_mq's
+ * scores (each row its own top k, ids [B*Q][k], count [B*Q], mask [B*Q][N]);
+ * in exact mode row r is rescored with query r and the keys of sequence r / Q.
+ * Workspace: lit_topk_workspace_bytes(B*Q, N, k) bytes. */
+lit_status lit_topk_select_mq(const float* scores, int32_t B, int32_t Q, int32_t N, int32_t k,
+                              const lit_idx_in* exact, const float* hints, int32_t* ids,
+                              int32_t* count, uint8_t* mask, void* ws, size_t ws_bytes,
+                              void* stream);
 
 #ifdef __cplusplus
 }

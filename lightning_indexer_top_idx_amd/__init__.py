@@ -35,6 +35,7 @@ EXPORTS = [
     "lit_attn_workspace_bytes", "lit_sparse_attn_decode", "lit_golden_workspace_bytes", "lit_golden_topk",
     "lit_topp_workspace_bytes", "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall",
     "lit_gate_workspace_bytes", "lit_lsa_gate", "lit_pool_plan", "lit_pool_gather", "lit_pool_remap_ids",
+    "lit_idx_score_mq", "lit_topk_select_mq",
 ]
 
 
@@ -98,9 +99,11 @@ def load(path: str = LIB_PATH):
     L.lit_pool_plan.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
     L.lit_pool_gather.argtypes = [vp, i32, ctypes.c_int64, i32, vp, i32, vp, vp]
     L.lit_pool_remap_ids.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
+    L.lit_idx_score_mq.argtypes = [ctypes.POINTER(IdxIn), i32, vp, vp, i32, i32, vp, vp, vp]
+    L.lit_topk_select_mq.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(IdxIn), vp, vp, vp, vp, vp, sz, vp]
     for name in ("lit_idx_score", "lit_topk_select", "lit_sparse_attn_decode", "lit_golden_topk",
                  "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall", "lit_lsa_gate", "lit_pool_plan",
-                 "lit_pool_gather", "lit_pool_remap_ids"):
+                 "lit_pool_gather", "lit_pool_remap_ids", "lit_idx_score_mq", "lit_topk_select_mq"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -212,6 +215,50 @@ def topk_select(scores, k: int, exact=None, hints=None, want_mask: bool = True, 
     _check(L.lit_topk_select(scores.data_ptr(), B, N, k, ctypes.byref(desc) if desc is not None else None,
                              _ptr(hints), ids.data_ptr(), count.data_ptr(), _ptr(mask), ws.data_ptr(), ws.numel(),
                              _stream(scores)))
+    return ids, count, mask
+
+
+def idx_in_mq(q_idx, w, k_idx) -> IdxIn:
+    """Descriptor of Q queries per sequence: q_idx [B,Q,H,128], w [B,Q,H], k_idx [B,N,128]."""
+    _need_cuda(q_idx, w, k_idx)
+    if q_idx.dim() != 4 or w.shape != q_idx.shape[:3] or k_idx.shape[0] != q_idx.shape[0]:
+        raise ValueError("q_idx [B,Q,H,128], w [B,Q,H] and k_idx [B,N,128] disagree")
+    return IdxIn(q_idx.data_ptr(), w.data_ptr(), k_idx.data_ptr(), _dtype_code(q_idx), q_idx.shape[2])
+
+
+def idx_score_mq(q_idx, w, k_idx, lengths=None, allowed=None, want_hints: bool = True, out=None):
+    """Multi-query indexer scores: [B,Q,N] fp32 and hints [B,Q,hints_len(N)].
+    lengths [B,Q] int32: entries visible to each query (None: all)."""
+    torch = _torch()
+    B, Q, N = q_idx.shape[0], q_idx.shape[1], k_idx.shape[1]
+    _need_cuda(allowed, lengths)
+    if lengths is not None and (lengths.dtype != torch.int32 or tuple(lengths.shape) != (B, Q)):
+        raise ValueError("lengths must be int32 [B,Q]")
+    scores = out if out is not None else torch.empty(B, Q, N, dtype=torch.float32, device=k_idx.device)
+    hints = torch.empty(B, Q, hints_len(N), dtype=torch.float32, device=k_idx.device) if want_hints else None
+    desc = idx_in_mq(q_idx, w, k_idx)
+    _check(load().lit_idx_score_mq(ctypes.byref(desc), Q, _ptr(lengths), _ptr(allowed), B, N, scores.data_ptr(),
+                                   _ptr(hints), _stream(k_idx)))
+    return scores, hints
+
+
+def topk_select_mq(scores, k: int, exact=None, hints=None, want_mask: bool = True, ws=None):
+    """Per-row top-k of idx_score_mq's scores [B,Q,N]: ids [B,Q,k], count [B,Q],
+    mask [B,Q,N]. exact: (q_idx [B,Q,H,128], w, k_idx) -> fp64-exact selection."""
+    torch = _torch()
+    _need_cuda(scores, hints)
+    B, Q, N = scores.shape
+    dev = scores.device
+    ids = torch.empty(B, Q, k, dtype=torch.int32, device=dev)
+    count = torch.empty(B, Q, dtype=torch.int32, device=dev)
+    mask = torch.empty(B, Q, N, dtype=torch.uint8, device=dev) if want_mask else None
+    L = load()
+    if ws is None:
+        ws = workspace(L.lit_topk_workspace_bytes(B * Q, N, k), dev)
+    desc = idx_in_mq(*exact) if exact is not None else None
+    _check(L.lit_topk_select_mq(scores.data_ptr(), B, Q, N, k, ctypes.byref(desc) if desc is not None else None,
+                                _ptr(hints), ids.data_ptr(), count.data_ptr(), _ptr(mask), ws.data_ptr(), ws.numel(),
+                                _stream(scores)))
     return ids, count, mask
 
 

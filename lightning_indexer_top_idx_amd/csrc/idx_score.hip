@@ -130,12 +130,13 @@ __device__ __forceinline__ void keys_to_operands(u32x4* slab, const u32x4 (&kr)[
 }
 
 // Scores of the lane's entry (lane = 16 g + c holds entry base + lane): the
-// allowed mask applied, the score stored, and the group maximum returned in
-// the group's last lane (c = 15; a running maximum along the 16-lane row on
-// DPP shifts; entries at or past N count as -inf).
-__device__ __forceinline__ float store_score(float v, int e, int N, const uint8_t* ab, float* sb) {
+// allowed mask and the visible length nv applied (entries at or past nv are
+// not visible to the query and score -inf), the score stored, and the group
+// maximum returned in the group's last lane (c = 15; a running maximum along
+// the 16-lane row on DPP shifts; entries at or past N count as -inf).
+__device__ __forceinline__ float store_score(float v, int e, int N, int nv, const uint8_t* ab, float* sb) {
   if (e < N) {
-    if (ab && ab[e] == 0) v = -INFINITY;
+    if (e >= nv || (ab && ab[e] == 0)) v = -INFINITY;
     sb[e] = v;
   } else {
     v = -INFINITY;
@@ -153,31 +154,42 @@ __device__ __forceinline__ float store_score(float v, int e, int N, const uint8_
 // NB - 1 half-steps (NB - 1 times 8 KB per wave) are in flight while one is
 // multiplied (three buffers measured fastest: a fourth adds registers, not
 // bandwidth).
-template <int MT, int S, int NB, bool CONTIG>
+//
+// A workgroup scores QW queries of one sequence (a "unit"): every key operand
+// it loads is multiplied with each query's heads in turn, so a sequence with
+// Q queries (draft tokens, a prefill chunk) streams its keys once per QW
+// queries. Row r = b * Q + query of scores and hints belongs to query
+// r - b * Q of sequence b; lengths[r] (or N) entries are visible to it.
+template <int MT, int S, int NB, bool CONTIG, int QW>
 __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* __restrict__ q,
                                                              const float* __restrict__ w,
                                                              const uint16_t* __restrict__ k,
-                                                             const uint8_t* __restrict__ allowed, int H,
-                                                             int N, int nchunks, float* __restrict__ scores,
+                                                             const uint8_t* __restrict__ allowed,
+                                                             const int32_t* __restrict__ lengths, int H, int N,
+                                                             int Q, int nqg, int nchunks, float* __restrict__ scores,
                                                              float* __restrict__ hints, int hints_len, int seq_xcd) {
   constexpr int NH = 2 * S;  // half-steps per wave
-  __shared__ u32x4 qlds[MT * 4 * 64];
-  __shared__ float wlds[64];
+  static_assert(QW >= 1 && QW <= 4, "one wave writes each query's bound sums");
+  __shared__ u32x4 qlds[QW][MT * 4 * 64];
+  __shared__ float wlds[QW][64];
   __shared__ float nmax[4][S];
-  __shared__ double qterm[2][MT * 16];  // |w_h| ||q_h||, |w_h| (first workgroup of a sequence)
+  __shared__ double qterm[QW][2][MT * 16];  // |w_h| ||q_h||, |w_h| (first workgroup of a unit)
   __shared__ u32x4 kslab[CONTIG ? 4 : 1][CONTIG ? 32 * KT_LD : 1];
-  // seq_xcd: a 1-D grid in which sequence b's workgroups all have ids equal to
-  // b modulo 8, i.e. run on XCD b % 8, where the selection of sequence b (one
-  // workgroup, id b) then finds its scores in that XCD's L2
-  int b, bx;
+  // seq_xcd: a 1-D grid in which unit u's workgroups all have ids equal to
+  // u modulo 8, i.e. run on XCD u % 8, where the selection of a single-query
+  // sequence u (one workgroup, id u) then finds its scores in that XCD's L2
+  int u, bx;
   if (seq_xcd) {
     const int nx = (nchunks + S - 1) / S, slot = (int)blockIdx.x >> 3;
     bx = slot % nx;
-    b = (slot / nx) * 8 + ((int)blockIdx.x & 7);
+    u = (slot / nx) * 8 + ((int)blockIdx.x & 7);
   } else {
-    b = blockIdx.y;
+    u = blockIdx.y;
     bx = blockIdx.x;
   }
+  const int b = u / nqg, q0 = (u - b * nqg) * QW;
+  const int nq = min(QW, Q - q0);  // queries of this unit (the last unit of a sequence may have fewer)
+  const int r0 = b * Q + q0;       // its first row
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
@@ -198,14 +210,15 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
     if (h < NH) load_half(h, kr[h]);
 
   // Stage q as MFMA A operands: operand (mt, j) lane (hh + 16*gg) holds head
-  // 16*mt + hh, dims 8*gg + 32*j .. +7.
-  const uint16_t* qb = q + (size_t)b * H * LIT_IDX_DIM;
-  for (int idx = tid; idx < MT * 16 * 16; idx += 256) {
-    const int h = idx >> 4, d8 = idx & 15;  // the 16 lanes of a row hold one head
+  // 16*mt + hh, dims 8*gg + 32*j .. +7. Queries past nq stage zeros.
+  for (int idx = tid; idx < QW * MT * 16 * 16; idx += 256) {
+    const int qi = idx / (MT * 256), hd = idx - qi * (MT * 256);
+    const int h = hd >> 4, d8 = hd & 15;  // the 16 lanes of a row hold one head
+    const bool live = h < H && qi < nq;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (h < H) v = *(const u32x4*)(qb + h * LIT_IDX_DIM + d8 * 8);
+    if (live) v = *(const u32x4*)(q + ((size_t)(r0 + qi) * H + h) * LIT_IDX_DIM + d8 * 8);
     const int mt = h >> 4, hh = h & 15, gg = d8 & 3, j = d8 >> 2;
-    qlds[(mt * 4 + j) * 64 + hh + 16 * gg] = v;
+    qlds[qi][(mt * 4 + j) * 64 + hh + 16 * gg] = v;
     if (bounds) {
       double ss = 0.0;
 #pragma unroll
@@ -219,24 +232,32 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
       ss += dpp_f64<0x114>(ss);
       ss += dpp_f64<0x118>(ss);
       if (d8 == 15) {
-        const double a = h < H ? fabs((double)w[(size_t)b * H + h]) : 0.0;
-        qterm[0][h] = a * sqrt(ss);
-        qterm[1][h] = a;
+        const double a = live ? fabs((double)w[(size_t)(r0 + qi) * H + h]) : 0.0;
+        qterm[qi][0][h] = a * sqrt(ss);
+        qterm[qi][1][h] = a;
       }
     }
   }
-  if (tid < 64) wlds[tid] = tid < H ? w[(size_t)b * H + tid] : 0.f;
+  for (int i = tid; i < QW * 64; i += 256) {
+    const int qi = i >> 6, h = i & 63;
+    wlds[qi][h] = h < H && qi < nq ? w[(size_t)(r0 + qi) * H + h] : 0.f;
+  }
   lds_barrier();
-  if (bounds && wid == 0)
-    write_q_bounds(qterm[0], qterm[1], MT * 16, hints + (size_t)b * hints_len + nchunks + (N + LIT_HINT_GROUP - 1) / LIT_HINT_GROUP);
-  float wr[MT][4];
-  load_lane_weights<MT>(wlds, wr);
+  const int hq_off = nchunks + (N + LIT_HINT_GROUP - 1) / LIT_HINT_GROUP;  // the query-side sums in a hints row
+  if (bounds && wid < nq)  // one wave per query (QW <= 4)
+    write_q_bounds(qterm[wid][0], qterm[wid][1], MT * 16, hints + (size_t)(r0 + wid) * hints_len + hq_off);
+  float wr[QW][MT][4];
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) load_lane_weights<MT>(wlds[qi], wr[qi]);
+  int nv[QW];  // entries visible to each query
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) nv[qi] = lengths && qi < nq ? lengths[r0 + qi] : N;
 
   const uint8_t* ab = allowed ? allowed + (size_t)b * N : nullptr;
-  float* sb = scores + (size_t)b * N;
-  float* gm = hints ? hints + (size_t)b * hints_len + nchunks : nullptr;
 
-  float my_score = 0.f, my_n2 = 0.f;
+  float my_score[QW], my_n2 = 0.f;
+#pragma unroll
+  for (int qi = 0; qi < QW; qi++) my_score[qi] = 0.f;
 #pragma unroll
   for (int h = 0; h < NH; h++) {
     if (h + NB - 1 < NH) load_half(h + NB - 1, kr[(h + NB - 1) % NB]);
@@ -245,70 +266,86 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
     u32x4 kt[2][4];
     if (CONTIG) keys_to_operands(kslab[wid], reinterpret_cast<const u32x4(&)[8]>(kr[h % NB]), lane, g, c, kt);
     const u32x4 (&kc)[2][4] = CONTIG ? kt : kr[h % NB];
-    f32x4 acc[2][MT];
+    f32x4 gram[2];
+#pragma unroll
+    for (int qi = 0; qi < QW; qi++) {
+      f32x4 acc[2][MT];
+#pragma unroll
+      for (int G = 0; G < 2; G++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) acc[G][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, qlds[qi][(mt * 4 + j) * 64 + lane]);
+#pragma unroll
+          for (int G = 0; G < 2; G++)
+            acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kc[G][j]),
+                                                                 acc[G][mt], 0, 0, 0);
+        }
+      if (qi == 0) {
+        // key norms: the 16 x 16 Gram matrix of each column group on the matrix
+        // cores (A = B = the group's key registers). Its largest entry is its
+        // largest diagonal entry (Cauchy-Schwarz), the largest squared norm.
+#pragma unroll
+        for (int G = 0; G < 2; G++) {
+          gram[G] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            gram[G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[G][j]),
+                                                              __builtin_bit_cast(bf16x8, kc[G][j]), gram[G], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int G = 0; G < 2; G++) {
+        const float p = weighted_relu<MT>(acc[G], wr[qi]);
+        if (2 * (h & 1) + G == g) my_score[qi] = p;  // the column group that holds this lane's entry
+      }
+    }
 #pragma unroll
     for (int G = 0; G < 2; G++)
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) acc[G][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, qlds[(mt * 4 + j) * 64 + lane]);
-#pragma unroll
-        for (int G = 0; G < 2; G++)
-          acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kc[G][j]),
-                                                               acc[G][mt], 0, 0, 0);
-      }
-    // key norms: the 16 x 16 Gram matrix of each column group on the matrix
-    // cores (A = B = the group's key registers). Its largest entry is its
-    // largest diagonal entry (Cauchy-Schwarz), the largest squared norm.
-    f32x4 gram[2];
-#pragma unroll
-    for (int G = 0; G < 2; G++) {
-      gram[G] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        gram[G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[G][j]),
-                                                          __builtin_bit_cast(bf16x8, kc[G][j]), gram[G], 0, 0, 0);
-    }
-#pragma unroll
-    for (int G = 0; G < 2; G++) {
-      const float p = weighted_relu<MT>(acc[G], wr);
-      if (2 * (h & 1) + G == g) my_score = p;  // the column group that holds this lane's entry
-#pragma unroll
       for (int i = 0; i < 4; i++) my_n2 = fmaxf(my_n2, gram[G][i]);
-    }
     if (h & 1) {
       // chunk h/2 done: lane = 16*g + c holds entry base + lane
       const int s = h >> 1;
       const int base = wg_base + s * CHUNK + wid * 64;
       const int e = base + lane;
-      const float gmax = store_score(my_score, e, N, ab, sb);
-      if (gm && c == 15 && base + 16 * g < N) gm[(base + 16 * g) / 16] = gmax;
+#pragma unroll
+      for (int qi = 0; qi < QW; qi++) {
+        if (qi < nq) {
+          const size_t row = (size_t)(r0 + qi);
+          const float gmax = store_score(my_score[qi], e, N, nv[qi], ab, scores + row * N);
+          if (hints && c == 15 && base + 16 * g < N) hints[row * hints_len + nchunks + (base + 16 * g) / 16] = gmax;
+        }
+      }
       const float m = wave_max(my_n2);
       if (lane == 0) nmax[wid][s] = m;
       my_n2 = 0.f;
     }
   }
   __syncthreads();
-  if (hints && tid < S) {
-    const int chunk = bx * S + tid;
-    if (chunk < nchunks) {
-      const float m = fmaxf(fmaxf(nmax[0][tid], nmax[1][tid]), fmaxf(nmax[2][tid], nmax[3][tid]));
-      hints[(size_t)b * hints_len + chunk] = norm_bound(m);
+  if (hints && tid < S * QW) {
+    const int s = tid % S, qi = tid / S;
+    const int chunk = bx * S + s;
+    if (chunk < nchunks && qi < nq) {
+      const float m = fmaxf(fmaxf(nmax[0][s], nmax[1][s]), fmaxf(nmax[2][s], nmax[3][s]));
+      hints[(size_t)(r0 + qi) * hints_len + chunk] = norm_bound(m);
     }
   }
 }
 
 // FP32 inputs: v_mfma_f32_16x16x4_f32, lane l holds A[l%16][l/16] and
-// B[l/16][l%16]; K-step j pairs lane group g with dim 32*g + j.
+// B[l/16][l%16]; K-step j pairs lane group g with dim 32*g + j. One query (row
+// b of scores; its keys are those of sequence b / Q) per workgroup row.
 template <int MT>
 __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restrict__ q,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ k,
-                                                            const uint8_t* __restrict__ allowed, int H,
-                                                            int N, int nchunks, float* __restrict__ scores,
+                                                            const uint8_t* __restrict__ allowed,
+                                                            const int32_t* __restrict__ lengths, int H,
+                                                            int N, int Q, int nchunks, float* __restrict__ scores,
                                                             float* __restrict__ hints, int hints_len) {
   __shared__ float qlds[MT * 32 * 64];
   __shared__ float wlds[64];
@@ -342,9 +379,11 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
   float wr[MT][4];
   load_lane_weights<MT>(wlds, wr);
 
-  const float* kb = k + (size_t)b * N * LIT_IDX_DIM;
-  const uint8_t* ab = allowed ? allowed + (size_t)b * N : nullptr;
+  const int bk = b / Q;  // the sequence whose keys this query reads
+  const float* kb = k + (size_t)bk * N * LIT_IDX_DIM;
+  const uint8_t* ab = allowed ? allowed + (size_t)bk * N : nullptr;
   float* sb = scores + (size_t)b * N;
+  const int nv = lengths ? lengths[b] : N;
   const int base = blockIdx.x * CHUNK + wid * 64;
   float my_score = 0.f, my_n2 = 0.f;
 #pragma unroll 1
@@ -378,7 +417,7 @@ __global__ __launch_bounds__(256) void idx_score_f32_kernel(const float* __restr
     }
   }
   const int e = base + lane;
-  const float gmax = store_score(my_score, e, N, ab, sb);
+  const float gmax = store_score(my_score, e, N, nv, ab, sb);
   if (hints && c == 15 && base + 16 * g < N) hints[(size_t)b * hints_len + nchunks + (base + 16 * g) / 16] = gmax;
   const float m = wave_max(my_n2);
   if (lane == 0) nmax[wid] = m;
@@ -450,32 +489,85 @@ lit_status check_idx_inputs(const lit_idx_in* in, int32_t B, int32_t N, const ch
 
 using namespace lit;
 
-template <int MT>
-static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed, int N,
-                        int nchunks, float* scores, float* hints, int hl) {
+template <int MT, int QW>
+static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed,
+                        const int32_t* lengths, int N, int Q, int nqg, int nchunks, float* scores, float* hints,
+                        int hl) {
   const uint16_t* q = (const uint16_t*)in->q;
   const uint16_t* k = (const uint16_t*)in->k;
-  // batches that fill the 8 XCDs evenly keep each sequence on one XCD
+  // unit counts that fill the 8 XCDs evenly keep each unit on one XCD
   const int seq_xcd = grid.y % 8 == 0;
   const dim3 g = seq_xcd ? dim3(grid.x * grid.y) : grid;
   if (S == 4)
-    idx_score_bf16_kernel<MT, 4, KEY_RING, KEY_CONTIG><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
-  else if (S == 2)
-    idx_score_bf16_kernel<MT, 2, KEY_RING, KEY_CONTIG><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 4, KEY_RING, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
+  else if (S == 2 && QW == 1)
+    idx_score_bf16_kernel<MT, 2, KEY_RING, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
   else
-    idx_score_bf16_kernel<MT, 1, KEY_RING, KEY_CONTIG><<<g, 256, 0, st>>>(q, in->w, k, allowed, in->H, N, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 1, KEY_RING, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
 }
 
 template <int MT>
-static void launch_f32(dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed, int N,
-                       int nchunks, float* scores, float* hints, int hl) {
-  idx_score_f32_kernel<MT><<<grid, 256, 0, st>>>((const float*)in->q, in->w, (const float*)in->k, allowed, in->H,
-                                                 N, nchunks, scores, hints, hl);
+static void launch_f32(dim3 grid, hipStream_t st, const lit_idx_in* in, const uint8_t* allowed,
+                       const int32_t* lengths, int N, int Q, int nchunks, float* scores, float* hints, int hl) {
+  idx_score_f32_kernel<MT><<<grid, 256, 0, st>>>((const float*)in->q, in->w, (const float*)in->k, allowed, lengths,
+                                                 in->H, N, Q, nchunks, scores, hints, hl);
 }
 
 extern "C" int32_t lit_idx_hints_len(int32_t N) {
   if (N < 1) return 0;
   return (int32_t)(cdiv(N, LIT_KNORM_CHUNK) + cdiv(N, LIT_HINT_GROUP) + LIT_HINT_QBOUND);
+}
+
+// Q queries per sequence; Q == 1 with lengths == NULL is lit_idx_score.
+static lit_status idx_score_rows(const lit_idx_in* in, int32_t Q, const int32_t* lengths, const uint8_t* allowed,
+                                 int32_t B, int32_t N, float* scores, float* hints, void* stream, const char* who) {
+  const int nchunks = (int)cdiv(N, CHUNK);
+  const int hl = lit_idx_hints_len(N);
+  const int MT = (in->H + 15) / 16;
+  hipStream_t hs = (hipStream_t)stream;
+  if (in->dtype == LIT_BF16) {
+    // Queries per workgroup: one for single queries; two for a pair of draft
+    // tokens; four for many queries, where the key operands are reused the most.
+    const int QW = Q == 1 ? 1 : (Q == 2 ? 2 : 4);
+    const int nqg = (Q + QW - 1) / QW;
+    const int64_t units = (int64_t)B * nqg;
+    if (units > 65535 * 8) return fail(LIT_ERR_SHAPE, "%s: B x ceil(Q/%d) = %lld workgroup rows, above 524280", who, QW, (long long)units);
+    // More chunks per workgroup when there is plenty of work: amortises the q
+    // staging and lets every workgroup keep its next chunk's keys in flight;
+    // about 512 workgroups (two per CU) keep all of them resident at once.
+    const int64_t total = units * nchunks;
+    const int S = total >= 2048 ? 4 : (total >= 1024 && QW == 1 ? 2 : 1);
+    dim3 grid((unsigned)cdiv(nchunks, S), (unsigned)units);
+    if (grid.y > 65535 && grid.y % 8 != 0)
+      return fail(LIT_ERR_SHAPE, "%s: %u workgroup rows (above 65535 they must be a multiple of 8)", who, grid.y);
+#define LIT_MT_CASES(QWV)                                                                                   \
+  switch (MT) {                                                                                             \
+    case 1: launch_bf16<1, QWV>(S, grid, hs, in, allowed, lengths, N, Q, nqg, nchunks, scores, hints, hl); break; \
+    case 2: launch_bf16<2, QWV>(S, grid, hs, in, allowed, lengths, N, Q, nqg, nchunks, scores, hints, hl); break; \
+    case 3: launch_bf16<3, QWV>(S, grid, hs, in, allowed, lengths, N, Q, nqg, nchunks, scores, hints, hl); break; \
+    default: launch_bf16<4, QWV>(S, grid, hs, in, allowed, lengths, N, Q, nqg, nchunks, scores, hints, hl); break; \
+  }
+    if (QW == 1) {
+      LIT_MT_CASES(1)
+    } else if (QW == 2) {
+      LIT_MT_CASES(2)
+    } else {
+      LIT_MT_CASES(4)
+    }
+#undef LIT_MT_CASES
+  } else {
+    const int64_t rows = (int64_t)B * Q;
+    if (rows > 65535) return fail(LIT_ERR_SHAPE, "%s: B x Q = %lld fp32 query rows, above 65535", who, (long long)rows);
+    dim3 grid((unsigned)nchunks, (unsigned)rows);
+    switch (MT) {
+      case 1: launch_f32<1>(grid, hs, in, allowed, lengths, N, Q, nchunks, scores, hints, hl); break;
+      case 2: launch_f32<2>(grid, hs, in, allowed, lengths, N, Q, nchunks, scores, hints, hl); break;
+      case 3: launch_f32<3>(grid, hs, in, allowed, lengths, N, Q, nchunks, scores, hints, hl); break;
+      default: launch_f32<4>(grid, hs, in, allowed, lengths, N, Q, nchunks, scores, hints, hl); break;
+    }
+  }
+  LIT_CHECK_LAUNCH(who);
+  return LIT_OK;
 }
 
 extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,
@@ -486,34 +578,22 @@ extern "C" lit_status lit_idx_score(const lit_idx_in* in, const uint8_t* allowed
   if (!scores) return fail(LIT_ERR_NULL, "lit_idx_score: scores is NULL");
   if (!aligned(scores, 4) || (hints && !aligned(hints, 4)))
     return fail(LIT_ERR_ALIGN, "lit_idx_score: scores/hints must be 4-byte aligned");
-  const int nchunks = (int)cdiv(N, CHUNK);
-  const int hl = lit_idx_hints_len(N);
-  const int MT = (in->H + 15) / 16;
-  hipStream_t hs = (hipStream_t)stream;
-  if (in->dtype == LIT_BF16) {
-    // More chunks per workgroup when there is plenty of work: amortises the q
-    // staging and lets every workgroup keep its next chunk's keys in flight;
-    // about 512 workgroups (two per CU) keep all of them resident at once.
-    const int64_t total = (int64_t)B * nchunks;
-    const int S = total >= 2048 ? 4 : (total >= 1024 ? 2 : 1);
-    dim3 grid((unsigned)cdiv(nchunks, S), (unsigned)B);
-    switch (MT) {
-      case 1: launch_bf16<1>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-      case 2: launch_bf16<2>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-      case 3: launch_bf16<3>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-      default: launch_bf16<4>(S, grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-    }
-  } else {
-    dim3 grid((unsigned)nchunks, (unsigned)B);
-    switch (MT) {
-      case 1: launch_f32<1>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-      case 2: launch_f32<2>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-      case 3: launch_f32<3>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-      default: launch_f32<4>(grid, hs, in, allowed, N, nchunks, scores, hints, hl); break;
-    }
-  }
-  LIT_CHECK_LAUNCH("lit_idx_score");
-  return LIT_OK;
+  return idx_score_rows(in, 1, nullptr, allowed, B, N, scores, hints, stream, "lit_idx_score");
+}
+
+extern "C" lit_status lit_idx_score_mq(const lit_idx_in* in, int32_t Q, const int32_t* lengths,
+                                       const uint8_t* allowed, int32_t B, int32_t N, float* scores, float* hints,
+                                       void* stream) {
+  clear_error();
+  const char* who = "lit_idx_score_mq";
+  lit_status st = check_idx_in(in, B, N, who);
+  if (st != LIT_OK) return st;
+  if (Q < 1 || Q > LIT_MAX_QUERIES) return fail(LIT_ERR_SHAPE, "%s: Q=%d outside 1..%d", who, Q, LIT_MAX_QUERIES);
+  if ((int64_t)B * Q * N > ((int64_t)1 << 40)) return fail(LIT_ERR_SHAPE, "%s: B x Q x N above 2^40", who);
+  if (!scores) return fail(LIT_ERR_NULL, "%s: scores is NULL", who);
+  if (!aligned(scores, 4) || (hints && !aligned(hints, 4)) || (lengths && !aligned(lengths, 4)))
+    return fail(LIT_ERR_ALIGN, "%s: scores, hints and lengths must be 4-byte aligned", who);
+  return idx_score_rows(in, Q, lengths, allowed, B, N, scores, hints, stream, who);
 }
 
 extern "C" lit_status lit_idx_score_exact(const lit_idx_in* in, const uint8_t* allowed, int32_t B, int32_t N,

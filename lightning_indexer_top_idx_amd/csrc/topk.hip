@@ -73,6 +73,7 @@ struct TopkParams {
   const void* q;
   const float* w;
   const void* kidx;
+  int kq;  // rows per key batch: row b reads the keys of sequence b / kq
   int dtype, H;
   const float* hints;
   int hints_len, nchunks;
@@ -197,7 +198,7 @@ __device__ void stage_qT(const TopkParams& P, int b, float* qT) {
 __device__ __forceinline__ double rescore(const TopkParams& P, int b, int n, const float* qT, float* krow,
                                           float w_h) {
   const int lane = threadIdx.x & 63;
-  const size_t row = ((size_t)b * P.N + n) * LIT_IDX_DIM;
+  const size_t row = ((size_t)(b / P.kq) * P.N + n) * LIT_IDX_DIM;
   for (int d = lane; d < LIT_IDX_DIM; d += 64) krow[d] = load_idx(P.kidx, P.dtype, row + d);
   wave_sync();
   const double s = exact_score_wave(qT, krow, w_h, P.H);
@@ -266,7 +267,7 @@ __device__ __forceinline__ void band_scores_bcast(const TopkParams& P, int b, co
   const float* qr = qP + lane * QP_STRIDE;
   // the sequence's keys (a wave-uniform base) and 32-bit element offsets in it
   // (N * 128 < 2^32 on the paths that call this)
-  const size_t kbase = (size_t)b * P.N * LIT_IDX_DIM;
+  const size_t kbase = (size_t)(b / P.kq) * P.N * LIT_IDX_DIM;
   uint32_t roff[BW];
 #pragma unroll
   for (int j = 0; j < BW; j++) {
@@ -1015,7 +1016,7 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   uint32_t touch[4] = {0u, 0u, 0u, 0u};
   if (P.exact && bm) {
     constexpr int RW = LIT_IDX_DIM * (BF16 ? 2 : 4) / 4;  // dwords per key row
-    const uint32_t* kb = reinterpret_cast<const uint32_t*>(P.kidx) + (size_t)b * N * RW;
+    const uint32_t* kb = reinterpret_cast<const uint32_t*>(P.kidx) + (size_t)(b / P.kq) * N * RW;
     const uint32_t bm2 = bm & (bm - 1u);
     const int ea = e0 + __ffs(bm) - 1, eb = bm2 ? e0 + __ffs(bm2) - 1 : ea;
     touch[0] = kb[(size_t)ea * RW];
@@ -1358,24 +1359,25 @@ extern "C" size_t lit_topk_workspace_bytes(int32_t B, int32_t N, int32_t k) {
   return round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256) + round_up(per, 256);
 }
 
-extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k, const lit_idx_in* exact,
-                                      const float* hints, int32_t* ids, int32_t* count, uint8_t* mask, void* ws,
-                                      size_t ws_bytes, void* stream) {
-  clear_error();
-  if (!scores || !ids || !count) return fail(LIT_ERR_NULL, "lit_topk_select: scores, ids and count must be non-NULL");
-  if (B < 1 || N < 1 || k < 1) return fail(LIT_ERR_SHAPE, "lit_topk_select: B=%d N=%d k=%d must be >= 1", B, N, k);
-  if (N > (1 << 24)) return fail(LIT_ERR_SHAPE, "lit_topk_select: N=%d above 2^24", N);
+// B rows of scores; rows kq*s .. kq*s + kq-1 share the keys of sequence s.
+static lit_status topk_rows(const float* scores, int32_t B, int32_t kq, int32_t N, int32_t k, const lit_idx_in* exact,
+                            const float* hints, int32_t* ids, int32_t* count, uint8_t* mask, void* ws,
+                            size_t ws_bytes, void* stream, const char* who) {
+  if (!scores || !ids || !count) return fail(LIT_ERR_NULL, "%s: scores, ids and count must be non-NULL", who);
+  if (B < 1 || N < 1 || k < 1) return fail(LIT_ERR_SHAPE, "%s: rows=%d N=%d k=%d must be >= 1", who, B, N, k);
+  if (B > (1 << 30) / 2) return fail(LIT_ERR_SHAPE, "%s: %d rows above 2^29", who, B);
+  if (N > (1 << 24)) return fail(LIT_ERR_SHAPE, "%s: N=%d above 2^24", who, N);
   if (!aligned(scores, 4) || !aligned(ids, 4) || !aligned(count, 4) || (hints && !aligned(hints, 4)))
-    return fail(LIT_ERR_ALIGN, "lit_topk_select: scores, hints, ids and count must be 4-byte aligned");
+    return fail(LIT_ERR_ALIGN, "%s: scores, hints, ids and count must be 4-byte aligned", who);
   if (exact) {
-    lit_status st = check_idx_inputs(exact, B, N, "lit_topk_select(exact)");
+    lit_status st = check_idx_inputs(exact, B / kq, N, who);
     if (st != LIT_OK) return st;
-    if (!hints) return fail(LIT_ERR_NULL, "lit_topk_select: exact mode needs the hints side output of lit_idx_score");
+    if (!hints) return fail(LIT_ERR_NULL, "%s: exact mode needs the hints side output of the scoring call", who);
   }
   const size_t need = lit_topk_workspace_bytes(B, N, k);
   if (!ws || ws_bytes < need)
-    return fail(LIT_ERR_WORKSPACE, "lit_topk_select: workspace of %zu bytes given, %zu needed", ws_bytes, need);
-  if (!aligned(ws, 256)) return fail(LIT_ERR_ALIGN, "lit_topk_select: workspace must be 256-byte aligned");
+    return fail(LIT_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", who, ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(LIT_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
   const size_t per = (size_t)B * (size_t)N;
   uint8_t* w8 = (uint8_t*)ws;
   TopkParams P;
@@ -1386,6 +1388,7 @@ extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N,
   P.q = exact ? exact->q : nullptr;
   P.w = exact ? exact->w : nullptr;
   P.kidx = exact ? exact->k : nullptr;
+  P.kq = kq;
   P.dtype = exact ? (int)exact->dtype : 0;
   P.H = exact ? exact->H : 0;
   P.hints = hints;
@@ -1401,19 +1404,37 @@ extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N,
     const size_t lds = std::max(sizeof(FullLds), sizeof(SmallLds));
     const bool bf16 = P.exact && P.dtype == LIT_BF16;
     const void* kern = bf16 ? (const void*)topk_small_kernel<true> : (const void*)topk_small_kernel<false>;
-    lit_status st = allow_lds(kern, lds, "lit_topk_select");
+    lit_status st = allow_lds(kern, lds, who);
     if (st != LIT_OK) return st;
     if (bf16)
       topk_small_kernel<true><<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);
     else
       topk_small_kernel<false><<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);
-    LIT_CHECK_LAUNCH("lit_topk_select");
+    LIT_CHECK_LAUNCH(who);
     return LIT_OK;
   }
   const size_t lds = std::max(sizeof(FullLds), sizeof(FastLds));
-  lit_status st = allow_lds((const void*)topk_kernel, lds, "lit_topk_select");
+  lit_status st = allow_lds((const void*)topk_kernel, lds, who);
   if (st != LIT_OK) return st;
   topk_kernel<<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);
-  LIT_CHECK_LAUNCH("lit_topk_select");
+  LIT_CHECK_LAUNCH(who);
   return LIT_OK;
+}
+
+extern "C" lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k, const lit_idx_in* exact,
+                                      const float* hints, int32_t* ids, int32_t* count, uint8_t* mask, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  clear_error();
+  return topk_rows(scores, B, 1, N, k, exact, hints, ids, count, mask, ws, ws_bytes, stream, "lit_topk_select");
+}
+
+extern "C" lit_status lit_topk_select_mq(const float* scores, int32_t B, int32_t Q, int32_t N, int32_t k,
+                                         const lit_idx_in* exact, const float* hints, int32_t* ids, int32_t* count,
+                                         uint8_t* mask, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (Q < 1 || Q > LIT_MAX_QUERIES || B < 1)
+    return fail(LIT_ERR_SHAPE, "lit_topk_select_mq: B=%d, Q=%d (1..%d)", B, Q, LIT_MAX_QUERIES);
+  if ((int64_t)B * Q > (1 << 29)) return fail(LIT_ERR_SHAPE, "lit_topk_select_mq: B x Q above 2^29");
+  return topk_rows(scores, B * Q, Q, N, k, exact, hints, ids, count, mask, ws, ws_bytes, stream,
+                   "lit_topk_select_mq");
 }

@@ -142,3 +142,47 @@ def dense_layer_inputs(B: int, rows: int, Hq: int, layer: int, device="cpu") -> 
     q = synth.make_q(B, Hq, "bf16", g, device)
     kv = synth.make_kv(B, rows, "bf16", g, device)
     return q, kv
+
+
+# Several queries per sequence (the multi-query indexer): the index queries of
+# nearby tokens share a component, q_j = rho * q_0 + sqrt(1 - rho^2) * z_j
+# (z_j drawn like q_0), so the planted entries, aligned with q_0's head 0, stay
+# strong for every query; head weights are drawn afresh per query. Config id 6.
+MQ_CID = 6
+MQ_RHO = 0.8
+# depth-1 MTP: the current token and its draft, 32 sequences at 64K context
+MTP_Q = 2
+# a prefill chunk: the last 2048 tokens of a 64K prompt, one sequence
+PREFILL_Q = 2048
+PREFILL_T = 65536
+
+
+def extra_queries(idx: synth.IndexerInputs, Q: int, layer: int, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Q index queries per sequence [B,Q,H,128] and weights [B,Q,H] around the
+    single query of `idx` (which becomes query 0)."""
+    B, H = idx.q_idx.shape[0], idx.q_idx.shape[1]
+    g = synth.generator(device, MQ_CID, layer)
+    q0 = idx.q_idx.float()
+    z = torch.randn(B, Q, H, synth.IDX_DIM, generator=g, device=device)
+    q = MQ_RHO * q0[:, None] + math.sqrt(1.0 - MQ_RHO ** 2) * z
+    q[:, 0] = q0
+    w = torch.rand(B, Q, H, generator=g, device=device)
+    w[:, 0] = idx.w
+    return q.to(idx.q_idx.dtype).contiguous(), w.contiguous()
+
+
+def mq_inputs(wl: Workload, Q: int, layer: int = 0, device="cpu", B: Optional[int] = None,
+              N: Optional[int] = None) -> synth.IndexerInputs:
+    """Index queries [B,Q,H,128], weights [B,Q,H] and the keys [B,N,128] of
+    layer_inputs(wl, layer) (whose own query is query 0)."""
+    L = layer_inputs(wl, layer, device, B=B, N=N)
+    q, w = extra_queries(L.idx, Q, layer, device)
+    return synth.IndexerInputs(q, w, L.idx.k_idx, L.idx.planted)
+
+
+def causal_lengths(B: int, Q: int, t0: int, device="cpu") -> torch.Tensor:
+    """Entries visible to the queries of tokens t0 .. t0+Q-1 (0-based positions):
+    a 4:1 compressed entry exists once its four tokens do, so token t sees
+    floor((t + 1) / 4) entries. [B,Q] int32."""
+    t = torch.arange(t0, t0 + Q, device=device, dtype=torch.int64)
+    return ((t + 1) // 4).to(torch.int32).expand(B, Q).contiguous()

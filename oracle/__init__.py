@@ -292,6 +292,37 @@ def pool_plan(gate, window: int, C: int):
     return m, cnt, ac
 
 
+def idx_score_mq(q, w, k, lengths=None, allowed=None) -> np.ndarray:
+    """The multi-query indexer: Q queries per sequence scored against that
+    sequence's keys (depth-1 MTP verifies the draft token with the current one;
+    a prefill chunk scores every token; [ARCH], the series list and (A)). Query
+    j of sequence b is row (b, j) and sees the entries n < lengths[b][j] (all N
+    when lengths is None); each row is the a1 score of that query against k[b],
+    -inf where the entry is hidden or not allowed. q [B,Q,H,128], w [B,Q,H],
+    k [B,N,128], lengths [B,Q], allowed [B,N] -> fp64 [B,Q,N]."""
+    q, w, k = np_of(q), np.ascontiguousarray(np_of(w), np.float32), np_of(k)
+    B, Q = q.shape[0], q.shape[1]
+    N = k.shape[1]
+    al = None if allowed is None else np.asarray(np_of(allowed)) != 0
+    ln = None if lengths is None else np.asarray(np_of(lengths), np.int64)
+    out = np.empty((B, Q, N), np.float64)
+    for b in range(B):
+        for j in range(Q):
+            vis = np.ones(N, bool) if al is None else al[b].copy()
+            if ln is not None:
+                vis[max(int(ln[b, j]), 0):] = False
+            out[b, j] = idx_score(q[b, j][None], w[b, j][None], k[b][None], vis[None].astype(np.uint8))[0]
+    return out
+
+
+def topk_mq(scores64, k: int):
+    """The per-query top-k of idx_score_mq's rows: ids [B,Q,k], count [B,Q], mask [B,Q,N]."""
+    s = np.ascontiguousarray(np_of(scores64), np.float64)
+    B, Q, N = s.shape
+    ids, cnt, mask = topk(s.reshape(B * Q, N), k)
+    return ids.reshape(B, Q, k), cnt.reshape(B, Q), mask.reshape(B, Q, N)
+
+
 def topp_vote(x, is_logits: bool, top_p: float = 0.6, min_votes: int = 3):
     """a9 ([LSA] 3.2): x [L,B,N] fp64 -> gold [B,N] u8, gold_count [B], votes [B,N]."""
     x = np.ascontiguousarray(np_of(x), np.float64)

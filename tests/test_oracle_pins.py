@@ -515,3 +515,68 @@ def test_pool_plan_invariants_on_random_gates():
         assert set(np.flatnonzero(g[b]).tolist()) <= set(kept.tolist())     # every gated entry is in
         assert (a[b][300 - c[b]:] == g[b][kept]).all() and a[b][: 300 - c[b]].sum() == 0
         assert c[b] == len(set(np.flatnonzero(g[b]).tolist()) | set(range(268, 300)))
+
+
+# ---------------------------------------------------------------- multi-query indexer
+
+def _unit_keys(B, N):
+    # key n of sequence b = (b + 1) * e_(n mod 128): the head dot products read
+    # one coordinate of the query, scaled by the sequence's number
+    k = np.zeros((B, N, 128), np.float32)
+    for b in range(B):
+        for n in range(N):
+            k[b, n, n % 128] = b + 1
+    return k
+
+
+def test_mq_score_closed_form_rows_keys_weights_and_lengths():
+    # two heads per query: head 0 = a, head 1 = -a, weights (r+1, 10(r+1)) for
+    # row r = b*Q + j. Against key (b+1) e_i the score is
+    #   (b+1)(r+1) * (a_i if a_i > 0 else -10 a_i)
+    # (ReLU keeps exactly one head), and -inf from lengths[b][j] on.
+    B, Q, N = 2, 3, 150
+    a = rng.integers(-4, 5, size=(B, Q, 128)).astype(np.float32) / 4
+    q = np.stack([a, -a], axis=2)  # [B,Q,2,128]
+    r = np.arange(B * Q, dtype=np.float32).reshape(B, Q) + 1
+    w = np.stack([r, 10 * r], axis=2)
+    lengths = np.array([[150, 7, 0], [129, 1, 200]], np.int32)
+    s = oracle.idx_score_mq(q, w, _unit_keys(B, N), lengths)
+    for b in range(B):
+        for j in range(Q):
+            for n in range(N):
+                ai = a[b, j, n % 128]
+                want = (b + 1) * r[b, j] * (ai if ai > 0 else -10 * ai)
+                if n >= min(lengths[b, j], N):
+                    want = -np.inf
+                assert s[b, j, n] == want, (b, j, n)
+
+
+def test_mq_score_allowed_is_shared_by_the_queries_of_a_sequence():
+    B, Q, N = 2, 2, 40
+    a = np.abs(rng.standard_normal((B, Q, 1, 128))).astype(np.float32) + 0.5
+    w = np.ones((B, Q, 1), np.float32)
+    allowed = np.zeros((B, N), np.uint8)
+    allowed[0, ::3] = 1
+    allowed[1, 5:9] = 1
+    s = oracle.idx_score_mq(a, w, _unit_keys(B, N), None, allowed)
+    for b in range(B):
+        for j in range(Q):
+            assert (np.isfinite(s[b, j]) == (allowed[b] == 1)).all()
+            vis = np.flatnonzero(allowed[b])
+            assert np.array_equal(s[b, j, vis], (b + 1) * a[b, j, 0, vis % 128])
+
+
+def test_mq_topk_rows_select_among_visible_entries():
+    # query j sees j+2 entries with scores 1..; its top-3 are the best of those
+    B, Q, N = 1, 4, 12
+    s = np.full((B, Q, N), 0.0)
+    s[0] = np.arange(N)[None, :] % 5 + 1.0
+    for j in range(Q):
+        s[0, j, j + 2:] = -np.inf
+    ids, cnt, mask = oracle.topk_mq(s, 3)
+    for j in range(Q):
+        vis = list(range(j + 2))
+        want = sorted(sorted(vis, key=lambda n: (-s[0, j, n], n))[:3])
+        assert cnt[0, j] == min(3, j + 2)
+        assert ids[0, j, : cnt[0, j]].tolist() == want and (ids[0, j, cnt[0, j]:] == -1).all()
+        assert mask[0, j].sum() == cnt[0, j]
