@@ -18,7 +18,7 @@ the eager result) and replayed. Besides the headline line the JSON carries:
                  500K batch-4 step (distinct layers rotated so every replay
                  streams from HBM), and the LSA cold-pool fetch at the gate
                  workload's shapes.
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only lookahead|prefill|offload]
 """
 from __future__ import annotations
 
@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--only", choices=["lookahead", "prefill", "offload"],
+                    help="run one secondary measurement alone and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus above 1 is not supported "
@@ -182,8 +184,13 @@ def main():
         torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    wl = W.CTX64K_B
     scale = 1.0 / math.sqrt(512)
+    if args.only:
+        fn = {"lookahead": lookahead, "prefill": lambda lit, W, dev, scale: prefill(lit, W, dev),
+              "offload": offload}[args.only]
+        print(json.dumps({args.only: fn(lit, W, dev, scale)}))
+        return
+    wl = W.CTX64K_B
     print(f"[bench] generating {wl.name}: {wl.layers} layers x {wl.B} sequences x N={wl.N}", file=sys.stderr,
           flush=True)
     layers = [W.layer_inputs(wl, l, dev) for l in range(wl.layers)]
@@ -411,6 +418,78 @@ def prefill(lit, W, dev):
             "all_counts_k": ok}
 
 
+FP64_PEAK_TFLOPS = 78.6
+
+
+def lookahead(lit, W, dev, scale):
+    """The lookahead golden at the gate workload's shapes (8 sequences, 16384
+    entries, FP8 rows, 64 heads, top-1024) over a tau = 64 step horizon: the
+    fp64 logits of 64 x 64 query rows against every row (a [4096 x 512] x [512
+    x 16384] product per sequence on the fp64 matrix cores), each step's
+    golden top-1024, and their union. Reported: the logits kernel's rate
+    against the fp64 matrix-core peak, the whole call, and how much of the
+    horizon's union three selections of the current step cover (the LSA gate
+    at layers 10/12/20, the native top-1024 at layer 10, the current step's
+    golden) -- on synthetic data, so these coverages describe the inputs, not
+    the model. The rate counts the logits' flops over the whole call (the
+    softmax, top-k and union passes included)."""
+    import torch
+
+    wl = W.GATE64K
+    T = W.TAU
+    keys = [W.layer_inputs(wl, l, dev).idx.k_idx for l in W.GATE_LAYERS]
+    gl = [W.gate_layer(wl, l, kk, dev) for l, kk in zip(W.GATE_LAYERS, keys)]
+    gate, _ = lit.lsa_gate(gl, 0.5)
+    del gl, keys
+    L = W.layer_inputs(wl, 10, dev)
+    q = W.horizon_queries(L.q, T, 10, dev)
+    s_, h_ = lit.idx_score(L.idx.q_idx, L.idx.w, L.idx.k_idx)
+    _, _, native = lit.topk_select(s_, wl.k, exact=(L.idx.q_idx, L.idx.w, L.idx.k_idx), hints=h_)
+    C = lit.load()
+    B, Hq, N, k = wl.B, wl.Hq, wl.N, wl.k
+    ws = torch.empty(C.lit_lookahead_workspace_bytes(B, T, Hq, N, k), dtype=torch.uint8, device=dev)
+    hits = torch.empty(B, N, dtype=torch.int32, device=dev)
+    um = torch.empty(B, N, dtype=torch.uint8, device=dev)
+    uc = torch.empty(B, dtype=torch.int32, device=dev)
+    sids = torch.empty(B, T, k, dtype=torch.int32, device=dev)
+    desc = lit.kv_desc(L.kv)
+
+    def call(s):
+        assert C.lit_lookahead_golden(q.data_ptr(), lit.LIT_BF16, T, Hq, ctypes.byref(desc), B, scale, k,
+                                      sids.data_ptr(), hits.data_ptr(), um.data_ptr(), uc.data_ptr(), None,
+                                      ws.data_ptr(), ws.numel(), s) == 0, lit.last_error()
+
+    s0 = torch.cuda.current_stream().cuda_stream
+    call(s0)
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call(s0)
+    e1.record()
+    torch.cuda.synchronize()
+    total_s = e0.elapsed_time(e1) / 1e3 / reps
+    flops = 2.0 * B * T * Hq * 512 * N
+    first = sids[:, 0]
+    gold0 = torch.zeros(B, N, dtype=torch.uint8, device=dev)
+    gold0.scatter_(1, first.clamp(min=0).long(), 1)
+    cov = {}
+    for name, m in (("lsa_gate", gate), ("native_top1024", native), ("current_golden", gold0)):
+        inter, _, cu = lit.recall(m, um)
+        cov[name] = round(float(inter.sum().item()) / float(cu.sum().item()), 4)
+    res = {"sequences": B, "entries": N, "horizon": T, "heads": Hq, "k": k,
+           "call_ms": round(total_s * 1e3, 2), "logits_flops": flops,
+           "call_TFLOPs_fp64": round(flops / total_s / 1e12, 1),
+           "call_fp64_mfma_frac": round(flops / total_s / 1e12 / FP64_PEAK_TFLOPS, 4),
+           "union_mean": round(float(uc.float().mean().item()), 1),
+           "union_over_k": round(float(uc.float().mean().item()) / k, 3),
+           "union_coverage": cov}
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def others(lit, W, dev, scale):
     """Secondary figures: 64K batch-1 latency and the 500K batch-4 step."""
     import torch
@@ -469,6 +548,8 @@ def others(lit, W, dev, scale):
     res["gate64k_offload"] = offload(lit, W, dev, scale)
     print("[bench] multi-query indexer: prefill chunk", file=sys.stderr, flush=True)
     res["prefill_chunk_indexer"] = prefill(lit, W, dev)
+    print("[bench] lookahead golden", file=sys.stderr, flush=True)
+    res["lookahead_golden_gate64k"] = lookahead(lit, W, dev, scale)
     return res
 
 

@@ -9,6 +9,7 @@
  *   lit_sparse_attn_decode  MQA attention over the kept rows plus the SWA window
  *   lit_golden_topk      dense "golden" attention and its top-k (measurement)
  *   lit_golden_topp_vote top-p 0.6 per layer, then a cross-layer vote (labels)
+ *   lit_lookahead_golden the golden sets of the next T steps and their union
  *   lit_recall           set overlap of two selections
  *   lit_lsa_gate         sigmoid chunk gate of FlashMemory/LSA (candidate set)
  *   lit_pool_plan / lit_pool_gather / lit_pool_remap_ids
@@ -80,6 +81,7 @@ extern "C" {
 #define LIT_MAX_Q_HEADS 64
 #define LIT_MAX_WINDOW 8192
 #define LIT_MAX_QUERIES 65536 /* queries per sequence of the multi-query calls */
+#define LIT_MAX_HORIZON 1024  /* decode steps of a lookahead golden */
 
 typedef enum {
   LIT_OK = 0,
@@ -238,6 +240,33 @@ lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t Hq, const l
                            int32_t B, float scale, int32_t k,
                            int32_t* ids, int32_t* count, uint8_t* mask, double* pbar,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---- NEXT: the lookahead golden -------------------------------------------------
+ * [FMEN] "The one caveat I didn't test: lookahead" and [LSA] 2.2: the gate is
+ * meant to predict what the next tau = 64 decode steps will attend to, not what
+ * the current step does, and the golden for that target needs the dense
+ * attention of every step of the horizon. For sequence b and each step t of the
+ * horizon (query q[b][t], the same N rows), G[b][t] is the a6 golden set:
+ *     P[h][n] = softmax_n(scale * (q[b][t][h] . kv[b][n])),  pbar[n] = (sum_h P[h][n]) / Hq,
+ *     G[b][t] = top-k of pbar (descending, then index ascending)       (fp64)
+ * and the lookahead golden is what the horizon needs:
+ *     hits[b][n] = #{t : n in G[b][t]},  union_mask[b][n] = hits[b][n] > 0,
+ *     union_count[b] = #{n : hits[b][n] > 0}.
+ * The logits are fp64 sums of exact products (matrix cores; the order of the
+ * fp64 additions is not sequential, so pbar matches a sequential fp64 sum to a
+ * relative 1e-12, not bit for bit).
+ * q         : [B][T][Hq][512] (the T queries of the horizon), dtype as for a6.
+ * step_ids  : [B][T][k] int32 output (each step's golden ids ascending, tail -1) or NULL.
+ * hits      : [B][N] int32 output or NULL;  union_mask : [B][N] u8 output or NULL;
+ * union_count : [B] int32 output;  pbar : [B][T][N] fp64 output or NULL.
+ * Workspace: lit_lookahead_workspace_bytes(B, T, Hq, N, k) bytes (it holds the
+ * fp64 logits, B*T*Hq*N*8 bytes: 4.3 GB at B = 8, T = Hq = 64, N = 16384). */
+size_t lit_lookahead_workspace_bytes(int32_t B, int32_t T, int32_t Hq, int32_t N, int32_t k);
+lit_status lit_lookahead_golden(const void* q, lit_dtype q_dtype, int32_t T, int32_t Hq,
+                                const lit_kv* kv, int32_t B, float scale, int32_t k,
+                                int32_t* step_ids, int32_t* hits, uint8_t* union_mask,
+                                int32_t* union_count, double* pbar, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* ---- a9: top-p per layer, then a cross-layer vote -----------------------------
  * [LSA] 3.2: per layer, turn the scores into probabilities with a softmax, keep

@@ -35,7 +35,7 @@ EXPORTS = [
     "lit_attn_workspace_bytes", "lit_sparse_attn_decode", "lit_golden_workspace_bytes", "lit_golden_topk",
     "lit_topp_workspace_bytes", "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall",
     "lit_gate_workspace_bytes", "lit_lsa_gate", "lit_pool_plan", "lit_pool_gather", "lit_pool_remap_ids",
-    "lit_idx_score_mq", "lit_topk_select_mq",
+    "lit_idx_score_mq", "lit_topk_select_mq", "lit_lookahead_workspace_bytes", "lit_lookahead_golden",
 ]
 
 
@@ -101,9 +101,13 @@ def load(path: str = LIB_PATH):
     L.lit_pool_remap_ids.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
     L.lit_idx_score_mq.argtypes = [ctypes.POINTER(IdxIn), i32, vp, vp, i32, i32, vp, vp, vp]
     L.lit_topk_select_mq.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(IdxIn), vp, vp, vp, vp, vp, sz, vp]
+    L.lit_lookahead_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.lit_lookahead_workspace_bytes.restype = sz
+    L.lit_lookahead_golden.argtypes = [vp, ctypes.c_int, i32, i32, ctypes.POINTER(KVDesc), i32, f32, i32, vp, vp, vp,
+                                       vp, vp, vp, sz, vp]
     for name in ("lit_idx_score", "lit_topk_select", "lit_sparse_attn_decode", "lit_golden_topk",
                  "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall", "lit_lsa_gate", "lit_pool_plan",
-                 "lit_pool_gather", "lit_pool_remap_ids", "lit_idx_score_mq", "lit_topk_select_mq"):
+                 "lit_pool_gather", "lit_pool_remap_ids", "lit_idx_score_mq", "lit_topk_select_mq", "lit_lookahead_golden"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -301,6 +305,30 @@ def golden_topk(q, kv, k: int, scale: float = DEFAULT_SCALE, want_pbar: bool = T
                              ids.data_ptr(), count.data_ptr(), _ptr(mask), _ptr(pbar), ws.data_ptr(), ws.numel(),
                              _stream(q)))
     return ids, count, mask, pbar
+
+
+def lookahead_golden(q, kv, k: int, scale: float = DEFAULT_SCALE, want_step_ids: bool = True,
+                     want_pbar: bool = False, ws=None):
+    """Lookahead golden of the T queries q [B,T,Hq,512] against kv: step_ids
+    [B,T,k], hits [B,N] int32, union_mask [B,N] u8, union_count [B], pbar [B,T,N]."""
+    torch = _torch()
+    _need_cuda(q)
+    B, T, Hq = q.shape[0], q.shape[1], q.shape[2]
+    desc = kv_desc(kv)
+    N = desc.n_rows
+    dev = q.device
+    step_ids = torch.empty(B, T, k, dtype=torch.int32, device=dev) if want_step_ids else None
+    hits = torch.empty(B, N, dtype=torch.int32, device=dev)
+    umask = torch.empty(B, N, dtype=torch.uint8, device=dev)
+    ucount = torch.empty(B, dtype=torch.int32, device=dev)
+    pbar = torch.empty(B, T, N, dtype=torch.float64, device=dev) if want_pbar else None
+    L = load()
+    if ws is None:
+        ws = workspace(L.lit_lookahead_workspace_bytes(B, T, Hq, N, k), dev)
+    _check(L.lit_lookahead_golden(q.data_ptr(), _dtype_code(q), T, Hq, ctypes.byref(desc), B, float(scale), k,
+                                  _ptr(step_ids), hits.data_ptr(), umask.data_ptr(), ucount.data_ptr(), _ptr(pbar),
+                                  ws.data_ptr(), ws.numel(), _stream(q)))
+    return step_ids, hits, umask, ucount, pbar
 
 
 def golden_topp_vote(x, is_logits: bool, top_p: float = 0.6, min_votes: int = 3, want_votes: bool = True, ws=None):

@@ -275,6 +275,190 @@ __global__ __launch_bounds__(256) void vote_kernel(const int32_t* __restrict__ v
   if (tid == 0) gold_count[b] = red[0] + red[1] + red[2] + red[3];
 }
 
+// ---- lookahead golden ------------------------------------------------------------
+//
+// Logits of T queries x Hq heads against every row of a sequence: a [T*Hq x 512]
+// x [512 x N] product, computed on the fp64 matrix cores (v_mfma_f64_16x16x4f64:
+// lane l holds A[l%16][l/16] and B[l/16][l%16] of a 16x4 / 4x16 step, and its
+// result register r holds D[l/16 + 4r][l%16] -- rows interleaved by four,
+// unlike the fp32 16x16 forms, as measured on gfx950). Products of the bf16 / fp32 / decoded FP8
+// inputs are exact in fp64, so the logits differ from a sequential fp64 sum only
+// by the order of the fp64 additions. A workgroup computes a 64 x 64 tile (four
+// waves of 32 x 32, i.e. 2 x 2 blocks of 16 x 16), staging 32 dims of both
+// operands in LDS at a time, converted to fp64 once.
+typedef double f64x4 __attribute__((__vector_size__(4 * sizeof(double))));
+constexpr int LA_TILE = 64;
+constexpr int LA_KC = 32;
+
+// Raw bits of 8 consecutive dims of one row (one thread's share of a stage):
+// fp32 in two 16-byte words, bf16 in one, FP8 bytes in the first half of one
+// (RoPE dims as bf16), and the row's E8M0 scale byte of those dims.
+struct Raw8 {
+  u32x4 w[2];
+  uint32_t sb;
+};
+
+__device__ __forceinline__ Raw8 load_q8(int q_dtype, const void* q, size_t off, bool live) {
+  Raw8 r{};
+  if (live) {
+    if (q_dtype == LIT_F32) {
+      r.w[0] = *(const u32x4*)((const float*)q + off);
+      r.w[1] = *(const u32x4*)((const float*)q + off + 4);
+    } else {
+      r.w[0] = *(const u32x4*)((const uint16_t*)q + off);
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ Raw8 load_kv8(int kv_dtype, const void* data, const uint16_t* rope, const uint8_t* scale,
+                                         size_t row, int d, bool live) {
+  Raw8 r{};
+  if (!live) return r;
+  if (kv_dtype == LIT_F32) {
+    r.w[0] = *(const u32x4*)((const float*)data + row * LIT_KV_DIM + d);
+    r.w[1] = *(const u32x4*)((const float*)data + row * LIT_KV_DIM + d + 4);
+  } else if (kv_dtype == LIT_BF16) {
+    r.w[0] = *(const u32x4*)((const uint16_t*)data + row * LIT_KV_DIM + d);
+  } else if (d >= LIT_KV_FP8_DIMS) {
+    r.w[0] = *(const u32x4*)(rope + row * LIT_KV_ROPE_DIMS + d - LIT_KV_FP8_DIMS);
+  } else {
+    const u32x2 v = *(const u32x2*)((const uint8_t*)data + row * LIT_KV_FP8_DIMS + d);
+    r.w[0][0] = v[0];
+    r.w[0][1] = v[1];
+    r.sb = scale[row * LIT_KV_SCALE_STRIDE + d / LIT_KV_FP8_GROUP];
+  }
+  return r;
+}
+
+// OCP E4M3FN byte and E8M0 scale byte to fp32, as kv_elem_f32 decodes them.
+__device__ __forceinline__ float fp8_e4m3_f32(uint32_t byte) {
+  const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
+  float v;
+  if (e == 15u && m == 7u)
+    v = __uint_as_float(0x7fc00000u);
+  else if (e == 0u)
+    v = (float)m * 0x1p-9f;
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t sb) {
+  return sb == 255u ? __uint_as_float(0x7fc00000u) : (sb == 0u ? 0x1p-127f : __uint_as_float(sb << 23));
+}
+
+// The 8 values of a Raw8 as fp64 (the value the fp32 decode gives, widened).
+__device__ __forceinline__ void widen8(int dtype, bool fp8_part, const Raw8& r, double (&x)[8]) {
+  if (dtype == LIT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[i] = (double)__uint_as_float(r.w[0][i]);
+      x[4 + i] = (double)__uint_as_float(r.w[1][i]);
+    }
+  } else if (!fp8_part) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x[2 * i] = (double)bf16_lo(r.w[0][i]);
+      x[2 * i + 1] = (double)bf16_hi(r.w[0][i]);
+    }
+  } else {
+    const float sc = e8m0_f32(r.sb);
+#pragma unroll
+    for (int i = 0; i < 8; i++) x[i] = (double)(fp8_e4m3_f32((r.w[0][i >> 2] >> (8 * (i & 3))) & 255u) * sc);
+  }
+}
+
+__global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, int q_dtype, int M, int kv_dtype,
+                                                               const void* data, const uint16_t* rope,
+                                                               const uint8_t* scale, int N, double sc,
+                                                               double* __restrict__ X) {
+  __shared__ double As[LA_KC][LA_TILE + 1];  // [dim][row]
+  __shared__ double Bs[LA_KC][LA_TILE + 1];  // [dim][entry]
+  const int b = blockIdx.z, m0 = blockIdx.y * LA_TILE, n0 = blockIdx.x * LA_TILE;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = (wid >> 1) * 32, wn = (wid & 1) * 32;
+  const int r16 = lane & 15, k4 = lane >> 4;
+  // staging: thread tid takes dims d0 .. d0+7 of row rr of both operands
+  const int rr = tid >> 2, d0 = (tid & 3) * 8;
+  const int m = m0 + rr, n = n0 + rr;
+  const size_t qoff = ((size_t)b * M + m) * LIT_KV_DIM + d0;
+  const size_t krow = (size_t)b * N + n;
+  const bool fp8 = kv_dtype == LIT_FP8E4M3_G64_ROPE_BF16;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // the next stage's raw operands are loaded while this stage multiplies
+  Raw8 ra = load_q8(q_dtype, q, qoff, m < M);
+  Raw8 rb = load_kv8(kv_dtype, data, rope, scale, krow, d0, n < N);
+  for (int k0 = 0; k0 < LIT_KV_DIM; k0 += LA_KC) {
+    double xa[8], xb[8];
+    widen8(q_dtype, false, ra, xa);
+    widen8(kv_dtype, fp8 && k0 + d0 < LIT_KV_FP8_DIMS, rb, xb);
+    __syncthreads();  // the previous stage's reads are done
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      As[d0 + i][rr] = xa[i];
+      Bs[d0 + i][rr] = xb[i];
+    }
+    __syncthreads();
+    if (k0 + LA_KC < LIT_KV_DIM) {
+      ra = load_q8(q_dtype, q, qoff + k0 + LA_KC, m < M);
+      rb = load_kv8(kv_dtype, data, rope, scale, krow, k0 + LA_KC + d0, n < N);
+    }
+#pragma unroll
+    for (int kk = 0; kk < LA_KC; kk += 4) {
+      double a[2], bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) a[i] = As[kk + k4][wm + 16 * i + r16];
+#pragma unroll
+      for (int j = 0; j < 2; j++) bb[j] = Bs[kk + k4][wn + 16 * j + r16];
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int nn = n0 + wn + 16 * j + r16;
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int mm = m0 + wm + 16 * i + k4 + 4 * r;
+        if (mm < M && nn < N) X[((size_t)b * M + mm) * N + nn] = sc * acc[i][j][r];
+      }
+    }
+}
+
+// hits[b][n] = number of the T steps whose golden set holds n (t ascending);
+// umask = hits > 0. One thread per entry.
+__global__ __launch_bounds__(256) void lookahead_union_kernel(const uint8_t* __restrict__ step_mask, int T, int N,
+                                                              int32_t* __restrict__ hits, uint8_t* __restrict__ umask) {
+  const int b = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  int h = 0;
+  for (int t = 0; t < T; t++) h += step_mask[((size_t)b * T + t) * N + n];
+  if (hits) hits[(size_t)b * N + n] = h;
+  umask[(size_t)b * N + n] = h > 0;
+}
+
+// ucount[b] = number of set bytes of umask[b].
+__global__ __launch_bounds__(256) void count_u8_kernel(const uint8_t* __restrict__ umask, int N,
+                                                       int32_t* __restrict__ ucount) {
+  __shared__ int red[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int c = 0;
+  for (int n = tid; n < N; n += 256) c += umask[(size_t)b * N + n] != 0;
+  c = wave_sum(c);
+  if ((tid & 63) == 0) red[tid >> 6] = c;
+  __syncthreads();
+  if (tid == 0) ucount[b] = red[0] + red[1] + red[2] + red[3];
+}
+
 struct GoldenWs {
   double* X;
   double* stats;
@@ -388,6 +572,91 @@ extern "C" lit_status lit_golden_topp_vote(const double* x, int32_t is_logits, i
   topp_kernel<<<dim3((unsigned)rows), 1024, 0, st>>>(x, is_logits, B, N, np2, top_p, prob, keys, idx, vacc);
   LIT_CHECK_LAUNCH(who);
   vote_kernel<<<dim3((unsigned)B), 256, 0, st>>>(vacc, N, min_votes, gold, gold_count, votes);
+  LIT_CHECK_LAUNCH(who);
+  return LIT_OK;
+}
+
+// ---- lookahead golden --------------------------------------------------------------
+
+namespace {
+struct LookaheadWs {
+  GoldenWs g;  // logits / stats / pbar / selection scratch of the B*T (sequence, step) rows
+  int32_t* ids;
+  int32_t* cnt;
+  uint8_t* mask;
+  uint8_t* umask;
+  size_t bytes;
+};
+
+LookaheadWs lookahead_ws(void* base, int B, int T, int Hq, int N, int k) {
+  LookaheadWs w;
+  w.g = golden_ws(base, B * T, Hq, N);
+  uint8_t* p = (uint8_t*)base;
+  size_t off = w.g.bytes;
+  w.ids = (int32_t*)(p + off);
+  off += round_up((size_t)B * T * k * sizeof(int32_t), 256);
+  w.cnt = (int32_t*)(p + off);
+  off += round_up((size_t)B * T * sizeof(int32_t), 256);
+  w.mask = p + off;
+  off += round_up((size_t)B * T * N, 256);
+  w.umask = p + off;
+  off += round_up((size_t)B * N, 256);
+  w.bytes = off;
+  return w;
+}
+}  // namespace
+
+extern "C" size_t lit_lookahead_workspace_bytes(int32_t B, int32_t T, int32_t Hq, int32_t N, int32_t k) {
+  if (B < 1 || T < 1 || Hq < 1 || N < 1 || k < 1) return 0;
+  return lookahead_ws(nullptr, B, T, Hq, N, k).bytes;
+}
+
+extern "C" lit_status lit_lookahead_golden(const void* q, lit_dtype q_dtype, int32_t T, int32_t Hq, const lit_kv* kv,
+                                           int32_t B, float scale, int32_t k, int32_t* step_ids, int32_t* hits,
+                                           uint8_t* union_mask, int32_t* union_count, double* pbar, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  clear_error();
+  const char* who = "lit_lookahead_golden";
+  if (!q || !kv || !kv->data || !union_count)
+    return fail(LIT_ERR_NULL, "%s: q, kv and union_count are required", who);
+  if (B < 1 || T < 1 || T > LIT_MAX_HORIZON || Hq < 1 || Hq > LIT_MAX_Q_HEADS || kv->n_rows < 1 || k < 1)
+    return fail(LIT_ERR_SHAPE, "%s: B=%d T=%d (1..%d) Hq=%d N=%d k=%d", who, B, T, LIT_MAX_HORIZON, Hq, kv->n_rows, k);
+  if ((int64_t)B * T > 65535) return fail(LIT_ERR_SHAPE, "%s: B x T = %lld above 65535", who, (long long)B * T);
+  if (kv->dtype == LIT_F32 ? q_dtype != LIT_F32 : q_dtype != LIT_BF16)
+    return fail(LIT_ERR_DTYPE, "%s: query dtype %d does not match rows dtype %d", who, (int)q_dtype, (int)kv->dtype);
+  if (kv->dtype != LIT_F32 && kv->dtype != LIT_BF16 && kv->dtype != LIT_FP8E4M3_G64_ROPE_BF16)
+    return fail(LIT_ERR_DTYPE, "%s: kv dtype %d unsupported", who, (int)kv->dtype);
+  if (kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 && (!kv->rope || !kv->scale))
+    return fail(LIT_ERR_NULL, "%s: FP8 rows need rope and scale arrays", who);
+  if (!aligned(q, 16) || !aligned(kv->data, kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 ? 8 : 16) ||
+      (kv->rope && !aligned(kv->rope, 16)))
+    return fail(LIT_ERR_ALIGN, "%s: q and the rows must be 16-byte aligned (FP8 row bytes 8-byte)", who);
+  const int N = kv->n_rows;
+  LookaheadWs W = lookahead_ws(ws, B, T, Hq, N, k);
+  if (!ws || ws_bytes < W.bytes)
+    return fail(LIT_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", who, ws_bytes, W.bytes);
+  if (!aligned(ws, 256) || (pbar && !aligned(pbar, 8)) || (step_ids && !aligned(step_ids, 4)) ||
+      (hits && !aligned(hits, 4)) || !aligned(union_count, 4))
+    return fail(LIT_ERR_ALIGN, "%s: workspace 256-byte, pbar 8-byte, integer outputs 4-byte aligned", who);
+  hipStream_t st = (hipStream_t)stream;
+  const int BT = B * T, M = T * Hq;
+  double* pb = pbar ? pbar : W.g.pbar;
+  int32_t* ids = step_ids ? step_ids : W.ids;
+  dim3 g1((unsigned)cdiv(N, LA_TILE), (unsigned)cdiv(M, LA_TILE), (unsigned)B);
+  lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, M, (int)kv->dtype, kv->data,
+                                              (const uint16_t*)kv->rope, kv->scale, N, (double)scale, W.g.X);
+  LIT_CHECK_LAUNCH(who);
+  // each (sequence, step) row is one a6 golden: softmax per head, head average, top-k
+  golden_stats_kernel<<<dim3((unsigned)(BT * Hq)), 1024, 0, st>>>(W.g.X, N, W.g.stats);
+  LIT_CHECK_LAUNCH(who);
+  golden_pbar_kernel<<<dim3((unsigned)cdiv(N, 256), (unsigned)BT), 256, 0, st>>>(W.g.X, W.g.stats, Hq, N, pb);
+  LIT_CHECK_LAUNCH(who);
+  topk_f64_kernel<<<dim3((unsigned)BT), 1024, 0, st>>>(pb, N, k, W.g.sel, ids, W.cnt, W.mask);
+  LIT_CHECK_LAUNCH(who);
+  uint8_t* um = union_mask ? union_mask : W.umask;
+  lookahead_union_kernel<<<dim3((unsigned)cdiv(N, 256), (unsigned)B), 256, 0, st>>>(W.mask, T, N, hits, um);
+  LIT_CHECK_LAUNCH(who);
+  count_u8_kernel<<<dim3((unsigned)B), 256, 0, st>>>(um, N, union_count);
   LIT_CHECK_LAUNCH(who);
   return LIT_OK;
 }

@@ -186,3 +186,19 @@ def causal_lengths(B: int, Q: int, t0: int, device="cpu") -> torch.Tensor:
     floor((t + 1) / 4) entries. [B,Q] int32."""
     t = torch.arange(t0, t0 + Q, device=device, dtype=torch.int64)
     return ((t + 1) // 4).to(torch.int32).expand(B, Q).contiguous()
+
+
+# The lookahead golden: the attention queries of the next TAU decode steps,
+# drawn like the multi-query index queries (step 0 is the layer's own query,
+# step t >= 1 mixes it with a fresh draw: rho * q_0 + sqrt(1 - rho^2) * z_t).
+TAU = 64
+
+
+def horizon_queries(q0: torch.Tensor, T: int, layer: int, device="cpu") -> torch.Tensor:
+    """[B,T,Hq,512] attention queries of a T-step horizon around q0 [B,Hq,512]."""
+    B, Hq, D = q0.shape
+    g = synth.generator(device, MQ_CID, 1000 + layer)
+    z = torch.randn(B, T, Hq, D, generator=g, device=device)
+    q = MQ_RHO * q0.float()[:, None] + math.sqrt(1.0 - MQ_RHO ** 2) * z
+    q[:, 0] = q0.float()
+    return q.to(q0.dtype).contiguous()

@@ -225,6 +225,29 @@ def golden(q, kv, scale: float, k: int):
     return ids, cnt, mask, pbar
 
 
+def lookahead_golden(q, kv, scale: float, k: int):
+    """The lookahead golden ([FMEN] "The one caveat I didn't test: lookahead";
+    [LSA] 2.2: the gate predicts what the next 64 steps need): for every step t
+    of the horizon, the a6 golden set of its query q[:, t] against the same rows;
+    hits[b][n] counts the steps whose set holds n, the union is hits > 0.
+    q [B,T,Hq,512] -> step_ids [B,T,k], hits [B,N], union_mask [B,N] u8,
+    union_count [B], pbar [B,T,N]."""
+    q = np_of(q)
+    kv = kv_from(kv)
+    B, T = q.shape[0], q.shape[1]
+    N = kv.n_rows
+    step_ids = np.empty((B, T, k), np.int32)
+    hits = np.zeros((B, N), np.int32)
+    pbar = np.empty((B, T, N), np.float64)
+    for t in range(T):
+        ids, _, mask, pb = golden(np.ascontiguousarray(q[:, t]), kv, scale, k)
+        step_ids[:, t] = ids
+        hits += mask.astype(np.int32)
+        pbar[:, t] = pb
+    umask = (hits > 0).astype(np.uint8)
+    return step_ids, hits, umask, umask.sum(-1).astype(np.int32), pbar
+
+
 def recall(a, m):
     """a7 ([FMEN] "Act 1", "Act 3"): intersection and set sizes per sequence."""
     a = np.ascontiguousarray(np_of(a), np.uint8)

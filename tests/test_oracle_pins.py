@@ -580,3 +580,52 @@ def test_mq_topk_rows_select_among_visible_entries():
         assert cnt[0, j] == min(3, j + 2)
         assert ids[0, j, : cnt[0, j]].tolist() == want and (ids[0, j, cnt[0, j]:] == -1).all()
         assert mask[0, j].sum() == cnt[0, j]
+
+
+# ---------------------------------------------------------------- lookahead golden
+
+def test_lookahead_sharp_queries_give_known_sets_union_and_hits():
+    # rows are 4 * e_i (i < 512); step t's query points at rows a_t and c_t on
+    # every head with a large weight, so its top-2 is {a_t, c_t} exactly; the
+    # union is the set of all a_t, c_t and hits counts repeats across steps
+    B, T, Hq, N = 2, 5, 3, 40
+    kv = np.zeros((B, N, 512), np.float32)
+    for n in range(N):
+        kv[:, n, n] = 4.0
+    targets = [[(3, 7), (7, 9), (3, 7), (0, 39), (12, 9)], [(1, 2), (1, 2), (1, 2), (1, 2), (5, 6)]]
+    q = np.zeros((B, T, Hq, 512), np.float32)
+    for b in range(B):
+        for t, (a, c) in enumerate(targets[b]):
+            q[b, t, :, a] = 8.0
+            q[b, t, :, c] = 8.0
+    ids, hits, um, uc, pbar = oracle.lookahead_golden(q, _kv(kv), 0.5, 2)
+    for b in range(B):
+        want_hits = np.zeros(N, int)
+        for t, (a, c) in enumerate(targets[b]):
+            assert ids[b, t].tolist() == sorted([a, c])
+            want_hits[a] += 1
+            want_hits[c] += 1
+        assert hits[b].tolist() == want_hits.tolist()
+        assert um[b].tolist() == (want_hits > 0).astype(int).tolist()
+        assert uc[b] == len({x for ac in targets[b] for x in ac})
+    # two targets share the mass: each gets (1 - 38 eps) / 2 with eps = e^-16 / (2 + 38 e^-16)
+    e = math.exp(-16.0)
+    np.testing.assert_allclose(pbar[0, 0, 3], 1.0 / (2 + 38 * e), rtol=1e-12)
+    np.testing.assert_allclose(pbar[0, 0, 5], e / (2 + 38 * e), rtol=1e-12)
+
+
+def test_lookahead_one_step_is_the_current_golden_and_union_grows_with_the_horizon():
+    B, T, Hq, N, k = 1, 6, 4, 80, 9
+    kv = rng.standard_normal((B, N, 512)).astype(np.float32)
+    q = rng.standard_normal((B, T, Hq, 512)).astype(np.float32)
+    ids, hits, um, uc, pbar = oracle.lookahead_golden(q, _kv(kv), 0.044, k)
+    # each step: the library softmax's head average, its top-k
+    for t in range(T):
+        x = float(np.float32(0.044)) * (q[0, t].astype(np.float64) @ kv[0].astype(np.float64).T)
+        ref = scipy.special.softmax(x, axis=-1).mean(0)
+        np.testing.assert_allclose(pbar[0, t], ref, rtol=1e-12)
+        assert ids[0, t].tolist() == sorted(np.argsort(-ref, kind="stable")[:k].tolist())
+    assert hits.sum() == T * k and k <= uc[0] <= min(N, T * k)
+    # the union of a prefix of the horizon is contained in the union of the whole horizon
+    _, h3, _, u3, _ = oracle.lookahead_golden(q[:, :3], _kv(kv), 0.044, k)
+    assert (h3 <= hits).all() and u3[0] <= uc[0]
