@@ -571,7 +571,20 @@ def offload(lit, W, dev, scale):
     keys = [W.layer_inputs(wl, l, dev).idx.k_idx for l in W.GATE_LAYERS]
     gl = [W.gate_layer(wl, l, kk, dev) for l, kk in zip(W.GATE_LAYERS, keys)]
     gate, gcnt = lit.lsa_gate(gl, 0.5)
-    del gl, keys
+    # the gate itself (a8): three layers' projections and entry scores
+    g0 = gl[0]
+    gws = lit.workspace(lit.load().lit_gate_workspace_bytes(3, wl.B, g0.w_proj.shape[0], g0.wq_a.shape[0], wl.N), dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        lit.lsa_gate(gl, 0.5, ws=gws)
+    e1.record()
+    torch.cuda.synchronize()
+    gate_s = e0.elapsed_time(e1) / 1e3 / 5
+    gate_bytes = sum(Ly.wq_a.numel() * 2 + Ly.wq_b.numel() * 2 + Ly.w_proj.numel() * 2 + Ly.k.numel() * 2
+                     + Ly.h.numel() * 4 for Ly in gl) + 2 * wl.B * wl.N
+    del gl, keys, gws
     L = W.layer_inputs(wl, 10, dev)
     # the pool holds the largest kept set (a first plan at full size counts them)
     _, pc, _ = lit.pool_plan(gate, wl.window, wl.N)
@@ -622,6 +635,8 @@ def offload(lit, W, dev, scale):
     resident_s = time_graph(gr, 20) / 20
     compact_s = time_graph(gcp, 20) / 20
     return {"sequences": wl.B, "entries": wl.N, "keep_frac": round(float(gcnt.float().mean().item()) / wl.N, 4),
+            "gate_us_3_layers": round(gate_s * 1e6, 1), "gate_hbm_frac": round(gate_bytes / gate_s / 1e9 / HBM_PEAK_GBS, 4),
+            "gate_us_per_step_amortized": round(gate_s * 1e6 / 64, 2),
             "pool_rows": C, "row_bytes": row_bytes, "fetch_bytes_per_layer": link_bytes,
             "fetch_us_per_layer": round(fetch_s * 1e6, 1), "link_GBs": round(link_bytes / fetch_s / 1e9, 2),
             "pinned_copy_GBs": round(link_bytes / copy_s / 1e9, 2),

@@ -313,7 +313,9 @@ lit_status lit_recall(const uint8_t* a, const uint8_t* m, int32_t B, int32_t N,
  * gate[b][n] = OR over layers of keep; gate_count[b] = number kept.
  * The decision is exact: the fp64 value of z in canonical order (h, then d
  * ascending; each product rounded before it is added) decides it.
- * layers : host array of n_layers (1..8) structs; threshold in (0,1).
+ * layers : host array of n_layers (1..8) structs; threshold in (0,1);
+ *          d_model and rank multiples of 64, at most 4096; the projection
+ *          matrices and keys 16-byte aligned.
  * Workspace: lit_gate_workspace_bytes(n_layers, B, H, rank, N) bytes. */
 size_t lit_gate_workspace_bytes(int32_t n_layers, int32_t B, int32_t H, int32_t rank, int32_t N);
 lit_status lit_lsa_gate(const lit_gate_layer* layers, int32_t n_layers, int32_t B, int32_t N,
