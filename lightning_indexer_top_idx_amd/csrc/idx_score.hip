@@ -336,6 +336,205 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   }
 }
 
+// Many queries per sequence (a prefill chunk): the scores are a [Q*H x 128] x
+// [128 x N] product followed by the weighted ReLU over each query's heads, far
+// above the matrix cores' ridge, so the work is arranged as a GEMM. Each wave
+// keeps two queries' 64 heads as A operands in registers for the whole launch;
+// the eight waves of a workgroup (16 queries) share 64-entry key tiles staged
+// in LDS, double-buffered, the next tile's loads in flight while the current
+// one is multiplied. Per 16-entry column block a wave reads the four K-steps'
+// B operands once and issues 2 x 16 MFMAs, so LDS supplies 1 KiB per 8 MFMAs.
+// Outputs and hints are those of idx_score_bf16_kernel for the same rows.
+constexpr int GM_WAVES = 8;                  // waves per workgroup
+constexpr int GM_QPW = 2;                    // queries per wave
+constexpr int GM_QPB = GM_WAVES * GM_QPW;    // queries per workgroup
+constexpr int GM_ET = 64;                    // entries per key tile
+constexpr int GM_KS = LIT_IDX_DIM + 8;       // bf16 per LDS key row (pad spreads banks)
+constexpr int GM_TILES_PER_CHUNK = CHUNK / GM_ET;
+
+__global__ __launch_bounds__(GM_WAVES * 64, 1) void idx_score_gemm_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
+    const uint8_t* __restrict__ allowed, const int32_t* __restrict__ lengths, int H, int N, int Q, int tiles_per_wg,
+    int nchunks, float* __restrict__ scores, float* __restrict__ hints, int hints_len) {
+  constexpr int MT = 4;  // head blocks of 16 (heads past H are zeros)
+  __shared__ __align__(16) uint16_t ks[2][GM_ET * GM_KS];
+  __shared__ float nmax_s[2][GM_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.z, qg = blockIdx.y;
+  const int ntiles = (N + GM_ET - 1) / GM_ET;
+  const int t0 = blockIdx.x * tiles_per_wg, t1 = min(ntiles, t0 + tiles_per_wg);
+  const uint16_t* kb = k + (size_t)b * N * LIT_IDX_DIM;
+  const uint8_t* ab = allowed ? allowed + (size_t)b * N : nullptr;
+  const int hq_off = nchunks + (N + LIT_HINT_GROUP - 1) / LIT_HINT_GROUP;
+
+  // this wave's queries: A operands (qi, mt, j), lane (c + 16 g) = head 16 mt + c, dims 8 g + 32 j .. +7
+  int rq[GM_QPW], nv[GM_QPW];
+  bool qlive[GM_QPW];
+  u32x4 A[GM_QPW][MT][4];
+  float wr[GM_QPW][MT][4];
+#pragma unroll
+  for (int qi = 0; qi < GM_QPW; qi++) {
+    const int jq = qg * GM_QPB + wid * GM_QPW + qi;
+    qlive[qi] = jq < Q;
+    rq[qi] = b * Q + min(jq, Q - 1);
+    nv[qi] = lengths && qlive[qi] ? lengths[rq[qi]] : N;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const int h = 16 * mt + c;
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        A[qi][mt][j] = h < H && qlive[qi] ? *(const u32x4*)(q + ((size_t)rq[qi] * H + h) * LIT_IDX_DIM + 8 * g + 32 * j)
+                                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int hw = 16 * mt + 4 * g + i;
+        wr[qi][mt][i] = hw < H && qlive[qi] ? w[(size_t)rq[qi] * H + hw] : 0.f;
+      }
+    }
+  }
+  // the query-side bound sums of each live query (first workgroup along the entries)
+  if (hints && blockIdx.x == 0) {
+#pragma unroll
+    for (int qi = 0; qi < GM_QPW; qi++) {
+      double qs = 0.0, as = 0.0;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        double ss = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const double lo = (double)bf16_lo(A[qi][mt][j][i]), hi = (double)bf16_hi(A[qi][mt][j][i]);
+            ss += lo * lo;
+            ss += hi * hi;
+          }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const int h = 16 * mt + c;
+        const double a = h < H && qlive[qi] ? fabs((double)w[(size_t)rq[qi] * H + h]) : 0.0;
+        qs += a * sqrt(ss);
+        as += a;
+      }
+      qs = wave_sum_f64_dpp(g == 0 ? qs : 0.0);
+      as = wave_sum_f64_dpp(g == 0 ? as : 0.0);
+      if (lane == 0 && qlive[qi]) {
+        uint32_t* u = reinterpret_cast<uint32_t*>(hints + (size_t)rq[qi] * hints_len + hq_off);
+        const uint64_t qb = (uint64_t)__double_as_longlong(qs), abb = (uint64_t)__double_as_longlong(as);
+        u[0] = (uint32_t)qb;
+        u[1] = (uint32_t)(qb >> 32);
+        u[2] = (uint32_t)abb;
+        u[3] = (uint32_t)(abb >> 32);
+      }
+    }
+  }
+
+  // key tile staging: thread tid takes entry tid / 8, dims 16 (tid % 8) .. +15
+  const int se = tid >> 3, sp = tid & 7;
+  auto load_tile = [&](int t, u32x4 (&r)[2]) {
+    const int e = min(t * GM_ET + se, N - 1);  // past N: row N-1 (in bounds; a real row keeps the norm bound valid)
+    const u32x4* src = (const u32x4*)(kb + (size_t)e * LIT_IDX_DIM + 16 * sp);
+    r[0] = src[0];
+    r[1] = src[1];
+  };
+  // Key-norm bounds: the largest squared norm of a 256-entry chunk, reduced
+  // when the chunk's last tile is staged and written (to every row of the
+  // workgroup) after the next barrier; two slots, as chunks alternate.
+  float cmax = 0.f;
+  int pend = -1;  // chunk whose maximum waits in nmax_s[pend & 1] (the same in every thread)
+  auto stage_tile = [&](int u, int buf, const u32x4 (&r)[2]) {
+    uint16_t* dst = &ks[buf][se * GM_KS + 16 * sp];
+    *(u32x4*)dst = r[0];
+    *(u32x4*)(dst + 8) = r[1];
+    float n2 = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float lo = bf16_lo(r[h2][i]), hi = bf16_hi(r[h2][i]);
+        n2 = fmaf(lo, lo, n2);
+        n2 = fmaf(hi, hi, n2);
+      }
+    n2 += __shfl_xor(n2, 1);
+    n2 += __shfl_xor(n2, 2);
+    n2 += __shfl_xor(n2, 4);
+    if (u % GM_TILES_PER_CHUNK == 0) cmax = 0.f;
+    cmax = fmaxf(cmax, n2);
+    if ((u + 1) % GM_TILES_PER_CHUNK == 0 || u + 1 == ntiles) {
+      const float m = wave_max(cmax);
+      const int ch = u / GM_TILES_PER_CHUNK;
+      if (lane == 0) nmax_s[ch & 1][wid] = m;
+      pend = ch;
+    }
+  };
+  auto flush_norm = [&]() {  // after a barrier
+    if (pend >= 0) {
+      if (hints && tid < GM_QPB && qg * GM_QPB + tid < Q) {
+        float m = nmax_s[pend & 1][0];
+#pragma unroll
+        for (int i = 1; i < GM_WAVES; i++) m = fmaxf(m, nmax_s[pend & 1][i]);
+        hints[((size_t)b * Q + qg * GM_QPB + tid) * hints_len + pend] = norm_bound(m);
+      }
+      pend = -1;
+    }
+  };
+  u32x4 raw[2];
+  if (t0 < t1) {
+    load_tile(t0, raw);
+    stage_tile(t0, 0, raw);
+  }
+  lds_barrier();
+  flush_norm();
+#pragma unroll 1
+  for (int t = t0; t < t1; t++) {
+    const int buf = (t - t0) & 1;
+    const bool more = t + 1 < t1;
+    if (more) load_tile(t + 1, raw);
+    const int tb = t * GM_ET;
+    // the B operands of column block cb + 1 are read while block cb multiplies
+    u32x4 kB[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) kB[0][j] = *(const u32x4*)&ks[buf][c * GM_KS + 8 * g + 32 * j];
+#pragma unroll
+    for (int cb = 0; cb < GM_ET / 16; cb++) {
+      if (cb + 1 < GM_ET / 16) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          kB[(cb + 1) & 1][j] = *(const u32x4*)&ks[buf][(16 * (cb + 1) + c) * GM_KS + 8 * g + 32 * j];
+      }
+      const int e = tb + 16 * cb + c;
+      const bool hidden = e >= N || (ab && ab[min(e, N - 1)] == 0);
+#pragma unroll
+      for (int qi = 0; qi < GM_QPW; qi++) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[qi][mt][j]),
+                                                              __builtin_bit_cast(bf16x8, kB[cb & 1][j]), acc[mt], 0,
+                                                              0, 0);
+        float v = weighted_relu<MT>(acc, wr[qi]);  // every lane of column c: entry e's score
+        if (hidden || e >= nv[qi]) v = -INFINITY;
+        if (qlive[qi] && g == 0 && e < N) scores[(size_t)rq[qi] * N + e] = v;
+        // the 16-entry group maximum along the row of 16 lanes (lane c = 15 ends with it)
+        constexpr uint32_t NEG_INF = 0xff800000u;
+        v = fmaxf(v, __uint_as_float(dpp_u32<0x111>(NEG_INF, __float_as_uint(v))));
+        v = fmaxf(v, __uint_as_float(dpp_u32<0x112>(NEG_INF, __float_as_uint(v))));
+        v = fmaxf(v, __uint_as_float(dpp_u32<0x114>(NEG_INF, __float_as_uint(v))));
+        v = fmaxf(v, __uint_as_float(dpp_u32<0x118>(NEG_INF, __float_as_uint(v))));
+        if (hints && qlive[qi] && lane == 15 && tb + 16 * cb < N)
+          hints[(size_t)rq[qi] * hints_len + nchunks + (tb + 16 * cb) / 16] = v;
+      }
+    }
+    if (more) stage_tile(t + 1, (t + 1 - t0) & 1, raw);
+    lds_barrier();
+    flush_norm();
+  }
+}
+
 // FP32 inputs: v_mfma_f32_16x16x4_f32, lane l holds A[l%16][l/16] and
 // B[l/16][l%16]; K-step j pairs lane group g with dim 32*g + j. One query (row
 // b of scores; its keys are those of sequence b / Q) per workgroup row.
@@ -525,7 +724,20 @@ static lit_status idx_score_rows(const lit_idx_in* in, int32_t Q, const int32_t*
   const int hl = lit_idx_hints_len(N);
   const int MT = (in->H + 15) / 16;
   hipStream_t hs = (hipStream_t)stream;
-  if (in->dtype == LIT_BF16) {
+  if (in->dtype == LIT_BF16 && Q >= GM_QPB) {
+    // many queries: the GEMM arrangement, 16 queries per workgroup, the entries
+    // split into ranges of whole chunks until about two workgroups per CU
+    const int qgs = (Q + GM_QPB - 1) / GM_QPB;
+    const int64_t rows = (int64_t)B * qgs;
+    if (qgs > 65535 || B > 65535) return fail(LIT_ERR_SHAPE, "%s: B=%d, Q=%d too large for the grid", who, B, Q);
+    const int splits = (int)std::max<int64_t>(1, std::min<int64_t>(nchunks, (512 + rows - 1) / rows));
+    const int chunks_per = (nchunks + splits - 1) / splits;
+    const int tiles_per = chunks_per * GM_TILES_PER_CHUNK;
+    const int ntiles = (int)cdiv(N, GM_ET);
+    dim3 grid((unsigned)cdiv(ntiles, tiles_per), (unsigned)qgs, (unsigned)B);
+    idx_score_gemm_kernel<<<grid, GM_WAVES * 64, 0, hs>>>((const uint16_t*)in->q, in->w, (const uint16_t*)in->k, allowed,
+                                                          lengths, in->H, N, Q, tiles_per, nchunks, scores, hints, hl);
+  } else if (in->dtype == LIT_BF16) {
     // Queries per workgroup: one for single queries; two for a pair of draft
     // tokens; four for many queries, where the key operands are reused the most.
     const int QW = Q == 1 ? 1 : (Q == 2 ? 2 : 4);

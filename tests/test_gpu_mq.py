@@ -61,7 +61,7 @@ def test_single_query_equals_lit_idx_score(dtype):
 
 
 @pytest.mark.parametrize("Q,B,N,causal", [(2, 3, 5003, False), (2, 2, 4100, True), (5, 2, 2000, True),
-                                          (9, 1, 1500, False)])
+                                          (9, 1, 1500, False), (37, 2, 1500, True), (16, 1, 2049, False)])
 def test_mq_scores_and_exact_topk_match_oracle(Q, B, N, causal):
     wl = W.CTX64K_B
     print(f"case mq Q={Q} B={B} N={N} causal={causal}", flush=True)
@@ -153,3 +153,29 @@ def test_prefill_chunk_sampled_rows():
         s64 = oracle.idx_score_mq(q[:, j:j + 1].cpu(), w[:, j:j + 1].cpu(), k.cpu(), lc[:, j:j + 1])
         rids, _, _ = oracle.topk_mq(s64, wl.k)
         assert np.array_equal(ic[0, j].numpy(), rids[0, 0]), j
+
+
+def test_many_query_arrangement_equals_few_query_arrangement():
+    # 32 queries take the GEMM arrangement (16 queries per workgroup, key tiles
+    # in LDS); 8 at a time take the key-streaming one. Both accumulate each head
+    # over the same four K-steps, so scores and group maxima agree bit for bit.
+    wl = W.CTX64K_B
+    print("case mq arrangements Q=32 vs 4 x 8", flush=True)
+    idx = W.mq_inputs(wl, 32, 9, "cuda", B=2, N=3001)
+    q, w, k = idx.q_idx, idx.w, idx.k_idx
+    lengths = W.causal_lengths(2, 32, 4 * 3001 - 40, "cuda")
+    s, h = lit.idx_score_mq(q, w, k, lengths)
+    nch, G = -(-3001 // 256), -(-3001 // 16)
+    for j0 in range(0, 32, 8):
+        sj, hj = lit.idx_score_mq(q[:, j0:j0 + 8].contiguous(), w[:, j0:j0 + 8].contiguous(), k,
+                                  lengths[:, j0:j0 + 8].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(s[:, j0:j0 + 8], sj)
+        assert torch.equal(h[:, j0:j0 + 8, nch:nch + G], hj[..., nch:nch + G])
+        # the query-side sums agree to their stated accuracy, the key-norm bounds bound the same norms
+        qa = h[:, j0:j0 + 8, nch + G:].contiguous().view(torch.float64)
+        qb = hj[..., nch + G:].contiguous().view(torch.float64)
+        assert torch.allclose(qa, qb, rtol=2.0 ** -40, atol=0)
+        kn = k.double().norm(dim=-1)
+        kn = torch.cat([kn, kn[:, -1:].expand(2, nch * 256 - 3001)], 1).view(2, nch, 256).amax(-1)
+        assert (h[:, j0:j0 + 8, :nch].double() >= kn[:, None]).all() and (hj[..., :nch].double() >= kn[:, None]).all()
