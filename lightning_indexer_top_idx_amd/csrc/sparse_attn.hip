@@ -585,6 +585,7 @@ constexpr int MH_RS = 520;         // bf16 per LDS row: 1040 B keeps rows 16-byt
 constexpr int MH_PS = MH_TR + 8;   // bf16 per LDS row of P (one head)
 constexpr int MH_TARGET = 256;     // workgroups aimed at: one per CU
 constexpr int MH_ROWS_CAP = 1152;  // rows of a selection slice resolved up front (a multiple of MH_TR)
+constexpr int MH_IDS_CACHE = 1024;  // ids copied to LDS up front (k_cap at most this; a multiple of 64)
 
 struct MhTile {
   uint16_t v[MH_TR * MH_RS];
@@ -788,6 +789,18 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   const int Hq = P.Hq;
   // the queries travel first, into the second tile buffer, while the row list is built
   mh_issue_q(P, b, hg, TB);
+  // The sequence's ids travel with them (all k_cap, so that their copy does not
+  // wait for the count), into the same buffer after the 16 query rows; the
+  // duplicate test and the row list then read LDS, and the count's load and
+  // the ids' copy are one round trip instead of three dependent ones.
+  int* ids_l = reinterpret_cast<int*>(TB.v + MH_HEADS * MH_RS);
+  const bool ids_cached = P.ids != nullptr && P.k_cap <= MH_IDS_CACHE;
+  if (ids_cached) {
+    const int32_t* src = P.ids + (size_t)b * P.k_cap;
+    for (int j0 = 64 * wid; j0 < P.k_cap; j0 += 64 * MH_WAVES)
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + min(j0 + lane, P.k_cap - 1)),
+                                       (__attribute__((address_space(3))) void*)(ids_l + j0), 4, 0, 0);
+  }
 
   RowList RL;
   RL.dense = P.ids == nullptr;
@@ -799,13 +812,15 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
     RL.Wc = 0;
     RL.total = P.N;
   } else {
-    RL.ids = P.ids + (size_t)b * P.k_cap;
+    RL.ids = ids_cached ? ids_l : P.ids + (size_t)b * P.k_cap;
     int c = P.count[b];
     c = c < 0 ? 0 : (c > P.k_cap ? P.k_cap : c);
     RL.c = c;
     RL.Wc = P.window;
     RL.total = c + P.window;
   }
+  if (ids_cached) wait_vm0();  // this wave's share of the ids (and queries) has landed
+  lds_barrier();               // ... and every wave's
   const int p0 = s * P.rows_per_split;
   const int p1 = min(RL.total, p0 + P.rows_per_split);
   if (!RL.dense && p1 > RL.c && RL.Wc > 0) {
