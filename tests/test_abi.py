@@ -142,3 +142,63 @@ def test_hints_length_layout(L):
     for n in (1, 15, 16, 17, 255, 256, 257, 16384, 125000):
         assert L.lit_idx_hints_len(n) == -(-n // 256) + -(-n // 16) + 4
     assert L.lit_idx_hints_len(0) == 0
+
+
+def test_gate_shape_limits(L):
+    p = ctypes.c_void_p
+    layers = (lit.GateLayerDesc * 1)(lit.GateLayerDesc(0x1000, 0x2000, 0x3000, 0x4000, 0x5000))
+    # d_model and rank must be multiples of 64 and at most 4096
+    assert L.lit_lsa_gate(layers, 1, 1, 100, 64, 4000, 2048, 0.5, p(0x6000), p(0x7000), p(0x8000), 1 << 30,
+                          None) == 2
+    assert L.lit_lsa_gate(layers, 1, 1, 100, 64, 4096, 8192, 0.5, p(0x6000), p(0x7000), p(0x8000), 1 << 30,
+                          None) == 2
+    # the projection matrices must be 16-byte aligned
+    mis = (lit.GateLayerDesc * 1)(lit.GateLayerDesc(0x1000, 0x2004, 0x3000, 0x4000, 0x5000))
+    assert L.lit_lsa_gate(mis, 1, 1, 100, 64, 4096, 2048, 0.5, p(0x6000), p(0x7000), p(0x8000), 1 << 30, None) == 3
+    # the workspace holds every layer's projections
+    assert L.lit_gate_workspace_bytes(3, 8, 64, 2048, 16384) == 3 * L.lit_gate_workspace_bytes(1, 8, 64, 2048, 16384)
+
+
+def test_multi_query_validation(L):
+    p = ctypes.c_void_p
+    d = lit.IdxIn(0x1000, 0x2000, 0x3000, 1, 64)
+    sc = p(0x4000)
+    assert L.lit_idx_score_mq(ctypes.byref(d), 0, None, None, 1, 100, sc, None, None) == 2
+    assert L.lit_idx_score_mq(ctypes.byref(d), 65537, None, None, 1, 100, sc, None, None) == 2
+    assert L.lit_idx_score_mq(ctypes.byref(d), 2, None, None, 1, 100, None, None, None) == 1
+    assert L.lit_idx_score_mq(ctypes.byref(d), 2, p(0x5002), None, 1, 100, sc, None, None) == 3  # lengths misaligned
+    assert L.lit_idx_score_mq(None, 2, None, None, 1, 100, sc, None, None) == 1
+    need = L.lit_topk_workspace_bytes(4, 100, 8)
+    assert L.lit_topk_select_mq(sc, 2, 0, 100, 8, None, None, p(0x6000), p(0x7000), None, p(0x8000), need, None) == 2
+    assert L.lit_topk_select_mq(sc, 2, 2, 100, 8, None, None, p(0x6000), p(0x7000), None, p(0x8000), need - 1,
+                                None) == 5
+    # exact mode needs the hints
+    assert L.lit_topk_select_mq(sc, 2, 2, 100, 8, ctypes.byref(d), None, p(0x6000), p(0x7000), None, p(0x8000), need,
+                                None) == 1
+
+
+def test_lookahead_validation(L):
+    p = ctypes.c_void_p
+    kv = lit.KVDesc(1, 100, 0x1000, None, None)
+    need = L.lit_lookahead_workspace_bytes(2, 8, 16, 100, 10)
+    assert need >= 2 * 8 * 16 * 100 * 8  # the fp64 logits
+    args = lambda T, q_dtype, ws_bytes: (p(0x2000), q_dtype, T, 16, ctypes.byref(kv), 2, 0.04, 10, None, None, None,
+                                         p(0x3000), None, p(0x4000), ws_bytes, None)
+    assert L.lit_lookahead_golden(*args(0, 1, need)) == 2
+    assert L.lit_lookahead_golden(*args(1025, 1, need)) == 2
+    assert L.lit_lookahead_golden(*args(8, 0, need)) == 4      # fp32 queries against bf16 rows
+    assert L.lit_lookahead_golden(*args(8, 1, need - 1)) == 5  # workspace too small
+    assert L.lit_lookahead_golden(None, 1, 8, 16, ctypes.byref(kv), 2, 0.04, 10, None, None, None, p(0x3000), None,
+                                  p(0x4000), need, None) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import json
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
