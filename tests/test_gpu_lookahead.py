@@ -78,3 +78,29 @@ def test_lookahead_single_step_equals_golden_topk():
     torch.cuda.synchronize()
     np.testing.assert_allclose(pbar[:, 0].cpu().numpy(), gpbar.cpu().numpy(), rtol=1e-12, atol=0)
     assert torch.equal(ids[:, 0], gids) and torch.equal(um, gmask) and torch.equal(uc, gcnt)
+
+
+def test_lookahead_full_size_sampled_steps():
+    # the benchmark's configuration: the gate workload's layer 10 (8 sequences x
+    # 16384 FP8 rows, 64 heads, top-1024) over a 64-step horizon; every
+    # sequence's union and hits must follow from its step sets, and sampled
+    # steps must equal the oracle's golden sets
+    wl = W.GATE64K
+    print("case lookahead full size gate64k T=64", flush=True)
+    L = W.layer_inputs(wl, 10, "cuda")
+    q = W.horizon_queries(L.q, W.TAU, 10, "cuda")
+    ids, hits, um, uc, _ = lit.lookahead_golden(q, L.kv, wl.k, SCALE)
+    torch.cuda.synchronize()
+    ic = ids.cpu().numpy()
+    assert (ic >= 0).all() and (np.diff(ic, axis=-1) > 0).all()  # k ascending ids per step
+    mine = np.zeros((wl.B, wl.N), np.int32)
+    for b in range(wl.B):
+        for t in range(W.TAU):
+            mine[b, ic[b, t]] += 1
+    assert np.array_equal(hits.cpu().numpy(), mine)
+    assert np.array_equal(uc.cpu().numpy(), (mine > 0).sum(-1))
+    for b, t in ((0, 0), (0, 63), (5, 31)):
+        qb = q[b:b + 1, t:t + 1].cpu()
+        kv = synth.KVRows("fp8", L.kv.data[b:b + 1].cpu(), L.kv.rope[b:b + 1].cpu(), L.kv.scale[b:b + 1].cpu())
+        rids, _, _, _, rp = oracle.lookahead_golden(qb, kv, SCALE, wl.k)
+        _assert_same_sets(ic[b:b + 1, t:t + 1], rids, rp, wl.k)
