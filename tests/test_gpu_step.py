@@ -102,3 +102,37 @@ def test_token_step_graph_replays_equal_eager():
     # and the layers against the oracle, after the replays
     for l in (0, 2, 3, 42):
         _check_layer(l, sched.layers[l])
+
+
+def test_token_step_full_size_sampled():
+    # the benchmark's 64K token step: 32 sequences, CSA layers over 16384
+    # entries (the timed workload's layers), HCA layers over 512 rows, SWA over
+    # 128, replayed from one graph; sampled (layer, sequence) pairs of each kind
+    # against the oracle
+    print("case token step full size T=65536 B=32", flush=True)
+    sched = _schedule(65536, 32)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        sched.run(torch.cuda.current_stream().cuda_stream)  # warm
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        sched.run(torch.cuda.current_stream().cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    for l, b in ((0, 3), (2, 0), (3, 7), (42, 31), (41, 30)):
+        Ly = sched.layers[l]
+        one = lambda x: x[b:b + 1].cpu()
+        if layer_kind(l) == "csa":
+            assert (Ly.count.cpu() == Ly.k).all()
+            q, w, k = Ly.L.idx.q_idx, Ly.L.idx.w, Ly.L.idx.k_idx
+            rids, rcnt, _ = oracle.topk(oracle.idx_score(one(q), one(w), one(k)), Ly.k)
+            assert np.array_equal(Ly.ids[b:b + 1].cpu().numpy(), rids), (l, b)
+            kv = type(Ly.L.kv)(Ly.L.kv.dtype, one(Ly.L.kv.data))
+            ref, _ = oracle.attend(one(Ly.L.q), kv, rids, rcnt, Ly.window, SCALE)
+        else:
+            kv = type(Ly.kv)(Ly.kv.dtype, one(Ly.kv.data))
+            ref, _ = oracle.attend(one(Ly.q), kv, None, None, 0, SCALE)
+        err = np.abs(Ly.out[b:b + 1].double().cpu().numpy() - ref).max(-1)
+        assert (err <= ATTN_TOL * np.abs(ref).max(-1)).all(), (l, b)
