@@ -838,7 +838,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   // positions 0 .. n-1 and the tile loop reads nothing but the tiles. Longer
   // slices are dense: their rows are their positions, computed per tile.
   const int nrows = max(p1 - p0, 0);
-  const bool all_rows = nrows <= MH_ROWS_CAP;
+  const bool all_rows = !RL.dense && nrows <= MH_ROWS_CAP;  // dense slices: rows are positions
   int n = nrows;  // attended rows of the slice
   if (all_rows) {
     constexpr int PER = (MH_ROWS_CAP + MH_THREADS - 1) / MH_THREADS;
@@ -863,6 +863,15 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
       rows_all[i] = p < p1 ? p : -1;
     }
   }
+  const size_t seq_rows = (size_t)b * P.N;
+  // (one LDS array, so that the compiler can tell its reads from the tile loads in flight)
+  auto tile_rows = [&](int tt) -> const int* { return rows_all + MH_TR * (all_rows ? tt : (tt & 3)); };
+  // a dense slice's first tile needs no row list: its loads go out now,
+  // alongside the queries'
+  if (!all_rows) {
+    lds_barrier();
+    if (0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
+  }
   // the queries as B operands, from the second tile buffer: K-step j, lane
   // (g, c16) holds dims 32j + 8g .. +7 of head c16 of the group
   wait_vm0();
@@ -871,10 +880,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
 #pragma unroll
   for (int j = 0; j < 16; j++) qreg[j] = *(const u32x4*)(TB.v + c16 * MH_RS + 32 * j + 8 * g);
   lds_barrier();
-  const size_t seq_rows = (size_t)b * P.N;
-  // (one LDS array, so that the compiler can tell its reads from the tile loads in flight)
-  auto tile_rows = [&](int tt) -> const int* { return rows_all + MH_TR * (all_rows ? tt : (tt & 3)); };
-  if (0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
+  if (all_rows && 0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
 
   MhState S;
 #pragma unroll
