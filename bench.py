@@ -314,10 +314,11 @@ def token_step(W, dev, scale, csa, T, hca_kv=None, reps=10):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def oracle_rate(fn, gpu_s_per_unit, unit, budget_s=4.0, max_units=50):
-    """The CPU oracle (one thread, as it stands) on a bounded sample of a
-    secondary measurement's work: fn() does one unit; it is run until about
-    budget_s has passed. Returned beside the GPU's seconds per unit."""
+def cpu_baseline_rate(fn, gpu_s_per_unit, unit, sample, budget_s=4.0, max_units=50):
+    """The cpu_baseline leg of a secondary measurement: the CPU oracle (one
+    thread, as it stands) on a bounded sample of the same work. fn() does one
+    unit and is run until about budget_s has passed. Returned as units/s, with
+    the GPU's units/s beside it."""
     import oracle
 
     oracle.build()
@@ -329,8 +330,8 @@ def oracle_rate(fn, gpu_s_per_unit, unit, budget_s=4.0, max_units=50):
         el = time.perf_counter() - t0
         if el >= budget_s or n >= max_units:
             break
-    return {"unit": unit, "oracle_s_per_unit": round(el / n, 5), "gpu_s_per_unit": gpu_s_per_unit,
-            "units_timed": n, "threads": 1, "kind": "oracle"}
+    return {"value": round(n / el, 3), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{sample}, {n} runs in {el:.1f} s", "gpu_value": round(1.0 / gpu_s_per_unit, 1)}
 
 
 def mtp(lit, W, dev, layers, paths, wl):
@@ -432,14 +433,15 @@ def prefill(lit, W, dev):
     import oracle
 
     qc, wc, kc, lc = q[:, :1].cpu(), w[:, :1].cpu(), k.cpu(), lengths[:, :1].cpu()
-    orc = oracle_rate(lambda: oracle.topk_mq(oracle.idx_score_mq(qc, wc, kc, lc), wl.k), (ts + tt) / Q,
-                      "one query row (fp64 scores over 16384 entries, exact top-512)")
+    orc = cpu_baseline_rate(lambda: oracle.topk_mq(oracle.idx_score_mq(qc, wc, kc, lc), wl.k), (ts + tt) / Q,
+                            "query rows/s", "query 0 of the chunk (fp64 scores over its 15873 visible entries, "
+                            "exact top-512)")
     del gs, gt
     torch.cuda.empty_cache()
     return {"queries": Q, "entries": N, "score_us": round(ts * 1e6, 1), "score_TFLOPs": round(tflops, 1),
             "mfma_bf16_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "topk_us": round(tt * 1e6, 1),
             "topk_us_per_query": round(tt * 1e6 / Q, 3), "tokens_per_s_indexer": round(Q / (ts + tt), 1),
-            "all_counts_k": ok, "oracle_baseline": orc}
+            "all_counts_k": ok, "cpu_baseline": orc}
 
 
 FP64_PEAK_TFLOPS = 78.6
@@ -507,10 +509,11 @@ def lookahead(lit, W, dev, scale):
 
     kv0 = synth.KVRows("fp8", L.kv.data[:1].cpu(), L.kv.rope[:1].cpu(), L.kv.scale[:1].cpu())
     q00 = q[:1, :1].cpu()
-    orc = oracle_rate(lambda: oracle.lookahead_golden(q00, kv0, scale, k), total_s / (B * T),
-                      "one horizon step of one sequence (dense fp64 softmax over 16384 FP8 rows, 64 heads, top-1024)")
+    orc = cpu_baseline_rate(lambda: oracle.lookahead_golden(q00, kv0, scale, k), total_s / (B * T),
+                            "horizon steps/s", "one horizon step of sequence 0 (dense fp64 softmax over 16384 FP8 "
+                            "rows, 64 heads, top-1024)")
     res = {"sequences": B, "entries": N, "horizon": T, "heads": Hq, "k": k,
-           "call_ms": round(total_s * 1e3, 2), "logits_flops": flops, "oracle_baseline": orc,
+           "call_ms": round(total_s * 1e3, 2), "logits_flops": flops, "cpu_baseline": orc,
            "call_TFLOPs_fp64": round(flops / total_s / 1e12, 1),
            "call_fp64_mfma_frac": round(flops / total_s / 1e12 / FP64_PEAK_TFLOPS, 4),
            "union_mean": round(float(uc.float().mean().item()), 1),
@@ -619,8 +622,8 @@ def offload(lit, W, dev, scale):
 
     one = [{"h": Ly.h[:1].cpu(), "wq_a": Ly.wq_a.cpu(), "wq_b": Ly.wq_b.cpu(), "w_proj": Ly.w_proj.cpu(),
             "k": Ly.k[:1].cpu()} for Ly in gl]
-    gate_orc = oracle_rate(lambda: oracle.lsa_gate(one, 0.5), gate_s / wl.B,
-                           "one sequence's gate over layers 10/12/20 (fp64 projections, 16384 entries)")
+    gate_orc = cpu_baseline_rate(lambda: oracle.lsa_gate(one, 0.5), gate_s / wl.B, "sequences/s",
+                                 "sequence 0's gate over layers 10/12/20 (fp64 projections, 16384 entries)")
     del gl, keys, gws
     L = W.layer_inputs(wl, 10, dev)
     # the pool holds the largest kept set (a first plan at full size counts them)
@@ -673,7 +676,7 @@ def offload(lit, W, dev, scale):
     compact_s = time_graph(gcp, 20) / 20
     return {"sequences": wl.B, "entries": wl.N, "keep_frac": round(float(gcnt.float().mean().item()) / wl.N, 4),
             "gate_us_3_layers": round(gate_s * 1e6, 1), "gate_hbm_frac": round(gate_bytes / gate_s / 1e9 / HBM_PEAK_GBS, 4),
-            "gate_us_per_step_amortized": round(gate_s * 1e6 / 64, 2), "gate_oracle_baseline": gate_orc,
+            "gate_us_per_step_amortized": round(gate_s * 1e6 / 64, 2), "gate_cpu_baseline": gate_orc,
             "pool_rows": C, "row_bytes": row_bytes, "fetch_bytes_per_layer": link_bytes,
             "fetch_us_per_layer": round(fetch_s * 1e6, 1), "link_GBs": round(link_bytes / fetch_s / 1e9, 2),
             "pinned_copy_GBs": round(link_bytes / copy_s / 1e9, 2),
