@@ -9,15 +9,17 @@
 // section "為什麼你沒辦法靠量化 KV 再省記憶體" - the non-RoPE dims are stored as
 // E4M3 in groups of 64 with a power-of-two scale, the RoPE dims as BF16.
 //
-// Layout of the work: a workgroup owns one sequence and a contiguous slice of
-// the row list (ids first, then the window rows not already selected). Per tile
-// of 32 rows it gathers the rows into LDS (1 KiB coalesced loads; FP8 rows are
-// dequantised exactly to BF16 on the way), then each wave (16 query heads)
-// computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = rows from LDS, B = the
-// wave's queries held in registers), updates an online softmax in fp32, and
-// accumulates O += P V with the same instruction (A = P straight from the S^T
-// accumulators, no transpose; B = V read from LDS). Slices of one sequence are
-// merged by a log-sum-exp combine.
+// Layout of the work: a workgroup of four waves owns 16 query heads of one
+// sequence and a contiguous slice of its row list (ids first, then the window
+// rows not already selected; a dense layer's rows are simply its positions).
+// Tiles of 64 rows arrive in LDS by direct-to-LDS loads, double-buffered, the
+// next tile's loads issued during the current tile's scores; FP8 rows arrive
+// raw and are widened to BF16 in place (exactly: an E4M3 value times a power of
+// two). Each wave scores 16 rows against the 16 heads (S^T = K Q^T on
+// v_mfma_f32_16x16x32_bf16, the queries in registers), the online softmax runs
+// in fp32, and O^T += V^T P^T uses the same instruction (A = V^T read from LDS
+// with transposed reads, B = P straight from the S^T accumulators). Slices of
+// one sequence are merged by a log-sum-exp combine kernel.
 #include <algorithm>
 #include <math.h>
 
@@ -27,7 +29,6 @@ namespace lit {
 namespace {
 
 constexpr int TILE = 32;
-constexpr int ROW_STRIDE = 520;  // bf16 per LDS row: 512 + 8 pad (spreads banks)
 constexpr int PART = 516;        // floats per partial: O[512], m, l, 2 pad
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -50,21 +51,6 @@ struct AttnParams {
   float* lse;
   float* part;  // [B][splits][Hq][PART] when splits > 1
 };
-
-// Exact E4M3FN -> BF16 with a power-of-two scale; the product has at most four
-// significant bits, so dropping the low half of the fp32 is exact.
-__device__ __forceinline__ uint32_t e4m3_bf16(uint32_t byte, float sc) {
-  const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
-  float v;
-  if (e == 15u && m == 7u)
-    v = __uint_as_float(0x7fc00000u);
-  else if (e == 0u)
-    v = (float)m * 0x1p-9f;
-  else
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  v = __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24)) * sc;
-  return __float_as_uint(v) >> 16;
-}
 
 __device__ __forceinline__ float e8m0_f32(uint32_t b) {
   if (b == 255u) return __uint_as_float(0x7fc00000u);
@@ -96,21 +82,6 @@ struct RowList {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TR = 64;            // rows per tile: wave w scores rows 16w .. 16w+15
-constexpr int HG_HEADS = 16;      // query heads per workgroup
-constexpr int TARGET_WGS = 512;   // two workgroups per CU
-constexpr int DW = LIT_KV_DIM / 4;  // output dims owned by one wave
-
-struct AttnLds {
-  uint16_t tile[TR * ROW_STRIDE];      // gathered rows, row-major (BF16)
-  uint16_t pbuf[HG_HEADS * (TR + 8)];  // softmax weights P[head][row] (BF16)
-  int rows[2][TR];
-  uint32_t dup[LIT_MAX_WINDOW / 32];
-  float wmax[4][HG_HEADS];  // per-wave tile maxima
-  float wl[4][HG_HEADS];    // per-wave running sums
-};
-constexpr int PSTRIDE = TR + 8;
-
 // Row slices and head groups -> workgroups: the head groups of one slice get
 // workgroup ids equal modulo 8, i.e. the same XCD, so its L2 serves the rows
 // to all of them.
@@ -134,284 +105,6 @@ __device__ __forceinline__ void unit_seq(int u, int B, int splits, int* b, int* 
   } else {
     *b = u / splits;
     *s = u % splits;
-  }
-}
-
-// Register-staged gather of one 64-row tile: BF16 rows are 64 chunks of 16 B;
-// FP8 rows 28 chunks of 16 E4M3 bytes (dequantised on the store) + 8 chunks of
-// RoPE BF16.
-template <int KVT>
-struct TileRegs {
-  static constexpr int CHUNKS = KVT == 0 ? 64 : 36;
-  static constexpr int UNITS = TR * CHUNKS;
-  static constexpr int PER = (UNITS + 255) / 256;
-  u32x4 v[PER];
-  uint8_t sc[PER];
-};
-
-template <int KVT>
-__device__ __forceinline__ void tile_load(const AttnParams& P, size_t seq_rows, const int* rows, TileRegs<KVT>& R) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < TileRegs<KVT>::PER; i++) {
-    const int u = tid + 256 * i;
-    const int r = u / TileRegs<KVT>::CHUNKS, ch = u % TileRegs<KVT>::CHUNKS;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    uint8_t sc = 127;
-    const int row = u < TileRegs<KVT>::UNITS ? rows[r] : -1;
-    if (row >= 0) {
-      const size_t rr = seq_rows + row;
-      if (KVT == 0) {
-        v = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)P.data + rr * LIT_KV_DIM + ch * 8));
-      } else if (ch < 28) {
-        v = __builtin_nontemporal_load((const u32x4*)(P.data + rr * LIT_KV_FP8_DIMS + ch * 16));
-        sc = P.scale[rr * LIT_KV_SCALE_STRIDE + (ch >> 2)];
-      } else {
-        v = __builtin_nontemporal_load((const u32x4*)(P.rope + rr * LIT_KV_ROPE_DIMS + (ch - 28) * 8));
-      }
-    }
-    R.v[i] = v;
-    R.sc[i] = sc;
-  }
-}
-
-template <int KVT>
-__device__ __forceinline__ void tile_store(uint16_t* tile, const TileRegs<KVT>& R) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < TileRegs<KVT>::PER; i++) {
-    const int u = tid + 256 * i;
-    if (u >= TileRegs<KVT>::UNITS) continue;
-    const int r = u / TileRegs<KVT>::CHUNKS, ch = u % TileRegs<KVT>::CHUNKS;
-    if (KVT == 0) {
-      *(u32x4*)(tile + r * ROW_STRIDE + ch * 8) = R.v[i];
-    } else if (ch < 28) {
-      const float sc = e8m0_f32(R.sc[i]);
-      u32x4 o0, o1;
-#pragma unroll
-      for (int w = 0; w < 4; w++) {
-        const uint32_t wv = R.v[i][w];
-        const uint32_t h0 = e4m3_bf16(wv & 255u, sc), h1 = e4m3_bf16((wv >> 8) & 255u, sc);
-        const uint32_t h2 = e4m3_bf16((wv >> 16) & 255u, sc), h3 = e4m3_bf16(wv >> 24, sc);
-        if (w < 2) {
-          o0[2 * w] = h0 | (h1 << 16);
-          o0[2 * w + 1] = h2 | (h3 << 16);
-        } else {
-          o1[2 * (w - 2)] = h0 | (h1 << 16);
-          o1[2 * (w - 2) + 1] = h2 | (h3 << 16);
-        }
-      }
-      *(u32x4*)(tile + r * ROW_STRIDE + ch * 16) = o0;
-      *(u32x4*)(tile + r * ROW_STRIDE + ch * 16 + 8) = o1;
-    } else {
-      *(u32x4*)(tile + r * ROW_STRIDE + LIT_KV_FP8_DIMS + (ch - 28) * 8) = R.v[i];
-    }
-  }
-}
-
-// One workgroup: one sequence, one group of 16 query heads, one slice of the
-// row list. Per 64-row tile, wave w scores rows 16w..16w+15 for the 16 heads
-// (S^T = K Q^T on v_mfma_f32_16x16x32_bf16), the waves agree on each head's
-// running max through LDS, and each wave accumulates its own quarter of the
-// output dims, O[:, 128w .. 128w+127] += P V, over all 64 rows
-// (v_mfma_f32_16x16x16_bf16, P from LDS). The next tile is in flight in
-// registers during the math.
-template <int KVT>
-__global__ __launch_bounds__(256, 2) void attn_hg_kernel(AttnParams P) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  AttnLds& L = *reinterpret_cast<AttnLds*>(smem);
-  const int HG = (P.Hq + HG_HEADS - 1) / HG_HEADS;
-  const int U = P.B * P.splits;
-  int u, hg;
-  if (!decode_unit(blockIdx.x, HG, U, &u, &hg)) return;
-  int b, s;
-  unit_seq(u, P.B, P.splits, &b, &s);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int Hq = P.Hq;
-
-  RowList RL;
-  RL.dense = P.ids == nullptr;
-  RL.N = P.N;
-  RL.dup = L.dup;
-  if (RL.dense) {
-    RL.ids = nullptr;
-    RL.c = 0;
-    RL.Wc = 0;
-    RL.total = P.N;
-  } else {
-    RL.ids = P.ids + (size_t)b * P.k_cap;
-    int c = P.count[b];
-    c = c < 0 ? 0 : (c > P.k_cap ? P.k_cap : c);
-    RL.c = c;
-    RL.Wc = P.window;
-    RL.total = c + P.window;
-  }
-  const int p0 = s * P.rows_per_split;
-  const int p1 = min(RL.total, p0 + P.rows_per_split);
-  if (!RL.dense && p1 > RL.c && RL.Wc > 0) {
-    for (int i = tid; i < (RL.Wc + 31) / 32; i += 256) L.dup[i] = 0u;
-    lds_barrier();
-    const int lo = P.N - RL.Wc;
-    for (int j = tid; j < RL.c; j += 256) {
-      const int id = RL.ids[j];
-      if (id >= lo && id < P.N) atomicOr(&L.dup[(id - lo) >> 5], 1u << ((id - lo) & 31));
-    }
-  }
-  lds_barrier();
-
-  // the 16 heads as B operands of S^T = K Q^T: K-step j, lane (c16 + 16 g) holds dims 8g + 32j .. +7
-  const int head = hg * HG_HEADS + c16;
-  u32x4 qreg[16];
-  {
-    const uint16_t* qh = P.q + ((size_t)b * Hq + head) * LIT_KV_DIM;
-#pragma unroll
-    for (int j = 0; j < 16; j++) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < Hq) v = *(const u32x4*)(qh + 8 * g + 32 * j);
-      qreg[j] = v;
-    }
-  }
-  // O[head 4g+i][dim 128 wid + 16 nt + c16]
-  f32x4 o[DW / 16];
-#pragma unroll
-  for (int nt = 0; nt < DW / 16; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_col = -INFINITY;  // running max of head c16 (every wave holds the same)
-  float l_run = 0.f;        // this wave's share of head c16's sum (its rows, lane group g)
-  const size_t seq_rows = (size_t)b * P.N;
-
-  int cur = 0;
-  int fnext = 0;  // ids read of the next tile's rows (threads < TR), one tile ahead
-  if (p0 < p1) {
-    if (tid < TR) {
-      L.rows[0][tid] = (p0 + tid < p1) ? RL.row(p0 + tid) : -1;
-      fnext = RL.fetch(p0 + TR + tid);
-    }
-    lds_barrier();
-    TileRegs<KVT> R;
-    tile_load<KVT>(P, seq_rows, L.rows[0], R);
-    tile_store<KVT>(L.tile, R);
-    lds_barrier();
-  }
-  // Nothing issued before the loop (queries, ids, first tile) may still be in
-  // flight at its head; otherwise the first use of the queries inside the loop
-  // would wait for every load, the next tile's prefetch included.
-  __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll 1
-  for (int t0 = p0; t0 < p1; t0 += TR) {
-    const int nxt = cur ^ 1;
-    const bool more = t0 + TR < p1;
-    if (tid < TR) {
-      if (more) L.rows[nxt][tid] = (t0 + TR + tid < p1) ? RL.resolve(t0 + TR + tid, fnext) : -1;
-      fnext = RL.fetch(t0 + 2 * TR + tid);  // lands with the tile loads below
-    }
-    lds_barrier();
-    TileRegs<KVT> R;
-    if (more) tile_load<KVT>(P, seq_rows, L.rows[nxt], R);  // the next tile is in flight during the math
-
-    // S^T for this wave's 16 rows: lane (g, c16) gets rows 16w + 4g + i of head c16
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t* krow = L.tile + (16 * wid + c16) * ROW_STRIDE + 8 * g;
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const u32x4 a0 = *(const u32x4*)(krow + 32 * j), a1 = *(const u32x4*)(krow + 32 * (j + 1));
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, qreg[j]),
-                                                       acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                       __builtin_bit_cast(bf16x8, qreg[j + 1]), acc1, 0, 0, 0);
-      }
-    }
-    float x[4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const bool valid = L.rows[cur][16 * wid + 4 * g + i] >= 0;
-      x[i] = valid ? (acc0[i] + acc1[i]) * P.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (g == 0) L.wmax[wid][c16] = tmax;
-    lds_barrier();
-    const float t_all = fmaxf(fmaxf(L.wmax[0][c16], L.wmax[1][c16]), fmaxf(L.wmax[2][c16], L.wmax[3][c16]));
-    const float m_new = fmaxf(m_col, t_all);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_col - m_use);  // head c16
-    m_col = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float pv = exp2f(x[i] - m_use);
-      psum += pv;
-      const uint32_t bits = __float_as_uint(pv);
-      L.pbuf[c16 * PSTRIDE + 16 * wid + 4 * g + i] = (uint16_t)((bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16);
-    }
-    l_run = l_run * alpha + psum;
-    lds_barrier();
-    // rescale this wave's O rows (heads 4g+i) when some running max moved
-    if (__any(alpha != 1.0f)) {
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) al[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int nt = 0; nt < DW / 16; nt++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) o[nt][i] *= al[i];
-    }
-    // O[:, dims of wave w] += P[16 x 64] V[64 x 128]: A = P (head c16, rows 16kb + 4g .. +3)
-#pragma unroll
-    for (int kb = 0; kb < TR / 16; kb++) {
-      const s16x4 pa = *(const s16x4*)(L.pbuf + c16 * PSTRIDE + 16 * kb + 4 * g);
-      const uint16_t* vr = L.tile + (16 * kb + 4 * g) * ROW_STRIDE + DW * wid + c16;
-#pragma unroll
-      for (int nt = 0; nt < DW / 16; nt++) {
-        const int d = 16 * nt;
-        u32x2 vb;
-        vb[0] = (uint32_t)vr[d] | ((uint32_t)vr[ROW_STRIDE + d] << 16);
-        vb[1] = (uint32_t)vr[2 * ROW_STRIDE + d] | ((uint32_t)vr[3 * ROW_STRIDE + d] << 16);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, vb), o[nt], 0, 0, 0);
-      }
-    }
-    lds_barrier();
-    if (more) tile_store<KVT>(L.tile, R);
-    cur = nxt;
-    lds_barrier();
-  }
-
-  // l per head: the four lane groups of every wave
-  float l_w = l_run;
-  l_w += __shfl_xor(l_w, 16);
-  l_w += __shfl_xor(l_w, 32);
-  if (g == 0) L.wl[wid][c16] = l_w;
-  lds_barrier();
-  float Ls[4], Ms[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int hh = 4 * g + i;
-    Ls[i] = (L.wl[0][hh] + L.wl[1][hh]) + (L.wl[2][hh] + L.wl[3][hh]);
-    Ms[i] = __shfl(m_col, hh);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int h = hg * HG_HEADS + 4 * g + i;
-    if (h >= Hq) continue;
-    if (P.splits == 1) {
-      float* oh = P.out + ((size_t)b * Hq + h) * LIT_KV_DIM + DW * wid;
-      const float inv = Ls[i] > 0.f ? 1.f / Ls[i] : 0.f;
-#pragma unroll
-      for (int nt = 0; nt < DW / 16; nt++) oh[16 * nt + c16] = o[nt][i] * inv;
-      if (P.lse && wid == 0 && c16 == 0)
-        P.lse[(size_t)b * Hq + h] = Ls[i] > 0.f ? Ms[i] * LN2 + logf(Ls[i]) : -INFINITY;
-    } else {
-      float* ph = P.part + (((size_t)b * P.splits + s) * Hq + h) * PART;
-#pragma unroll
-      for (int nt = 0; nt < DW / 16; nt++) ph[DW * wid + 16 * nt + c16] = o[nt][i];
-      if (wid == 0 && c16 == 0) {
-        ph[512] = Ms[i];
-        ph[513] = Ls[i];
-      }
-    }
   }
 }
 
@@ -629,27 +322,81 @@ __device__ __forceinline__ void mh_row_ids(const int* rws, int (&rid)[MH_ROWS_PE
 
 // One tile row (slot i of this wave's share) straight into LDS. A row that is
 // not attended (-1) loads row 0 instead: its weight is 0, and a finite value
-// keeps 0 * value = 0.
+// keeps 0 * value = 0. BF16 rows: 64 lanes x 16 B, the row as it is. FP8 rows
+// arrive raw in the row's slot, widened to BF16 in place before use (see
+// mh_widen_fp8): bytes 0..447 the E4M3 dims (lanes 0-27), 448..575 the BF16
+// RoPE dims (lanes 28-35), 576..583 the E8M0 scale bytes (a second, 4-byte
+// load by lanes 0-1); the other lanes load nothing.
+template <bool FP8>
 __device__ __forceinline__ void mh_issue_row(const AttnParams& P, size_t seq_rows, int r, int i, MhTile& T) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const size_t rr = seq_rows + (size_t)(r >= 0 ? r : 0);
-  const uint16_t* src = (const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane;
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)(T.v + (MH_ROWS_PER_WAVE * wid + i) * MH_RS),
-                                   16, 0, 0);
+  uint16_t* dst = T.v + (MH_ROWS_PER_WAVE * wid + i) * MH_RS;
+  if (!FP8) {
+    const uint16_t* src = (const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane;
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  } else {
+    if (lane < 36) {
+      const uint8_t* src = lane < 28 ? P.data + rr * LIT_KV_FP8_DIMS + 16 * lane
+                                     : reinterpret_cast<const uint8_t*>(P.rope + rr * LIT_KV_ROPE_DIMS) + 16 * (lane - 28);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+    if (lane < 2)
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(P.scale + rr * LIT_KV_SCALE_STRIDE + 4 * lane),
+          (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(dst) + 576), 4, 0, 0);
+  }
+}
+
+// A tile of raw FP8 rows widened to the BF16 row layout in place: thread t
+// takes row t / 4, quarter t % 4 (112 E4M3 dims and 16 RoPE dims), reads its
+// bytes into registers, and after a barrier writes them back as BF16. An
+// E4M3 value times its group's power of two is exact in BF16, which the scaled
+// conversion instruction produces (the same values the FP8 decode gives).
+__device__ __forceinline__ void mh_widen_fp8(MhTile& T) {
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, qq = tid & 3;
+  uint8_t* row = reinterpret_cast<uint8_t*>(T.v + r * MH_RS);
+  u32x4 f[7], ro[2];
+#pragma unroll
+  for (int i = 0; i < 7; i++) f[i] = *(const u32x4*)(row + 112 * qq + 16 * i);
+#pragma unroll
+  for (int i = 0; i < 2; i++) ro[i] = *(const u32x4*)(row + 448 + 32 * qq + 16 * i);
+  const u32x2 sc = *(const u32x2*)(row + 576);
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < 14; j++) {
+    const int d0 = 112 * qq + 8 * j;  // dims d0 .. d0+7 share one 64-dim scale group
+    const int grp = d0 >> 6;
+    const float scl = e8m0_f32((sc[grp >> 2] >> (8 * (grp & 3))) & 255u);
+    const uint32_t w0 = f[j >> 1][2 * (j & 1)], w1 = f[j >> 1][2 * (j & 1) + 1];
+    u32x4 o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scl, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scl, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scl, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scl, true));
+    *(u32x4*)(row + 2 * d0) = o;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++) *(u32x4*)(row + 2 * LIT_KV_FP8_DIMS + 32 * qq + 16 * i) = ro[i];
+  lds_barrier();
 }
 
 // This wave's share of a whole tile.
+template <bool FP8>
 __device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, const int* rws, MhTile& T) {
   int rid[MH_ROWS_PER_WAVE];
   mh_row_ids(rws, rid);
 #pragma unroll
-  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) mh_issue_row(P, seq_rows, rid[i], i, T);
+  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) mh_issue_row<FP8>(P, seq_rows, rid[i], i, T);
 }
 
 // nvalid: rows 0 .. nvalid-1 of the tile are attended, the rest are padding.
 // When NT is given, this wave's loads of that next tile (rows nrid) are issued
 // one per K-step of the scores, so that their issue overlaps the multiplies.
+template <bool FP8>
 __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, int nvalid, const u32x4 (&qreg)[16],
                                         MhState& S, float (*smax)[16], uint16_t* pbuf, MhTile* NT, size_t seq_rows,
                                         const int (&nrid)[MH_ROWS_PER_WAVE]) {
@@ -669,7 +416,7 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
   for (int j = 0; j < 16; j++) {
     const u32x4 ka = kq[j % KD];
     if (j + KD < 16) kq[j % KD] = *(const u32x4*)(krow + 32 * (j + KD));
-    if (NT) mh_issue_row(P, seq_rows, nrid[j], j, *NT);
+    if (NT) mh_issue_row<FP8>(P, seq_rows, nrid[j], j, *NT);
     acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qreg[j]),
                                                          acc[j & 3], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -771,6 +518,7 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   __shared__ MhTile TA, TB;
   __shared__ __align__(16) uint16_t pbuf[MH_HEADS * MH_PS];
@@ -870,7 +618,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   // alongside the queries'
   if (!all_rows) {
     lds_barrier();
-    if (0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
+    if (0 < n) mh_issue<FP8>(P, seq_rows, tile_rows(0), TA);
   }
   // the queries as B operands, from the second tile buffer: K-step j, lane
   // (g, c16) holds dims 32j + 8g .. +7 of head c16 of the group
@@ -880,7 +628,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
 #pragma unroll
   for (int j = 0; j < 16; j++) qreg[j] = *(const u32x4*)(TB.v + c16 * MH_RS + 32 * j + 8 * g);
   lds_barrier();
-  if (all_rows && 0 < n) mh_issue(P, seq_rows, tile_rows(0), TA);
+  if (all_rows && 0 < n) mh_issue<FP8>(P, seq_rows, tile_rows(0), TA);
 
   MhState S;
 #pragma unroll
@@ -904,10 +652,11 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
         rows_all[MH_TR * ((tt + 2) & 3) + tid] = p < p1 ? p : -1;
       }
       lds_barrier();
+      if (FP8) mh_widen_fp8(ab == 0 ? TA : TB);
       const bool more = q0 + MH_TR < n;
       int nrid[MH_ROWS_PER_WAVE];
       if (more) mh_row_ids(tile_rows(tt + 1), nrid);
-      mh_tile(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf, more ? (ab == 0 ? &TB : &TA) : nullptr, seq_rows,
+      mh_tile<FP8>(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf, more ? (ab == 0 ? &TB : &TA) : nullptr, seq_rows,
               nrid);
       // no barrier here: the next tile's opening barrier orders this tile's
       // reads of its buffer, pbuf and smax before anything rewrites them
@@ -965,16 +714,6 @@ void plan_mh(int B, int HG, int rows_max, bool sparse, int* splits, int* rows_pe
   *rows_per_split = tiles_per * MH_TR;
 }
 
-void plan_splits(int B, int HG, int rows_max, int* splits, int* rows_per_split) {
-  const int tiles = std::max(1, (rows_max + TR - 1) / TR);
-  const int want = std::max(1, (TARGET_WGS + B * HG - 1) / (B * HG));
-  int s = std::min(tiles, want);
-  const int tiles_per = (tiles + s - 1) / s;
-  s = (tiles + tiles_per - 1) / tiles_per;
-  *splits = s;
-  *rows_per_split = tiles_per * TR;
-}
-
 }  // namespace
 }  // namespace lit
 
@@ -982,14 +721,13 @@ using namespace lit;
 
 extern "C" size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
-  int s1, s2, rps;
-  plan_splits(B, (Hq + HG_HEADS - 1) / HG_HEADS, N + LIT_MAX_WINDOW, &s1, &rps);
+  // the most slices any call on these shapes can plan: a selection of up to
+  // N + LIT_MAX_WINDOW rows, or all N rows read densely
+  int s2, s3, rps;
   const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
   plan_mh(B, HGm, N + LIT_MAX_WINDOW, true, &s2, &rps);
-  int s3;
   plan_mh(B, HGm, N, false, &s3, &rps);
-  s2 = std::max(s2, s3);
-  const int s = std::max(s1, s2);
+  const int s = std::max(s2, s3);
   if (s <= 1) return 256;
   return round_up((size_t)B * s * Hq * PART * sizeof(float), 256);
 }
@@ -1021,8 +759,9 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   } else {
     return fail(LIT_ERR_DTYPE, "%s: kv dtype %d unsupported", who, (int)kv->dtype);
   }
-  if (!aligned(q, 16) || !aligned(kv->data, 16) || (kv->rope && !aligned(kv->rope, 16)) || !aligned(out, 16))
-    return fail(LIT_ERR_ALIGN, "%s: q, kv->data, kv->rope and out must be 16-byte aligned", who);
+  if (!aligned(q, 16) || !aligned(kv->data, 16) || (kv->rope && !aligned(kv->rope, 16)) || !aligned(out, 16) ||
+      (kv->scale && !aligned(kv->scale, 4)))
+    return fail(LIT_ERR_ALIGN, "%s: q, kv->data, kv->rope and out must be 16-byte aligned, kv->scale 4-byte", who);
   hipStream_t st = (hipStream_t)stream;
   if (kv->dtype == LIT_F32) {
     attn_f32_kernel<<<dim3((unsigned)(B * Hq)), dim3(256), 0, st>>>((const float*)q, Hq, (const float*)kv->data, N,
@@ -1032,12 +771,8 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   }
   const int rows_max = ids ? (k_cap + Wc) : N;
   AttnParams P;
-  const int HG = (Hq + HG_HEADS - 1) / HG_HEADS;
-  const bool mh = kv->dtype == LIT_BF16;  // BF16 rows: the direct-to-LDS kernel
-  if (mh)
-    plan_mh(B, (Hq + MH_HEADS - 1) / MH_HEADS, rows_max, ids != nullptr, &P.splits, &P.rows_per_split);
-  else
-    plan_splits(B, HG, rows_max, &P.splits, &P.rows_per_split);
+  const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
+  plan_mh(B, HGm, rows_max, ids != nullptr, &P.splits, &P.rows_per_split);
   P.B = B;
   if (P.splits > 1) {
     const size_t need = round_up((size_t)B * P.splits * Hq * PART * sizeof(float), 256);
@@ -1061,16 +796,11 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   P.lse = lse;
   P.part = (float*)ws;
   const int U = B * P.splits;
-  dim3 grid((unsigned)(((U + 7) / 8) * 8 * HG));
-  const size_t lds = sizeof(AttnLds);
-  if (mh) {
-    const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
-    attn_mh_kernel<<<dim3((unsigned)(((U + 7) / 8) * 8 * HGm)), dim3(MH_THREADS), 0, st>>>(P);
-  } else {
-    lit_status ls = allow_lds((const void*)attn_hg_kernel<1>, lds, who);
-    if (ls != LIT_OK) return ls;
-    attn_hg_kernel<1><<<grid, 256, lds, st>>>(P);
-  }
+  const dim3 grid((unsigned)(((U + 7) / 8) * 8 * HGm));
+  if (kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16)
+    attn_mh_kernel<true><<<grid, dim3(MH_THREADS), 0, st>>>(P);
+  else
+    attn_mh_kernel<false><<<grid, dim3(MH_THREADS), 0, st>>>(P);
   LIT_CHECK_LAUNCH(who);
   if (P.splits > 1) {
     launch_combine((const float*)ws, B, P.splits, Hq, out, lse, st);
