@@ -120,7 +120,8 @@ typedef struct {
  * MQA attention. Host struct, read during the call only.
  *   LIT_F32 / LIT_BF16: data = [B][N][512], 16-B aligned; rope, scale unused.
  *   LIT_FP8E4M3_G64_ROPE_BF16: data = [B][N][448] E4M3 bytes (16-B aligned),
- *     rope = [B][N][64] BF16 (16-B aligned), scale = [B][N][8] E8M0 bytes (byte 7 unused). */
+ *     rope = [B][N][64] BF16 (16-B aligned), scale = [B][N][8] E8M0 bytes (byte 7
+ *     unused; 4-B aligned). */
 typedef struct {
   lit_dtype dtype;
   int32_t n_rows; /* N */
@@ -214,7 +215,7 @@ lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k,
  *          every row (then count and window are ignored).
  * window : 0..LIT_MAX_WINDOW, clamped to N.
  * out    : [B][Hq][512] fp32 output (16-byte aligned); lse: [B][Hq] fp32 output or NULL.
- * q, kv->data and kv->rope must be 16-byte aligned. Errors: LIT_ERR_NULL,
+ * q, kv->data and kv->rope must be 16-byte aligned, kv->scale 4-byte. Errors: LIT_ERR_NULL,
  * LIT_ERR_SHAPE (B, Hq outside 1..64, window), LIT_ERR_DTYPE (unsupported row
  * or query dtype), LIT_ERR_ALIGN, LIT_ERR_WORKSPACE.
  * An empty R (count 0 and window 0) gives out = 0 and lse = -inf.

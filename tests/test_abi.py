@@ -99,6 +99,10 @@ def test_attention_validation(L):
     kvm = lit.KVDesc(1, 1000, 0x1004, None, None)
     assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kvm), 1, None, None, 0, 0, 0.04, p(0x2000), None,
                                     None, 0, None) == 3
+    # FP8 scale bytes read four at a time: a scale array off a 4-byte boundary is refused
+    kv8m = lit.KVDesc(2, 1000, 0x1000, 0x8000, 0x9002)
+    assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv8m), 1, None, None, 0, 0, 0.04, p(0x2000), None,
+                                    None, 0, None) == 3
     # many sequences split the rows: the workspace is required
     assert L.lit_attn_workspace_bytes(4, 64, 125000) > 256
     assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04, p(0x2000), None,
