@@ -28,7 +28,6 @@
 namespace lit {
 namespace {
 
-constexpr int TILE = 32;
 constexpr int PART = 516;        // floats per partial: O[512], m, l, 2 pad
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
