@@ -290,6 +290,45 @@ def test_fp8_rows_attention():
     assert_attn_close(out, ref)
 
 
+def _fp8_rows_wide_exponents(B, N, seed):
+    # FP8 rows whose 64-dim groups span scale exponents from 2^-14 to 2^3, with
+    # every 7th group all zero (scale byte 127, zero codes) and every 11th row's
+    # RoPE part zero: the widening must be exact for each scale
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(B, N, 7, 64, generator=g)
+    x = x * torch.exp2(torch.randint(-14, 4, (B, N, 7, 1), generator=g).float())
+    x.view(-1, 64)[::7] = 0
+    codes, sc = synth.fp8_encode(x.view(B, N, 448))
+    rope = torch.randn(B, N, 64, generator=g).to(torch.bfloat16)
+    rope[:, ::11] = 0
+    return synth.KVRows("fp8", codes, rope.contiguous(), sc)
+
+
+def test_fp8_rows_dense_ragged_and_sparse_with_window():
+    B, N, Hq = 3, 3001, 64
+    kv = _fp8_rows_wide_exponents(B, N, 21)
+    assert (kv.scale[..., :7] == 127).any() and (kv.scale[..., :7] < 127 - 10).any()
+    q = synth.make_q(B, Hq, "bf16", torch.Generator().manual_seed(22), "cpu")
+    # dense: every row (47 tiles of 64, the last one 57 rows)
+    out, lse = lit.sparse_attn_decode(q.cuda(), kv_dev(kv), None, None, 0, SCALE)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attend(q, kv, None, None, 0, SCALE)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(lse.double().cpu().numpy(), rlse, atol=2e-3, rtol=0)
+    # sparse: counts below the cap, ids inside the window (counted once), an empty selection
+    ids = np.full((B, 300), -1, np.int32)
+    ids[0, :300] = np.arange(0, 3000, 10)
+    ids[1, :40] = np.arange(2961, 3001)
+    ids[2, :0] = 0
+    cnt = np.array([300, 40, 0], np.int32)
+    out, lse = lit.sparse_attn_decode(q.cuda(), kv_dev(kv), torch.from_numpy(ids).cuda(),
+                                      torch.from_numpy(cnt).cuda(), 128, SCALE)
+    torch.cuda.synchronize()
+    ref, rlse = oracle.attend(q, kv, ids, cnt, 128, SCALE)
+    assert_attn_close(out, ref)
+    np.testing.assert_allclose(lse.double().cpu().numpy(), rlse, atol=2e-3, rtol=0)
+
+
 # ---------------------------------------------------------------- a6 / a7 / a9
 
 
