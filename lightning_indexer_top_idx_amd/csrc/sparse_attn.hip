@@ -108,12 +108,22 @@ __device__ __forceinline__ void unit_seq(int u, int B, int splits, int* b, int* 
 }
 
 // Log-sum-exp merge of the row slices of one (sequence, head): 128 threads,
-// four dims each. Up to SM slices are merged per pass; every load of a pass
-// (each slice's m, l and four partial dims) is requested before any is used.
+// four dims each. When the batch is a multiple of 8 the workgroups of sequence b
+// sit on XCD b % 8, where its slices wrote their partials. Up to SM slices are
+// merged per pass; every load of a pass (each slice's m, l and four partial
+// dims) is requested before any is used.
 template <int SM>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int splits, int Hq,
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int B, int splits, int Hq,
                                                            float* __restrict__ out, float* __restrict__ lse) {
-  const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d4 = threadIdx.x;
+  const int x = blockIdx.x, d4 = threadIdx.x;
+  int b, h;
+  if (B % 8 == 0) {
+    b = ((x >> 3) / Hq) * 8 + (x & 7);
+    h = (x >> 3) % Hq;
+  } else {
+    b = x / Hq;
+    h = x % Hq;
+  }
   const float* base = part + ((size_t)b * splits * Hq + h) * PART;
   const size_t stride = (size_t)Hq * PART;
   float M = -INFINITY, L = 0.f;
@@ -155,13 +165,13 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 void launch_combine(const float* part, int B, int splits, int Hq, float* out, float* lse, hipStream_t st) {
   const dim3 grid((unsigned)(B * Hq)), block(128);
   if (splits <= 2)
-    attn_combine_kernel<2><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+    attn_combine_kernel<2><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
   else if (splits <= 4)
-    attn_combine_kernel<4><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+    attn_combine_kernel<4><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
   else if (splits <= 8)
-    attn_combine_kernel<8><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+    attn_combine_kernel<8><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
   else
-    attn_combine_kernel<16><<<grid, block, 0, st>>>(part, splits, Hq, out, lse);
+    attn_combine_kernel<16><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
 }
 
 // FP32 rows and queries: one workgroup per (sequence, head), fp32 VALU with an
