@@ -1321,9 +1321,22 @@ __device__ void full_path(const TopkParams& P, FullLds& L, int b) {
   if (tid == 0) P.count[b] = out_base;
 }
 
+// Workgroup -> score row. Rows kq*s .. kq*s + kq-1 belong to sequence s; when
+// the sequences are a multiple of 8, every row of sequence s runs on XCD s % 8
+// (workgroup id mod 8). The scoring call writes a sequence's rows there when
+// one of its units covers all the sequence's queries (one query, or the two of
+// a draft step), so the selection finds them in that XCD's L2. With kq = 1 this
+// is the identity.
+__device__ __forceinline__ int block_row(const TopkParams& P) {
+  const int x = blockIdx.x;
+  if ((gridDim.x / P.kq) % 8 != 0) return x;
+  const int t = x >> 3;
+  return ((t / P.kq) * 8 + (x & 7)) * P.kq + t % P.kq;
+}
+
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int b = blockIdx.x;
+  const int b = block_row(P);
   if (P.hints && P.N <= GM_CAP * GROUP) {
     if (fast_path(P, *reinterpret_cast<FastLds*>(smem), b)) return;
     __syncthreads();
@@ -1341,7 +1354,7 @@ __device__ __noinline__ void full_path_call(TopkParams P, int b) {
 template <bool BF16>
 __global__ __launch_bounds__(TK_THREADS) void topk_small_kernel(TopkParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int b = blockIdx.x;
+  const int b = block_row(P);
   if (small_path<BF16>(P, *reinterpret_cast<SmallLds*>(smem), b)) return;
   __syncthreads();
   full_path_call(P, b);

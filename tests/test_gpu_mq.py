@@ -61,7 +61,8 @@ def test_single_query_equals_lit_idx_score(dtype):
 
 
 @pytest.mark.parametrize("Q,B,N,causal", [(2, 3, 5003, False), (2, 2, 4100, True), (5, 2, 2000, True),
-                                          (9, 1, 1500, False), (37, 2, 1500, True), (16, 1, 2049, False)])
+                                          (9, 1, 1500, False), (37, 2, 1500, True), (16, 1, 2049, False),
+                                          (2, 8, 1500, True), (3, 16, 700, False)])
 def test_mq_scores_and_exact_topk_match_oracle(Q, B, N, causal):
     wl = W.CTX64K_B
     print(f"case mq Q={Q} B={B} N={N} causal={causal}", flush=True)
