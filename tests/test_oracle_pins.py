@@ -629,3 +629,65 @@ def test_lookahead_one_step_is_the_current_golden_and_union_grows_with_the_horiz
     # the union of a prefix of the horizon is contained in the union of the whole horizon
     _, h3, _, u3, _ = oracle.lookahead_golden(q[:, :3], _kv(kv), 0.044, k)
     assert (h3 <= hits).all() and u3[0] <= uc[0]
+
+
+# ---------------------------------------------------------------- the chained step
+
+
+def _decode_tiny_job(k, window):
+    """Inputs of tests/golden/decode_tiny.json: the score_tiny indexer, three
+    marker rows and two hand-chosen attention heads plus one random head."""
+    _, q, w, kk = _tiny_from_fixture()
+    rows = np.zeros((3, 512), np.float32)
+    for r in range(3):
+        rows[r, 0], rows[r, 1], rows[r, 2 + r] = r, 1.0, 1.0
+    qa = np.zeros((3, 512), np.float32)
+    qa[1, 0] = 1.0
+    qa[2] = rng.standard_normal(512).astype(np.float32)
+    return {"q_idx": q[0], "w": w[0], "k_idx": kk[0], "k": k, "q": qa, "kv_dtype": oracle.F32, "data": rows,
+            "window": window, "scale_f": math.log(2.0)}, rows, qa
+
+
+def test_decode_query_hand_worked_chain():
+    fx = json.load(open(os.path.join(GOLDEN, "decode_tiny.json")))
+    ln = {"ln 2": math.log(2), "ln 3": math.log(3), "ln 6": math.log(6), "ln 7": math.log(7)}
+    frac = {"10/7": 10 / 7, "5/3": 5 / 3, "2/3": 2 / 3}
+    for case in fx["cases"]:
+        job, rows, qa = _decode_tiny_job(case["k"], case["window"])
+        (c, ids, out, lse), = oracle.decode_queries([job])
+        assert c == case["count"], case["work"]
+        assert ids.tolist() == case["ids"], case["work"]
+        # head 0: uniform weights over R; head 1: weights proportional to 2^r
+        np.testing.assert_allclose(out[0, 2:5], case["head0_weights"], rtol=0, atol=1e-15)
+        w1 = np.array(case["head1_weights_unnormalised"], np.float64)
+        np.testing.assert_allclose(out[1, 2:5], w1 / w1.sum(), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(out[1, 0], frac[case["head1_dim0"]], rtol=1e-14)
+        np.testing.assert_allclose(out[:2, 1], 1.0, rtol=1e-15)
+        np.testing.assert_allclose(lse[:2], [ln[s] for s in case["lse"]], rtol=1e-14)
+        # every head against the library softmax over the hand-listed rows
+        x = math.log(2.0) * (qa.astype(np.float64) @ rows[case["rows"]].astype(np.float64).T)
+        ref = scipy.special.softmax(x, axis=-1) @ rows[case["rows"]].astype(np.float64)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse, scipy.special.logsumexp(x, axis=-1), rtol=1e-13)
+
+
+def test_decode_query_equals_the_three_steps():
+    # the chain's wiring: the same count, ids and attention as score -> topk ->
+    # attend called one by one, for counts below and at k and windows past N
+    g = torch.Generator().manual_seed(21)
+    sc = float(np.float32(1.0 / math.sqrt(512)))  # the attention call takes its scale as fp32
+    for N, k, window in ((50, 8, 5), (50, 80, 7), (30, 10, 40)):
+        idx = synth.make_indexer(1, N, 4, "bf16", g, "cpu", planted_count=3)
+        kv = synth.make_kv(1, N, "bf16", g, "cpu")
+        q = synth.make_q(1, 3, "bf16", g, "cpu")
+        job = {"q_idx": oracle.np_of(idx.q_idx)[0], "w": oracle.np_of(idx.w)[0], "k_idx": oracle.np_of(idx.k_idx)[0],
+               "k": k, "q": oracle.np_of(q)[0], "kv_dtype": oracle.BF16, "data": oracle.np_of(kv.data)[0],
+               "window": window, "scale_f": sc}
+        (c, ids, out, lse), = oracle.decode_queries([job])
+        s = oracle.idx_score(idx.q_idx, idx.w, idx.k_idx)
+        rids, rc, _ = oracle.topk(s, k)
+        rout, rlse = oracle.attend(q, kv, rids, rc, window, sc)
+        assert c == rc[0] == min(k, N)
+        np.testing.assert_array_equal(ids, rids[0])
+        np.testing.assert_array_equal(out, rout[0])
+        np.testing.assert_array_equal(lse, rlse[0])
