@@ -51,6 +51,7 @@ class Workload:
     planted: Tuple = ("frac", 0.02)  # ("count", n) | ("frac", f) | ("uniform", lo, hi)
     alpha: float = 0.4
     hca_N: int = 0
+    shared_plant: bool = False  # one set of planted positions per sequence, shared by its layers
 
     def planted_spec(self, g, device):
         kind = self.planted[0]
@@ -69,7 +70,8 @@ CTX64K_B = Workload("ctx64k_b", 2, 32, csa_entries(65536), 64, 512, 128, 64, "bf
                     planted=("uniform", 0.01, 0.05))
 CTX500K = Workload("ctx500k", 3, 4, csa_entries(500000), 64, 512, 128, 64, "bf16", "bf16",
                    planted=("frac", 0.005), hca_N=hca_entries(500000))
-GATE64K = Workload("gate64k", 4, 8, csa_entries(65536), 64, 1024, 128, 64, "bf16", "fp8", layers=21)
+GATE64K = Workload("gate64k", 4, 8, csa_entries(65536), 64, 1024, 128, 64, "bf16", "fp8", layers=21,
+                   shared_plant=True)
 
 ALL = {w.name: w for w in (TINY, CTX64K, CTX64K_B, CTX500K, GATE64K)}
 
@@ -86,6 +88,8 @@ def layer_inputs(wl: Workload, layer: int = 0, device="cpu", B: Optional[int] = 
     """Inputs of one layer of a workload (B and N may be shrunk for tests)."""
     B = wl.B if B is None else B
     N = wl.N if N is None else N
+    if wl.shared_plant and planted_positions is None:
+        planted_positions = shared_planted(wl, device, B, N)
     if wl.cid == 0:
         g = torch.Generator(device=device)
         g.manual_seed(0)
@@ -113,11 +117,13 @@ def hca_inputs(wl: Workload, device="cpu", B: Optional[int] = None) -> Tuple[tor
 
 def shared_planted(wl: Workload, device="cpu", B: Optional[int] = None, N: Optional[int] = None):
     """Planted positions shared by all layers of a sequence (relevance belongs to
-    the context, not to a layer)."""
+    the context, not to a layer; with positions drawn per layer no entry would
+    be relevant in enough layers to win the cross-layer vote). The fraction is
+    the workload's planted fraction; sequence b's positions do not depend on B."""
     B = wl.B if B is None else B
     N = wl.N if N is None else N
     g = synth.generator(device, wl.cid, 999)
-    cnt = int(round(0.02 * N))
+    cnt = int(round(wl.planted[1] * N))
     return [torch.randperm(N, generator=g, device=device)[:cnt].sort().values for _ in range(B)]
 
 
