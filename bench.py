@@ -16,9 +16,10 @@ the eager result) and replayed. Besides the headline line the JSON carries:
   others       : the whole attention step of a token (2 SWA + 21 CSA + 20
                  HCA layers) at 64K and 500K, the 64K batch-1 latency, the
                  500K batch-4 step (distinct layers rotated so every replay
-                 streams from HBM), and the LSA cold-pool fetch at the gate
-                 workload's shapes.
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only lookahead|prefill|offload]
+                 streams from HBM), the LSA cold-pool fetch, the lookahead
+                 golden and the recall chain (gate, gated and native top-1024,
+                 vote labels) at the gate workload's shapes.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only lookahead|prefill|offload|recall]
 """
 from __future__ import annotations
 
@@ -109,8 +110,31 @@ def stored_traffic(workload):
         return None
 
 
-def cpu_baseline(layers, wl, k, window, scale, budget_s, max_queries, threads, gpu_paths):
-    """The oracle, as it stands, on a bounded sample of the same queries."""
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_share():
+    """Host threads the oracle may use: the process's CPU affinity, capped at
+    the CPU share a one-GPU job is given (OMP_NUM_THREADS when set, else 16)."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "16"))
+    except ValueError:
+        share = 16
+    return max(1, min(aff, share)), aff
+
+
+def cpu_baseline(layers, wl, k, window, scale, budget_s, max_queries, threads, gpu_paths, single_s=None):
+    """The oracle, as it stands, on a bounded sample of the same queries: on
+    `threads` host threads (the value) and on one thread (single_core)."""
     import numpy as np
     import oracle
 
@@ -133,15 +157,28 @@ def cpu_baseline(layers, wl, k, window, scale, budget_s, max_queries, threads, g
         oracle.decode_queries(jobs, threads=threads)
         done += len(jobs)
         elapsed += time.perf_counter() - t1
+    # one thread: whole queries until about single_s has passed
+    single_s = budget_s / 2 if single_s is None else single_s
+    n1, t1 = 0, time.perf_counter()
+    while True:
+        oracle.decode_queries([jobs[n1 % len(jobs)]], threads=1)
+        n1 += 1
+        e1 = time.perf_counter() - t1
+        if e1 >= single_s:
+            break
     ids_ok, worst = True, 0.0
     for (l, b), (c, rids, rout, _) in zip(keys, res):
         P = gpu_paths[l]
         ids_ok &= bool(np.array_equal(P.ids[b].cpu().numpy(), rids))
         o = P.out[b].double().cpu().numpy()
         worst = max(worst, float((np.abs(o - rout).max(-1) / np.abs(rout).max(-1)).max()))
+    share, aff = cpu_share()
     return {"value": done / elapsed, "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(jobs)} distinct queries of the timed workload (one sequence per layer), "
                       f"score+exact top-{k}+attention in fp64 C, {done} query runs in {elapsed:.1f} s",
+            "single_core": {"value": n1 / e1, "unit": "queries/s", "cores": 1,
+                            "sample": f"{n1} query runs of the same sample in {e1:.1f} s"},
+            "cpu_model": cpu_model(), "affinity_cores": aff,
             "parity_on_sample": {"ids_bit_exact": ids_ok, "attn_max_rel_err": worst}}
 
 
@@ -155,7 +192,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["lookahead", "prefill", "offload"],
+    ap.add_argument("--only", choices=["lookahead", "prefill", "offload", "recall"],
                     help="run one secondary measurement alone and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -187,7 +224,7 @@ def main():
     scale = 1.0 / math.sqrt(512)
     if args.only:
         fn = {"lookahead": lookahead, "prefill": lambda lit, W, dev, scale: prefill(lit, W, dev),
-              "offload": offload}[args.only]
+              "offload": offload, "recall": gate_recall}[args.only]
         print(json.dumps({args.only: fn(lit, W, dev, scale)}))
         return
     wl = W.CTX64K_B
@@ -204,6 +241,8 @@ def main():
     # eager reference, then the captured step; every replay must match it
     step(torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
+    # a negative count would mean a violated rounding bound (nothing selected)
+    assert all(bool((P.count == wl.k).all()) for P in paths), "a sequence selected fewer than k entries"
     ref_ids = [P.ids.clone() for P in paths]
     ref_out = [P.out.clone() for P in paths]
     g = capture(step)
@@ -237,7 +276,9 @@ def main():
     score_bytes = idx_score_bytes_per_query(wl.N, wl.H) * wl.B
     achieved = score_bytes / launch_s / 1e9
     traffic = stored_traffic(wl.name)
-    roofline = {"bound": "hbm", "kernel": "idx_score (indexer scores, MFMA bf16)", "achieved": round(achieved, 1),
+    roofline = {"bound": "hbm", "kernel": "idx_score (indexer scores, MFMA bf16)",
+                "scope": "this kernel alone; the whole path's fraction is path_roofline.frac",
+                "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "avg_launch_us": round(launch_s * 1e6, 2),
                 "algorithmic_bytes_per_launch": score_bytes}
@@ -258,7 +299,7 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        threads = min(16, len(os.sched_getaffinity(0)))
+        threads, _ = cpu_share()
         print(f"[bench] CPU oracle on {threads} threads", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(layers, wl, wl.k, wl.window, scale, args.cpu_seconds, wl.layers,
                                            threads, paths)
@@ -584,6 +625,40 @@ def others(lit, W, dev, scale):
     res["prefill_chunk_indexer"] = prefill(lit, W, dev)
     print("[bench] lookahead golden", file=sys.stderr, flush=True)
     res["lookahead_golden_gate64k"] = lookahead(lit, W, dev, scale)
+    print("[bench] gate-stress recall chain", file=sys.stderr, flush=True)
+    res["gate64k_recall"] = gate_recall(lit, W, dev, scale)
+    return res
+
+
+def gate_recall(lit, W, dev, scale):
+    """The gate-stress workload's reported figures: 8 sequences x 16384 entries,
+    FP8 rows, top-1024 over the 21 CSA layers; the gate of layers 10/12/20
+    (d_model 4096, rank 2048), the native and the gated exact top-1024 of every
+    layer, the vote labels (top-p 0.6, at least 3 of 21 layers) from the
+    indexer logits (R1) and from dense attention (R2), and the recalls of the
+    gated selection against each label set and against the native selection.
+    Synthetic inputs: the planted entries are aligned with the index queries
+    only, so R1 labels follow the indexer and R2 labels (dense attention over
+    unplanted rows) do not; these recalls describe the inputs, not the model."""
+    import torch
+    from lightning_indexer_top_idx_amd import labels
+
+    wl = W.GATE64K
+    keys = [W.layer_inputs(wl, l, dev).idx.k_idx for l in W.GATE_LAYERS]
+    gl = [W.gate_layer(wl, l, kk, dev) for l, kk in zip(W.GATE_LAYERS, keys)]
+    del keys
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r = labels.run_chain([(lambda l=l: W.layer_inputs(wl, l, dev)) for l in W.CSA_LAYERS], gl, wl.k, scale=scale)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    res = {"sequences": wl.B, "entries": wl.N, "layers": len(W.CSA_LAYERS), "k": wl.k,
+           "gate_layers": list(W.GATE_LAYERS), "top_p": 0.6, "min_votes": 3}
+    res.update(labels.summary(r, wl.N))
+    res["chain_s_with_input_generation"] = round(el, 2)
+    res["data"] = "synthetic: recalls describe the generated inputs, not the model's"
+    del r, gl
+    torch.cuda.empty_cache()
     return res
 
 

@@ -102,6 +102,8 @@ def summary(r: RecallChain, N: int) -> Dict[str, object]:
         g = r.gold_count[src].double()  # [B]
         ok = g > 0
         out[f"gold_count_{src}"] = [int(x) for x in r.gold_count[src].tolist()]
+        # each layer's top-p set size, averaged (the votes sum to the sets' sizes)
+        out[f"topp_set_mean_{src}"] = round(float(r.votes[src].double().sum().item()) / (len(r.x[src]) * len(g)), 1)
         out[f"gold_empty_sequences_{src}"] = int((~ok).sum().item())
         if ok.any():
             for who in ("gated", "native"):
