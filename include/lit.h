@@ -7,6 +7,7 @@
  *   lit_idx_score        score every compressed entry with the 128-dim index keys
  *   lit_topk_select      keep the k best entries (lower index wins ties)
  *   lit_sparse_attn_decode  MQA attention over the kept rows plus the SWA window
+ *   lit_sparse_attn_decode_noalloc  the same without a workspace argument
  *   lit_golden_topk      dense "golden" attention and its top-k (measurement)
  *   lit_golden_topp_vote top-p 0.6 per layer, then a cross-layer vote (labels)
  *   lit_lookahead_golden the golden sets of the next T steps and their union
@@ -41,7 +42,9 @@
  *   - The caller owns every buffer. The library allocates no device memory;
  *     scratch space comes from a caller-provided workspace whose size is given
  *     by the matching *_workspace_bytes() query. Workspace contents need no
- *     initialisation and are not meaningful after a call.
+ *     initialisation and are not meaningful after a call. The one exception is
+ *     lit_sparse_attn_decode_noalloc, whose scratch is a fixed device array the
+ *     library holds on each GPU (see that call).
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *   - Calls that overlap on one stream are ordered; calls on different streams
  *     that share an output or a workspace race.
@@ -226,6 +229,25 @@ lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, int32_t Hq, 
                                   int32_t k_cap, int32_t window, float scale,
                                   float* out, float* lse, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/* ---- allocation-free attention ------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same call
+ * as lit_sparse_attn_decode (same arguments, same results bit for bit) without
+ * the workspace: the partial results of its row slices go to a scratch array the
+ * library holds on each GPU it runs on, LIT_ATTN_SCRATCH_BYTES bytes, kept until
+ * the process ends. The call itself allocates nothing. A call whose plan needs
+ * more partial results than the array holds returns LIT_ERR_WORKSPACE and
+ * enqueues nothing (lit_attn_workspace_bytes(B, Hq, N) bounds the need; plans of
+ * at most 64 sequence-slices of 64 heads always fit). Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents (nothing in it
+ * needs to start at zero): calls on one stream are ordered, calls that overlap
+ * on one GPU (other streams, other threads) race. LIT_ERR_LAUNCH when no device
+ * is current or the array cannot be found on it. */
+#define LIT_ATTN_SCRATCH_BYTES (16u << 20)
+lit_status lit_sparse_attn_decode_noalloc(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,
+                                          int32_t B, const int32_t* ids, const int32_t* count, int32_t k_cap,
+                                          int32_t window, float scale, float* out, float* lse, void* stream);
 
 /* ---- a6: dense golden top-k ---------------------------------------------------
  * [FMEN] "Act 3": golden = what the model attends to under an unmasked softmax

@@ -8,7 +8,7 @@ HIP kernels; there is no fallback: if the library is not built, every call
 raises.
 
 Functions (same names as the C entry points, without the lit_ prefix):
-  idx_score, topk_select, sparse_attn_decode, golden_topk, golden_topp_vote,
+  idx_score, topk_select, sparse_attn_decode, sparse_attn_decode_noalloc, golden_topk, golden_topp_vote,
   idx_score_exact, recall, lsa_gate, pool_plan, pool_gather, pool_remap_ids.
 """
 from __future__ import annotations
@@ -32,7 +32,7 @@ _STATUS = {0: "LIT_OK", 1: "LIT_ERR_NULL", 2: "LIT_ERR_SHAPE", 3: "LIT_ERR_ALIGN
 
 EXPORTS = [
     "lit_abi_version", "lit_last_error", "lit_idx_hints_len", "lit_idx_score", "lit_topk_workspace_bytes", "lit_topk_select",
-    "lit_attn_workspace_bytes", "lit_sparse_attn_decode", "lit_golden_workspace_bytes", "lit_golden_topk",
+    "lit_attn_workspace_bytes", "lit_sparse_attn_decode", "lit_sparse_attn_decode_noalloc", "lit_golden_workspace_bytes", "lit_golden_topk",
     "lit_topp_workspace_bytes", "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall",
     "lit_gate_workspace_bytes", "lit_lsa_gate", "lit_pool_plan", "lit_pool_gather", "lit_pool_remap_ids",
     "lit_idx_score_mq", "lit_topk_select_mq", "lit_lookahead_workspace_bytes", "lit_lookahead_golden",
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH):
     L.lit_attn_workspace_bytes.restype = sz
     L.lit_sparse_attn_decode.argtypes = [vp, ctypes.c_int, i32, ctypes.POINTER(KVDesc), i32, vp, vp, i32, i32, f32,
                                          vp, vp, vp, sz, vp]
+    L.lit_sparse_attn_decode_noalloc.argtypes = [vp, ctypes.c_int, i32, ctypes.POINTER(KVDesc), i32, vp, vp, i32,
+                                                 i32, f32, vp, vp, vp]
     L.lit_golden_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.lit_golden_workspace_bytes.restype = sz
     L.lit_golden_topk.argtypes = [vp, ctypes.c_int, i32, ctypes.POINTER(KVDesc), i32, f32, i32, vp, vp, vp, vp, vp,
@@ -105,7 +107,8 @@ def load(path: str = LIB_PATH):
     L.lit_lookahead_workspace_bytes.restype = sz
     L.lit_lookahead_golden.argtypes = [vp, ctypes.c_int, i32, i32, ctypes.POINTER(KVDesc), i32, f32, i32, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
-    for name in ("lit_idx_score", "lit_topk_select", "lit_sparse_attn_decode", "lit_golden_topk",
+    for name in ("lit_idx_score", "lit_topk_select", "lit_sparse_attn_decode", "lit_sparse_attn_decode_noalloc",
+                 "lit_golden_topk",
                  "lit_golden_topp_vote", "lit_idx_score_exact", "lit_recall", "lit_lsa_gate", "lit_pool_plan",
                  "lit_pool_gather", "lit_pool_remap_ids", "lit_idx_score_mq", "lit_topk_select_mq", "lit_lookahead_golden"):
         getattr(L, name).restype = ctypes.c_int
@@ -283,6 +286,23 @@ def sparse_attn_decode(q, kv, ids=None, count=None, window: int = 128, scale: fl
     _check(L.lit_sparse_attn_decode(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(desc), B, _ptr(ids), _ptr(count),
                                     k_cap, int(window), float(scale), o.data_ptr(), _ptr(lse), ws.data_ptr(),
                                     ws.numel(), _stream(q)))
+    return o, lse
+
+
+def sparse_attn_decode_noalloc(q, kv, ids=None, count=None, window: int = 128, scale: float = DEFAULT_SCALE,
+                               out=None, lse=None):
+    """sparse_attn_decode without a workspace: the partial results go to the
+    library's scratch array on this GPU (the call allocates no device memory
+    beyond the outputs created here when `out` / `lse` are not given)."""
+    torch = _torch()
+    _need_cuda(q, ids, count, out, lse)
+    B, Hq = q.shape[0], q.shape[1]
+    o = out if out is not None else torch.empty(B, Hq, KV_DIM, dtype=torch.float32, device=q.device)
+    desc = kv_desc(kv)
+    k_cap = ids.shape[1] if ids is not None else 0
+    _check(load().lit_sparse_attn_decode_noalloc(q.data_ptr(), _dtype_code(q), Hq, ctypes.byref(desc), B, _ptr(ids),
+                                                 _ptr(count), k_cap, int(window), float(scale), o.data_ptr(), _ptr(lse),
+                                                 _stream(q)))
     return o, lse
 
 

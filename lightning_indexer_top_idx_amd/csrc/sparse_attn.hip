@@ -23,7 +23,16 @@
 #include <algorithm>
 #include <math.h>
 
+#include <mutex>
+
 #include "lit_common.h"
+
+// Library-owned scratch of the allocation-free call: the per-slice partial
+// results of the split attention. Each GPU the library runs on holds its own
+// copy until the process ends. Host code never uses the array's name as an
+// address: the device address of each GPU's copy is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept in scratch_dev.
+static __device__ __align__(256) uint8_t scratch[LIT_ATTN_SCRATCH_BYTES];
 
 namespace lit {
 namespace {
@@ -741,12 +750,18 @@ extern "C" size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N) {
   return round_up((size_t)B * s * Hq * PART * sizeof(float), 256);
 }
 
-extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv, int32_t B,
-                                             const int32_t* ids, const int32_t* count, int32_t k_cap, int32_t window,
-                                             float scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                                             void* stream) {
-  clear_error();
-  const char* who = "lit_sparse_attn_decode";
+namespace lit {
+namespace {
+
+lit_status scratch_address(const char* who, void** out);
+
+// The attention call behind both entry points: `ws` is the caller's workspace;
+// with from_scratch the library's scratch array takes its place once the
+// arguments are validated (a plan larger than the array is refused the same way
+// as a short workspace).
+lit_status attn_decode(const char* who, bool from_scratch, const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv, int32_t B,
+                       const int32_t* ids, const int32_t* count, int32_t k_cap, int32_t window, float scale,
+                       float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (!q || !kv || !out || !kv->data) return fail(LIT_ERR_NULL, "%s: q, kv, kv->data and out must be non-NULL", who);
   if (B < 1 || Hq < 1 || Hq > LIT_MAX_Q_HEADS || kv->n_rows < 1)
     return fail(LIT_ERR_SHAPE, "%s: B=%d Hq=%d (1..%d) N=%d", who, B, Hq, LIT_MAX_Q_HEADS, kv->n_rows);
@@ -785,8 +800,14 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
   P.B = B;
   if (P.splits > 1) {
     const size_t need = round_up((size_t)B * P.splits * Hq * PART * sizeof(float), 256);
+    if (from_scratch) {
+      const lit_status sst = scratch_address(who, &ws);
+      if (sst != LIT_OK) return sst;
+      ws_bytes = (size_t)LIT_ATTN_SCRATCH_BYTES;
+    }
     if (!ws || ws_bytes < need)
-      return fail(LIT_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", who, ws_bytes, need);
+      return fail(LIT_ERR_WORKSPACE, "%s: %zu bytes of partial results needed, the %s holds %zu", who, need,
+                  from_scratch ? "library's scratch array" : "workspace given", ws_bytes);
     if (!aligned(ws, 16)) return fail(LIT_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
   }
   P.q = (const uint16_t*)q;
@@ -816,4 +837,46 @@ extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, i
     LIT_CHECK_LAUNCH(who);
   }
   return LIT_OK;
+}
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[MAX_DEVICES];
+
+lit_status scratch_address(const char* who, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LIT_ERR_LAUNCH, "%s: no current HIP device: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(LIT_ERR_LAUNCH, "%s: device %d beyond %d", who, dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LIT_ERR_LAUNCH, "%s: cannot find the scratch array on device %d: %s", who, dev, hipGetErrorString(e));
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return LIT_OK;
+}
+
+}  // namespace
+}  // namespace lit
+
+extern "C" lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv, int32_t B,
+                                             const int32_t* ids, const int32_t* count, int32_t k_cap, int32_t window,
+                                             float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  clear_error();
+  return attn_decode("lit_sparse_attn_decode", false, q, q_dtype, Hq, kv, B, ids, count, k_cap, window, scale, out, lse, ws,
+                     ws_bytes, stream);
+}
+
+extern "C" lit_status lit_sparse_attn_decode_noalloc(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,
+                                                     int32_t B, const int32_t* ids, const int32_t* count,
+                                                     int32_t k_cap, int32_t window, float scale, float* out,
+                                                     float* lse, void* stream) {
+  clear_error();
+  return attn_decode("lit_sparse_attn_decode_noalloc", true, q, q_dtype, Hq, kv, B, ids, count, k_cap, window, scale,
+                     out, lse, nullptr, 0, stream);
 }

@@ -206,3 +206,19 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_attn_noalloc_validation(L):
+    # argument checks come before any device query, so they run without a GPU
+    p = ctypes.c_void_p
+    kv = lit.KVDesc(1, 1000, 0x1000, None, None)
+    assert L.lit_sparse_attn_decode_noalloc(None, 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04, p(0x2000),
+                                            None, None) == 1
+    assert L.lit_sparse_attn_decode_noalloc(p(0x3000), 1, 65, ctypes.byref(kv), 4, None, None, 0, 0, 0.04,
+                                            p(0x2000), None, None) == 2
+    assert L.lit_sparse_attn_decode_noalloc(p(0x3000), 0, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04,
+                                            p(0x2000), None, None) == 4  # fp32 queries against bf16 rows
+    assert L.lit_sparse_attn_decode_noalloc(p(0x3008), 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04,
+                                            p(0x2000), None, None) == 3
+    assert L.lit_sparse_attn_decode_noalloc(p(0x3000), 1, 64, ctypes.byref(kv), 4, p(0x4000), None, 512, 128, 0.04,
+                                            p(0x2000), None, None) == 1  # ids without count
