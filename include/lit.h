@@ -215,14 +215,19 @@ lit_status lit_topk_select(const float* scores, int32_t B, int32_t N, int32_t k,
  * kv     : rows, see lit_kv. FP8 rows are dequantised exactly (E4M3 value times
  *          2^(scale-127)) before use ([ARCH] KV precision).
  * ids    : [B][k_cap] ascending ids (tail -1) with count[b] valid, or NULL for
- *          every row (then count and window are ignored).
+ *          every row (then count and window are ignored). count[b] is taken
+ *          up to min(k_cap, N); a negative count[b] (lit_topk_select's sign of a
+ *          failed exact selection) makes out[b] and lse[b] NaN, so that the
+ *          failure cannot pass for an answer.
  * window : 0..LIT_MAX_WINDOW, clamped to N.
  * out    : [B][Hq][512] fp32 output (16-byte aligned); lse: [B][Hq] fp32 output or NULL.
  * q, kv->data and kv->rope must be 16-byte aligned, kv->scale 4-byte. Errors: LIT_ERR_NULL,
  * LIT_ERR_SHAPE (B, Hq outside 1..64, window), LIT_ERR_DTYPE (unsupported row
  * or query dtype), LIT_ERR_ALIGN, LIT_ERR_WORKSPACE.
  * An empty R (count 0 and window 0) gives out = 0 and lse = -inf.
- * Workspace: lit_attn_workspace_bytes(B, Hq, N) bytes, 16-byte aligned. */
+ * Workspace: lit_attn_workspace_bytes(B, Hq, N) bytes, 16-byte aligned; it
+ * covers every k_cap and window on these shapes. A workspace given off a 16-byte
+ * boundary is refused (LIT_ERR_ALIGN) whether or not the call would use it. */
 size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N);
 lit_status lit_sparse_attn_decode(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,
                                   int32_t B, const int32_t* ids, const int32_t* count,

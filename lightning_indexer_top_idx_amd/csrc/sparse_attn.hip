@@ -123,7 +123,8 @@ __device__ __forceinline__ void unit_seq(int u, int B, int splits, int* b, int* 
 // dims) is requested before any is used.
 template <int SM>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int B, int splits, int Hq,
-                                                           float* __restrict__ out, float* __restrict__ lse) {
+                                                           const int32_t* __restrict__ count, float* __restrict__ out,
+                                                           float* __restrict__ lse) {
   const int x = blockIdx.x, d4 = threadIdx.x;
   int b, h;
   if (B % 8 == 0) {
@@ -166,21 +167,23 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     }
     M = Mp;
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const bool bad = count && count[b] < 0;  // the selection failed: NaN outputs
+  const float inv = bad ? __builtin_nanf("") : (L > 0.f ? 1.f / L : 0.f);
   *(f32x4*)(out + ((size_t)b * Hq + h) * LIT_KV_DIM + 4 * d4) = acc * inv;
-  if (lse && d4 == 0) lse[(size_t)b * Hq + h] = L > 0.f ? M * LN2 + logf(L) : -INFINITY;
+  if (lse && d4 == 0) lse[(size_t)b * Hq + h] = bad ? __builtin_nanf("") : (L > 0.f ? M * LN2 + logf(L) : -INFINITY);
 }
 
-void launch_combine(const float* part, int B, int splits, int Hq, float* out, float* lse, hipStream_t st) {
+void launch_combine(const float* part, int B, int splits, int Hq, const int32_t* count, float* out, float* lse,
+                    hipStream_t st) {
   const dim3 grid((unsigned)(B * Hq)), block(128);
   if (splits <= 2)
-    attn_combine_kernel<2><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
+    attn_combine_kernel<2><<<grid, block, 0, st>>>(part, B, splits, Hq, count, out, lse);
   else if (splits <= 4)
-    attn_combine_kernel<4><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
+    attn_combine_kernel<4><<<grid, block, 0, st>>>(part, B, splits, Hq, count, out, lse);
   else if (splits <= 8)
-    attn_combine_kernel<8><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
+    attn_combine_kernel<8><<<grid, block, 0, st>>>(part, B, splits, Hq, count, out, lse);
   else
-    attn_combine_kernel<16><<<grid, block, 0, st>>>(part, B, splits, Hq, out, lse);
+    attn_combine_kernel<16><<<grid, block, 0, st>>>(part, B, splits, Hq, count, out, lse);
 }
 
 // FP32 rows and queries: one workgroup per (sequence, head), fp32 VALU with an
@@ -195,6 +198,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   __shared__ float red[8];
   const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
   const int tid = threadIdx.x;
+  bool bad = false;  // count[b] < 0: the selection failed; the outputs say so with NaN
   RowList RL;
   RL.dense = ids == nullptr;
   RL.N = N;
@@ -206,8 +210,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
     RL.total = N;
   } else {
     RL.ids = ids + (size_t)b * k_cap;
+    const int cap = min(k_cap, N);
     int c = count[b];
-    c = c < 0 ? 0 : (c > k_cap ? k_cap : c);
+    bad = c < 0;
+    c = c < 0 ? 0 : (c > cap ? cap : c);
     RL.c = c;
     RL.Wc = window;
     RL.total = c + window;
@@ -263,10 +269,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
     __syncthreads();
   }
   float* oh = out + ((size_t)b * Hq + h) * LIT_KV_DIM;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = bad ? __builtin_nanf("") : (l > 0.f ? 1.f / l : 0.f);
   oh[tid] = o0 * inv;
   oh[tid + 256] = o1 * inv;
-  if (lse && tid == 0) lse[(size_t)b * Hq + h] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (lse && tid == 0) lse[(size_t)b * Hq + h] = bad ? __builtin_nanf("") : (l > 0.f ? m + logf(l) : -INFINITY);
 }
 
 // ---------------------------------------------------------------- BF16 rows, 16 heads per workgroup
@@ -568,6 +574,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
                                        (__attribute__((address_space(3))) void*)(ids_l + j0), 4, 0, 0);
   }
 
+  bool bad = false;  // count[b] < 0: the selection failed; the outputs say so with NaN
   RowList RL;
   RL.dense = P.ids == nullptr;
   RL.N = P.N;
@@ -579,8 +586,10 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
     RL.total = P.N;
   } else {
     RL.ids = ids_cached ? ids_l : P.ids + (size_t)b * P.k_cap;
+    const int cap = min(P.k_cap, P.N);
     int c = P.count[b];
-    c = c < 0 ? 0 : (c > P.k_cap ? P.k_cap : c);
+    bad = c < 0;
+    c = c < 0 ? 0 : (c > cap ? cap : c);
     RL.c = c;
     RL.Wc = P.window;
     RL.total = c + P.window;
@@ -690,10 +699,11 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   if (hh < Hq) {
     if (P.splits == 1) {
       float* oh = P.out + ((size_t)b * Hq + hh) * LIT_KV_DIM + 128 * wid + 4 * g;
-      const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+      const float inv = bad ? __builtin_nanf("") : (Ls > 0.f ? 1.f / Ls : 0.f);
 #pragma unroll
       for (int nt = 0; nt < 8; nt++) *(f32x4*)(oh + 16 * nt) = S.o[nt] * inv;
-      if (P.lse && wid == 0 && g == 0) P.lse[(size_t)b * Hq + hh] = Ls > 0.f ? S.m_run * LN2 + logf(Ls) : -INFINITY;
+      if (P.lse && wid == 0 && g == 0)
+        P.lse[(size_t)b * Hq + hh] = bad ? __builtin_nanf("") : (Ls > 0.f ? S.m_run * LN2 + logf(Ls) : -INFINITY);
     } else {
       float* ph = P.part + (((size_t)b * P.splits + s) * Hq + hh) * PART;
 #pragma unroll
@@ -739,13 +749,16 @@ using namespace lit;
 
 extern "C" size_t lit_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N) {
   if (B < 1 || Hq < 1 || N < 1) return 0;
-  // the most slices any call on these shapes can plan: a selection of up to
-  // N + LIT_MAX_WINDOW rows, or all N rows read densely
-  int s2, s3, rps;
+  // A bound on the slices of any call on these shapes, whatever its k_cap and
+  // window: a call plans at most min(k_cap, N) + window <= N + LIT_MAX_WINDOW
+  // selected rows or N dense rows, and plan_mh never picks more slices than
+  // the larger of the round's share (capped by the tiles) and the slices that
+  // the LDS row list forces on the longest selection.
   const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
-  plan_mh(B, HGm, N + LIT_MAX_WINDOW, true, &s2, &rps);
-  plan_mh(B, HGm, N, false, &s3, &rps);
-  const int s = std::max(s2, s3);
+  const int tiles = (N + LIT_MAX_WINDOW + MH_TR - 1) / MH_TR;
+  const int want = std::max(1, (MH_TARGET + B * HGm - 1) / (B * HGm));
+  const int s_forced = (tiles * MH_TR + MH_ROWS_CAP - 1) / MH_ROWS_CAP;
+  const int s = std::max(std::min(tiles, want), s_forced);
   if (s <= 1) return 256;
   return round_up((size_t)B * s * Hq * PART * sizeof(float), 256);
 }
@@ -793,7 +806,10 @@ lit_status attn_decode(const char* who, bool from_scratch, const void* q, lit_dt
     LIT_CHECK_LAUNCH(who);
     return LIT_OK;
   }
-  const int rows_max = ids ? (k_cap + Wc) : N;
+  if (ws && !aligned(ws, 16)) return fail(LIT_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  // a selection holds at most N distinct ids (the kernel clamps count[b] to
+  // min(k_cap, N)), so a k_cap beyond N plans no more rows than N does
+  const int rows_max = ids ? (std::min(k_cap, N) + Wc) : N;
   AttnParams P;
   const int HGm = (Hq + MH_HEADS - 1) / MH_HEADS;
   plan_mh(B, HGm, rows_max, ids != nullptr, &P.splits, &P.rows_per_split);
@@ -808,7 +824,6 @@ lit_status attn_decode(const char* who, bool from_scratch, const void* q, lit_dt
     if (!ws || ws_bytes < need)
       return fail(LIT_ERR_WORKSPACE, "%s: %zu bytes of partial results needed, the %s holds %zu", who, need,
                   from_scratch ? "library's scratch array" : "workspace given", ws_bytes);
-    if (!aligned(ws, 16)) return fail(LIT_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
   }
   P.q = (const uint16_t*)q;
   P.Hq = Hq;
@@ -833,7 +848,7 @@ lit_status attn_decode(const char* who, bool from_scratch, const void* q, lit_dt
     attn_mh_kernel<false><<<grid, dim3(MH_THREADS), 0, st>>>(P);
   LIT_CHECK_LAUNCH(who);
   if (P.splits > 1) {
-    launch_combine((const float*)ws, B, P.splits, Hq, out, lse, st);
+    launch_combine((const float*)ws, B, P.splits, Hq, ids ? count : nullptr, out, lse, st);
     LIT_CHECK_LAUNCH(who);
   }
   return LIT_OK;

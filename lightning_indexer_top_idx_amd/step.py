@@ -78,6 +78,14 @@ class CsaLayer:
         self.select(stream)
         self.attend(stream)
 
+    def check(self):
+        """Raise if a sequence's exact selection failed (count < 0: the rounding
+        bound was violated; attention then wrote NaN for it). Waits for the
+        device; meant for an eager step, not inside a captured one."""
+        bad = (self.count < 0).nonzero().flatten().tolist()
+        if bad:
+            raise RuntimeError(f"exact top-k failed (count < 0) for sequences {bad}")
+
 
 class DenseLayer:
     """Attention over every row given: the HCA layer's compressed rows, or an
@@ -114,3 +122,9 @@ class TokenSchedule:
     def run(self, stream):
         for Ly in self.layers:
             Ly.run(stream)
+
+    def check(self):
+        """Raise if any CSA layer's exact selection failed (see CsaLayer.check)."""
+        for Ly in self.layers:
+            if isinstance(Ly, CsaLayer):
+                Ly.check()

@@ -103,10 +103,10 @@ def test_attention_validation(L):
     kv8m = lit.KVDesc(2, 1000, 0x1000, 0x8000, 0x9002)
     assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv8m), 1, None, None, 0, 0, 0.04, p(0x2000), None,
                                     None, 0, None) == 3
-    # many sequences split the rows: the workspace is required
+    # a workspace off a 16-byte boundary is refused before any planning
     assert L.lit_attn_workspace_bytes(4, 64, 125000) > 256
     assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04, p(0x2000), None,
-                                    None, 0, None) == 5
+                                    p(0x7008), 1 << 30, None) == 3
 
 
 def test_other_entry_points_validation(L):

@@ -236,6 +236,10 @@ def oracle_ids(inp, k):
     ("ragged", W.CTX64K, 3, 2049, 512, 128),
     ("window_over_n", W.CTX64K, 1, 100, 512, 300),
     ("no_window", W.CTX64K, 2, 3000, 256, 0),
+    # k beyond N: the selection's capacity exceeds the rows; the workspace the
+    # binding takes from lit_attn_workspace_bytes(B, Hq, N) must still suffice
+    ("kcap_over_n", W.CTX64K, 2, 300, 512, 128),
+    ("kcap_over_n_b1", W.CTX64K, 1, 100, 512, 128),
 ])
 def test_sparse_attention(name, wl, B, N, k, window):
     print(f"case {name}", flush=True)
@@ -265,6 +269,28 @@ def test_attention_counts_below_cap_duplicates_and_empty():
             assert (out[3] == 0).all() and torch.isneginf(lse[3]).all()
             ref[3] = 0
         assert_attn_close(out, ref)
+
+
+def test_failed_selection_gives_nan_for_its_sequence_only():
+    # count[b] = -1 (the exact selection's failure sign): that sequence's out
+    # and lse are NaN, the others match the oracle; on the split path (slices
+    # + combine), the single-slice path and the FP32 kernel
+    for name, wl, B, N, k, window, bad in (("split", W.CTX64K, 2, 3000, 256, 128, 0),
+                                             ("one_slice", W.CTX64K, 64, 1000, 64, 16, 3),
+                                             ("f32", W.TINY, 3, 1024, 64, 16, 1)):
+        print(f"case failed selection {name}", flush=True)
+        L = W.layer_inputs(wl, 0, "cpu", B=B, N=N)
+        rids, rcnt, _ = oracle_ids(L.idx, k)
+        cnt = rcnt.copy()
+        cnt[bad] = -1
+        out, lse = lit.sparse_attn_decode(dev(L.q), kv_dev(L.kv), dev(torch.from_numpy(rids)),
+                                          dev(torch.from_numpy(cnt)), window, SCALE)
+        torch.cuda.synchronize()
+        assert torch.isnan(out[bad]).all() and torch.isnan(lse[bad]).all(), name
+        keep = [b for b in range(out.shape[0]) if b != bad]
+        ref, rlse = oracle.attend(L.q, L.kv, rids, rcnt, window, SCALE)
+        assert_attn_close(out[keep], ref[keep])
+        np.testing.assert_allclose(lse[keep].double().cpu().numpy(), rlse[keep], atol=2e-3, rtol=0)
 
 
 def test_full_selection_equals_dense_and_hca_mode():
