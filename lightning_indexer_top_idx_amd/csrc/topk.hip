@@ -7,20 +7,22 @@
 // ids to the attention kernel. The pages build that mask on the host; here it
 // never leaves the device. Ties go to the lower index.
 //
-// One workgroup (1024 threads) per sequence. Up to 16384 entries a kernel of
-// its own keeps every score in registers (see the small path below). Fast path
-// (with the hints of lit_idx_score, 16384 < N <= 131072):
+// Up to 16384 entries per row, one workgroup (1024 threads) per row keeps every
+// score in registers (the small path below). Longer rows with the hints of
+// lit_idx_score (N <= 131072) take two kernels (the wide path below):
 //   1. the k-th largest of the per-16-entry score maxima is a lower bound L of
 //      the k-th largest score (it is the k-th largest of a subset of the scores);
-//   2. only groups whose maximum reaches L can hold top-k entries: their entries
-//      >= L are gathered into LDS, in index order (~k groups are read, not N);
-//   3. an MSB-first radix select over those candidates gives the k-th score T;
+//   2. only groups whose maximum reaches L - 2 Delta can hold top-k entries (or
+//      band members): many workgroups per row list their slices' entries above
+//      that bound, in index order (~k groups are read, not N), and rescore in
+//      fp64 those near L;
+//   3. one workgroup per row takes the k-th score T over those candidates;
 //   4. exact mode: every fp32 score is within Delta of its fp64 canonical value
 //      (Delta bounds the fp32 MFMA/FMA rounding through the key-norm hints and
 //      sum_h |w_h| |q_h|). Entries above T + 2 Delta are in for sure, entries below
-//      T - 2 Delta out; the few in between are rescored in fp64 in canonical
-//      order and the best of them taken by (score desc, index asc);
-//   5. a bitmap of the selection is compacted into ascending ids (and the mask).
+//      T - 2 Delta out; those in between are ranked by their fp64 canonical
+//      scores, and the best taken by (score desc, index asc);
+//   5. the selection is compacted into ascending ids (and the mask).
 // Anything that does not fit (no hints, larger N, too many candidates after ties)
 // falls back to scanning every score with the same steps.
 #include <algorithm>
@@ -46,7 +48,6 @@ constexpr int GROUP = LIT_HINT_GROUP;
 constexpr int GM_CAP = 8192;                   // group maxima in LDS: N <= 131072
 constexpr int CAND_CAP = 2048;                 // candidates >= L in LDS
 constexpr int FBAND_CAP = 1024;                // exact band in LDS
-constexpr int SEL_WORDS = GM_CAP * GROUP / 32;  // selection bitmap
 
 // Bound delta on |fp32 score - fp64 canonical score| for an entry whose key
 // norm is at most kmax. On the way to a score, every fp32 operation of
@@ -80,9 +81,13 @@ struct TopkParams {
   int32_t* ids;
   int32_t* count;
   uint8_t* mask;
-  double* ws_band_s;     // [B][N]
-  int32_t* ws_band_n;    // [B][N]
+  double* ws_band_s;     // [B][N] (wide path: exact scores of the rescored candidates)
+  int32_t* ws_band_n;    // [B][N] (wide path: candidate indices)
+  uint32_t* ws_ckey;     // [B][N] wide path: candidate keys
   uint8_t* ws_band_sel;  // [B][N]
+  int32_t* ws_wide;      // [B][WIDE_STRIDE] wide path: header and slice counts per row
+  int rows;              // B (rows of scores)
+  int wide_slices;       // slices per row of the wide path
 };
 
 struct FullLds {
@@ -102,27 +107,21 @@ constexpr int QP_STRIDE = LIT_IDX_DIM + 4;  // fp32 q row stride in LDS (spreads
 constexpr int BW = 4;        // band entries per wave and round of the broadcast rescoring
 constexpr int PSUM_LD = 66;  // fp64 row stride of the head terms (rows on distinct banks)
 
-struct FastLds {
+struct FastLds {  // the wide path's kernel B
   SelectScratch sc;
-  int imisc[8];
-  double dmisc[4];
-  double qn[64];
-  double wa[64];
-  float qP[64 * QP_STRIDE];
+  union {
+    float qP[64 * QP_STRIDE];  // the fallback's band rescoring
+    double cexact[CAND_CAP];   // exact scores kernel A took, by candidate position
+  };
   double psum[NWAVES][BW][PSUM_LD];  // head terms of the rescoring waves
   double band_s[FBAND_CAP];
   int32_t band_n[FBAND_CAP];
-  uint32_t band_k[FBAND_CAP];
   uint8_t cflag[CAND_CAP];
   union {  // never live at the same time
     uint32_t hist2k[2048];
-    uint16_t qlist[GM_CAP];
     uint16_t binpos[CAND_CAP];
   };
-  union {
-    uint32_t gkey[GM_CAP];
-    uint32_t sel[SEL_WORDS];
-  };
+  uint32_t sel[CAND_CAP / 32];  // bit i: candidate i selected
   uint32_t ckey[CAND_CAP];
   int32_t cidx[CAND_CAP];
 };
@@ -404,145 +403,114 @@ __device__ uint32_t hist_kth(KeyFn key, int M, int r, uint32_t kmin, uint32_t km
   return prefix + ((uint32_t)bin << shift);
 }
 
-// Gathers, in index order, the entries whose key is in [lo, hi) from the groups
-// whose maximum reaches lo. Appends at out_key/out_idx + base. Returns the
-// number found, or -1 (writing nothing) when base + found would exceed cap.
-// The qualifying groups are listed first so each thread loads about one group
-// (one 64-byte read) and all loads are in flight together.
-__device__ int gather_range(const float* sb, int N, const uint32_t* gkey, uint16_t* qlist, int G, uint32_t lo,
-                            uint32_t hi, uint32_t* out_key, int32_t* out_idx, int base, int cap,
-                            SelectScratch* sc) {
+// The row's q (fp32, exact mode) to LDS for the rescoring, one 8-dim piece
+// per thread (q and w are per row).
+__device__ void stage_q_rows(const TopkParams& P, float* qP, int b) {
   const int tid = threadIdx.x;
-  const bool vec = (reinterpret_cast<uintptr_t>(sb) & 15u) == 0;
-  auto load16 = [&](int g, float (&v)[GROUP]) {
-    const int e0 = GROUP * g;
-    if (vec && e0 + GROUP <= N) {
+  const int h = tid >> 4, d8 = tid & 15;
+  float x[8];
+  if (h < P.H) {
+    const size_t off = ((size_t)b * P.H + h) * LIT_IDX_DIM + 8 * d8;
+    if (P.dtype == LIT_BF16) {
+      const u32x4 v = *(const u32x4*)((const uint16_t*)P.q + off);
 #pragma unroll
-      for (int c = 0; c < GROUP / 4; c++) {
-        const f32x4 x = *(const f32x4*)(sb + e0 + 4 * c);
-#pragma unroll
-        for (int i = 0; i < 4; i++) v[4 * c + i] = x[i];
+      for (int i = 0; i < 4; i++) {
+        x[2 * i] = bf16_lo(v[i]);
+        x[2 * i + 1] = bf16_hi(v[i]);
       }
     } else {
+      const f32x4 v0 = *(const f32x4*)((const float*)P.q + off), v1 = *(const f32x4*)((const float*)P.q + off + 4);
 #pragma unroll
-      for (int i = 0; i < GROUP; i++) v[i] = e0 + i < N ? sb[e0 + i] : -INFINITY;
+      for (int i = 0; i < 4; i++) {
+        x[i] = v0[i];
+        x[4 + i] = v1[i];
+      }
     }
-  };
-  auto in_range = [&](float x) -> bool {
-    const uint32_t kk = score_key(x);
-    return (kk >= lo) && (kk < hi) && (kk != 0u);
-  };
-  // 1. list the qualifying groups in index order
-  const int gseg = (G + TK_THREADS - 1) / TK_THREADS;
-  const int ga = min(G, tid * gseg), ge = min(G, ga + gseg);
-  int nq = 0;
-  for (int g = ga; g < ge; g++) nq += gkey[g] >= lo;
-  int Q;
-  int qp = block_excl_scan(nq, sc->scan, &Q);
-  for (int g = ga; g < ge; g++)
-    if (gkey[g] >= lo) qlist[qp++] = (uint16_t)g;
-  lds_barrier();
-  // 2. count per contiguous run of list positions; the first group stays in registers
-  const int qseg = (Q + TK_THREADS - 1) / TK_THREADS;
-  const int qa = min(Q, tid * qseg), qe = min(Q, qa + qseg);
-  float v0[GROUP];
-  int c = 0;
-  if (qa < qe) {
-    load16(qlist[qa], v0);
+  } else {
 #pragma unroll
-    for (int i = 0; i < GROUP; i++) c += in_range(v0[i]);
+    for (int i = 0; i < 8; i++) x[i] = 0.f;
   }
-  for (int j = qa + 1; j < qe; j++) {
-    float v[GROUP];
-    load16(qlist[j], v);
-#pragma unroll
-    for (int i = 0; i < GROUP; i++) c += in_range(v[i]);
-  }
-  int total;
-  int p = base + block_excl_scan(c, sc->scan, &total);
-  if (base + total > cap) return -1;
-  if (qa < qe) {
-    const int e0 = GROUP * qlist[qa];
-#pragma unroll
-    for (int i = 0; i < GROUP; i++)
-      if (in_range(v0[i])) {
-        out_key[p] = score_key(v0[i]);
-        out_idx[p] = e0 + i;
-        p++;
-      }
-  }
-  for (int j = qa + 1; j < qe; j++) {
-    float v[GROUP];
-    const int g = qlist[j];
-    load16(g, v);
-#pragma unroll
-    for (int i = 0; i < GROUP; i++)
-      if (in_range(v[i])) {
-        out_key[p] = score_key(v[i]);
-        out_idx[p] = GROUP * g + i;
-        p++;
-      }
-  }
-  lds_barrier();
-  return total;
+  *(f32x4*)&qP[h * QP_STRIDE + 8 * d8] = f32x4{x[0], x[1], x[2], x[3]};
+  *(f32x4*)&qP[h * QP_STRIDE + 8 * d8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-// Returns false, having written nothing, when the sequence does not fit.
-__device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int N = P.N, k = P.k;
-  const float* sb = P.scores + (size_t)b * N;
-  const float* gmx = P.hints + (size_t)b * P.hints_len + P.nchunks;
-  int32_t* ids = P.ids + (size_t)b * k;
-  uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
-  const int G = (N + GROUP - 1) / GROUP;
-  const int W = (N + 31) / 32;
-  // the largest key-norm bound (exact mode), also loaded up front
-  float knorm = 0.f;
-  if (P.exact)
-    for (int j = tid; j < P.nchunks; j += TK_THREADS) knorm = fmaxf(knorm, P.hints[(size_t)b * P.hints_len + j]);
+// Wide path: for long rows one workgroup per row leaves most CUs idle while it
+// reads the group maxima, gathers candidates and rescores the band, so the
+// work is split over two kernels.
+//   A (S workgroups per row, slice s = groups s*GS .. +GS-1): every workgroup
+//     builds the histogram of all the row's group maxima and reads off L, the
+//     lower edge of the bin of the k-th largest (at least k entries reach it,
+//     so the k-th score T >= L), and H, the upper edge of the bin of the
+//     (k - WIDE_MARGIN)-th largest. In exact mode lo = L - 2 Delta and
+//     hx = H + 2 Delta (Delta from the hints). It lists its slice's entries
+//     with key >= lo (key, index), in index order, at the slice's own place in
+//     the workspace, rescores in fp64 those with key <= hx, and clears its
+//     slice of the mask.
+//   B (one workgroup per row): the lists concatenated are the candidates, in
+//     index order. Every entry of the exact top k is one: its fp32 score is at
+//     least T - 2 Delta >= lo. When fewer than k candidates lie above
+//     hx - 2 Delta, T <= hx - 2 Delta, so every candidate above hx has an exact
+//     score above the k-th exact score and is selected; the other k - (those)
+//     are the best rescored candidates by (exact score desc, index asc). When
+//     that test fails (or a list overflowed) B finds T itself and rescores its
+//     band; without exact mode it finds the k-th fp32 key.
+constexpr int WIDE_SLICES_MAX = 64;  // slices per row
+constexpr int WIDE_HDR = 8;          // header words per row before its slice counts
+constexpr int WIDE_STRIDE = WIDE_HDR + WIDE_SLICES_MAX;
+constexpr int WIDE_MARGIN = 64;      // ranks between the group maxima that give L and H
+constexpr int WIDE_RCAP = 256;       // entries one slice rescores
+constexpr int WIDE_RWAVES = 8;       // waves that rescore in kernel A
+constexpr uint32_t WIDE_OVERFLOW = 1u << 30;  // in a slice count: more than WIDE_RCAP to rescore
+// header words: 0 L, 1 lo, 2 selectable groups, 3 largest key-norm bound (bits),
+// 4-5 Delta, 6 hx, 7 the key of hx - 2 Delta (rounded down)
 
-  // 0. exact mode: q rows (fp32) and |w_h| |q_h|, one 8-dim piece per thread
-  if (P.exact) {
-    const int h = tid >> 4, d8 = tid & 15;
-    float x[8];
-    if (h < P.H) {
-      const size_t off = ((size_t)b * P.H + h) * LIT_IDX_DIM + 8 * d8;
-      if (P.dtype == LIT_BF16) {
-        const u32x4 v = *(const u32x4*)((const uint16_t*)P.q + off);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          x[2 * i] = bf16_lo(v[i]);
-          x[2 * i + 1] = bf16_hi(v[i]);
-        }
-      } else {
-        const f32x4 v0 = *(const f32x4*)((const float*)P.q + off), v1 = *(const f32x4*)((const float*)P.q + off + 4);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          x[i] = v0[i];
-          x[4 + i] = v1[i];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; i++) x[i] = 0.f;
-    }
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      L.qP[h * QP_STRIDE + 8 * d8 + i] = x[i];
-      ss += (double)x[i] * (double)x[i];
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
-    if (d8 == 0) {
-      const double wa = h < P.H ? fabs((double)P.w[(size_t)b * P.H + h]) : 0.0;
-      L.qn[h] = wa * sqrt(ss);
-      L.wa[h] = wa;
-    }
+// Kernel A's workgroup -> (row, slice). When the rows are a multiple of 8,
+// every slice of row b has a workgroup id equal to b modulo 8 (XCD b % 8, where
+// kernel B's workgroup b reads the lists); otherwise the slices of a row are
+// consecutive workgroups, spread over every XCD.
+__device__ __forceinline__ void wide_unit(int x, int rows, int S, int* b, int* s) {
+  if (rows % 8 == 0) {
+    *s = (x >> 3) % S;
+    *b = ((x >> 3) / S) * 8 + (x & 7);
+  } else {
+    *b = x / S;
+    *s = x % S;
   }
+}
 
-  // 1. group keys (+ the largest key-norm bound in exact mode)
+struct WideLds {  // kernel A
+  SelectScratch sc;
+  float qP[64 * QP_STRIDE];
+  union {
+    struct {
+      uint32_t hist2k[2048];
+      uint32_t gkey[GM_CAP];
+    };
+    double psum[WIDE_RWAVES][BW][PSUM_LD];  // once the group keys are dead
+  };
+  int32_t rl_n[WIDE_RCAP];     // entries to rescore
+  int32_t rl_slot[WIDE_RCAP];  // their places in the slice's list
+  double rl_s[WIDE_RCAP];      // their exact scores
+};
+
+__device__ void wide_candidates(const TopkParams& P, WideLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int S = P.wide_slices;
+  int b, s;
+  wide_unit((int)blockIdx.x, P.rows, S, &b, &s);
+  const int N = P.N, k = P.k;
+  const int G = (N + GROUP - 1) / GROUP;
+  const float* sb = P.scores + (size_t)b * N;
+  const float* hb = P.hints + (size_t)b * P.hints_len;
+  const float* gmx = hb + P.nchunks;
+
+  // 1. group keys (+ the largest key-norm bound, q and w in exact mode)
+  float knorm = 0.f, w_h = 0.f;
+  if (P.exact) {
+    for (int j = tid; j < P.nchunks; j += TK_THREADS) knorm = fmaxf(knorm, hb[j]);
+    w_h = lane < P.H ? P.w[(size_t)b * P.H + lane] : 0.f;
+    stage_q_rows(P, L.qP, b);
+  }
   int ns = 0;
   uint32_t kmin = 0xffffffffu, kmx = 0u;
   for (int g = tid; g < G; g += TK_THREADS) {
@@ -555,34 +523,155 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
     }
   }
   block_sum_min_max(ns, kmin, kmx, knorm, &L.sc);
-  if (ns == 0) {
-    for (int j = tid; j < k; j += TK_THREADS) ids[j] = -1;
-    if (mask)
-      for (int n = tid; n < N; n += TK_THREADS) mask[n] = 0;
-    if (tid == 0) P.count[b] = 0;
-    return true;
-  }
 
-  // 2. lower bound L: the lower edge of the histogram bin holding the k-th group maximum
-  uint32_t lkey = 1u;
+  // 2. L and H from one histogram of the group keys (the bins span the bits
+  //    below the common prefix of the smallest and largest)
+  uint32_t lkey = 1u, hkey = kmx;
   if (ns >= k) {
-    int above, inb, shift;
-    uint32_t prefix;
-    lkey = hist_kth([&](int i) -> uint32_t { return L.gkey[i]; }, G, k, kmin, kmx, L.hist2k, &L.sc, &above, &inb,
-                    &prefix, &shift);
+    const uint32_t diff = kmin ^ kmx;
+    const int hbit = diff ? 31 - __clz((int)diff) : 0;
+    const int shift = hbit > 10 ? hbit - 10 : 0;
+    const uint32_t prefix = kmx & ~((2u << hbit) - 1u);
+    for (int i = tid; i < 2048; i += TK_THREADS) L.hist2k[i] = 0u;
+    lds_barrier();
+    for (int i = tid; i < G; i += TK_THREADS) {
+      const uint32_t kk = L.gkey[i];
+      if (kk != 0u) atomicAdd(&L.hist2k[(kk - prefix) >> shift], 1u);
+    }
+    lds_barrier();
+    // cumulative counts from the top bin down: thread t owns bins 2047-2t, 2046-2t
+    const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
+    int tot;
+    const int ab = block_excl_scan(c0 + c1, L.sc.scan, &tot);
+    const int r1 = k, r2 = max(1, k - WIDE_MARGIN);
+    if (ab < r1 && r1 <= ab + c0) L.sc.misc[0] = 2047 - 2 * tid;
+    if (ab + c0 < r1 && r1 <= ab + c0 + c1) L.sc.misc[0] = 2046 - 2 * tid;
+    if (ab < r2 && r2 <= ab + c0) L.sc.misc[1] = 2047 - 2 * tid;
+    if (ab + c0 < r2 && r2 <= ab + c0 + c1) L.sc.misc[1] = 2046 - 2 * tid;
+    lds_barrier();
+    lkey = prefix + ((uint32_t)L.sc.misc[0] << shift);
+    hkey = min(kmx, prefix + ((uint32_t)(L.sc.misc[1] + 1) << shift) - 1u);
+  }
+  uint32_t lo = lkey, hx = 0u, c2 = 0u;
+  double delta = 0.0;
+  if (P.exact) {
+    const uint32_t* qb = reinterpret_cast<const uint32_t*>(hb + P.hints_len) - LIT_HINT_QBOUND;
+    const double Q = __longlong_as_double((long long)(((uint64_t)qb[1] << 32) | qb[0]));
+    const double Wa = __longlong_as_double((long long)(((uint64_t)qb[3] << 32) | qb[2]));
+    delta = score_err_bound(P.dtype == LIT_BF16, P.H, Q, (double)knorm, Wa);
+    if (lkey > 1u) {
+      const uint32_t l0 = score_key(__double2float_rd((double)key_score(lkey) - 2.0 * delta));
+      lo = l0 > 1u ? l0 : 1u;
+    }
+    const uint32_t h0 = score_key(__double2float_ru((double)key_score(hkey) + 2.0 * delta));
+    hx = h0 ? h0 : 0xff800000u;  // past the largest finite key: +inf's
+    c2 = score_key(__double2float_rd((double)key_score(hx) - 2.0 * delta));
   }
 
-  // 3. candidates >= L in index order
-  const int M1 = gather_range(sb, N, L.gkey, L.qlist, G, lkey, 0xffffffffu, L.ckey, L.cidx, 0, CAND_CAP, &L.sc);
-  if (M1 < 0) return false;
-  // (a key of 0xffffffff would be a NaN pattern: score_key maps NaN to 0)
+  // 3. this slice's entries >= lo, one group per thread, in index order; in
+  //    exact mode those <= hx are also listed for the rescoring
+  const int GS = (G + S - 1) / S;
+  const int g0 = min(G, s * GS), g1 = min(G, g0 + GS);
+  const int g = g0 + tid;
+  const bool live = g < g1 && L.gkey[g] >= lo;
+  uint32_t kv[GROUP];
+  int c = 0, r = 0;
+  if (live) {
+    const int e0 = GROUP * g;
+    if ((reinterpret_cast<uintptr_t>(sb) & 15u) == 0 && e0 + GROUP <= N) {
+#pragma unroll
+      for (int q = 0; q < GROUP / 4; q++) {
+        const f32x4 x = *(const f32x4*)(sb + e0 + 4 * q);
+#pragma unroll
+        for (int i = 0; i < 4; i++) kv[4 * q + i] = score_key(x[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < GROUP; i++) kv[i] = e0 + i < N ? score_key(sb[e0 + i]) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < GROUP; i++) {
+      c += kv[i] >= lo;  // lo >= 1: key 0 is never listed
+      r += kv[i] >= lo && kv[i] <= hx;
+    }
+  }
+  int tot;
+  int pos = block_excl_scan((c << 16) | r, L.sc.scan, &tot);
+  int rpos = pos & 0xffff;
+  pos >>= 16;
+  const int ctot = tot >> 16, rtot = tot & 0xffff;
+  const size_t base = (size_t)b * N + GROUP * g0;
+  uint32_t* ck = P.ws_ckey + base;
+  int32_t* ci = P.ws_band_n + base;
+  if (live) {
+#pragma unroll
+    for (int i = 0; i < GROUP; i++)
+      if (kv[i] >= lo) {
+        ck[pos] = kv[i];
+        ci[pos] = GROUP * g + i;
+        if (kv[i] <= hx && rpos < WIDE_RCAP) {
+          L.rl_n[rpos] = GROUP * g + i;
+          L.rl_slot[rpos] = pos;
+        }
+        rpos += kv[i] <= hx;
+        pos++;
+      }
+  }
+  int32_t* hdr = P.ws_wide + (size_t)b * WIDE_STRIDE;
+  if (tid == 0) {
+    hdr[WIDE_HDR + s] = ctot | (rtot > WIDE_RCAP ? (int)WIDE_OVERFLOW : 0);
+    if (s == 0) {
+      const uint64_t db = (uint64_t)__double_as_longlong(delta);
+      hdr[0] = (int32_t)lkey;
+      hdr[1] = (int32_t)lo;
+      hdr[2] = ns;
+      hdr[3] = __float_as_int(knorm);
+      hdr[4] = (int32_t)(uint32_t)db;
+      hdr[5] = (int32_t)(uint32_t)(db >> 32);
+      hdr[6] = (int32_t)hx;
+      hdr[7] = (int32_t)c2;
+    }
+  }
+  if (P.mask) {
+    uint8_t* mb = P.mask + (size_t)b * N;
+    const int m1 = min(N, GROUP * g1);
+    for (int n = GROUP * g0 + tid; n < m1; n += TK_THREADS) mb[n] = 0;
+  }
 
-  uint32_t* sel = L.sel;  // aliases gkey: cleared once gkey is no longer read
-  if (M1 <= k) {
-    for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
+  // 4. exact mode: the listed entries rescored in fp64 (the group keys are dead:
+  //    psum takes their place), their scores stored beside their list places
+  if (P.exact && rtot > 0 && rtot <= WIDE_RCAP) {
+    lds_barrier();  // the list, q and the last reads of the group keys
+    const int M = rtot;
+    const int nwr = min(WIDE_RWAVES, max(4, ((M + BW - 1) / BW + 3) & ~3));
+    for (int e = 0; e + wid < M && wid < nwr; e += nwr * BW) {
+      if (P.dtype == LIT_BF16)
+        band_scores_bcast<true>(P, b, L.qP, w_h, L.rl_n, M, e + wid, nwr, L.psum[wid], L.rl_s);
+      else
+        band_scores_bcast<false>(P, b, L.qP, w_h, L.rl_n, M, e + wid, nwr, L.psum[wid], L.rl_s);
+    }
     lds_barrier();
-    for (int i = tid; i < M1; i += TK_THREADS) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
-  } else {
+    double* cs = P.ws_band_s + base;
+    for (int i = tid; i < M; i += TK_THREADS) cs[L.rl_slot[i]] = L.rl_s[i];
+  }
+}
+
+// Kernel B's steps over the candidates in L.ckey / L.cidx (index order, M1 of
+// them: every entry with key >= lo, lo <= L, where L bounds the k-th key from
+// below). The selection is kept as one bit per candidate position and written
+// out by a scan over the candidates. Returns false, having written nothing,
+// when a capacity is exceeded or the band reaches below lo (the caller then
+// scans every score). The mask was cleared by kernel A: only selected entries
+// are set.
+__device__ bool finish_candidates(const TopkParams& P, FastLds& L, int b, int M1, uint32_t lo, double delta) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int N = P.N, k = P.k;
+  int32_t* ids = P.ids + (size_t)b * k;
+  uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
+  uint32_t* sel = L.sel;  // bit i: candidate i selected
+  const int SW = (M1 + 31) / 32;
+  for (int w = tid; w < SW; w += TK_THREADS) sel[w] = M1 <= k ? ~0u : 0u;  // M1 <= k: every candidate
+  if (M1 > k) {
     // 4. the k-th candidate: histogram bin, then exact ranks inside the bin
     uint32_t cmin = 0xffffffffu, cmx = 0u;
     int dummy = 0;
@@ -637,30 +726,17 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
     lds_barrier();
     const uint32_t T = (uint32_t)L.sc.misc[4];
     if (!P.exact) {
-      for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
-      lds_barrier();
       for (int i = tid; i < M1; i += TK_THREADS) {
-        const uint32_t ki = L.ckey[i];
-        const uint32_t bi = (ki - prefix) >> shift;
-        if (bi > bin_id || (bi == bin_id && L.cflag[i])) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
+        const uint32_t bi = (L.ckey[i] - prefix) >> shift;
+        if (bi > bin_id || (bi == bin_id && L.cflag[i])) atomicOr(&sel[i >> 5], 1u << (i & 31));
       }
     } else {
-      // 5. exact band around T
-      if (tid == 0) {
-        double Q = 0.0, Wa = 0.0;
-        for (int h = 0; h < P.H; h++) {
-          Q += L.qn[h];
-          Wa += L.wa[h];
-        }
-        const double delta = score_err_bound(P.dtype == LIT_BF16, P.H, Q, (double)knorm, Wa);
-        const double t = (double)key_score(T);
-        L.dmisc[2] = t - 2.0 * delta;
-        L.dmisc[3] = t + 2.0 * delta;
-      }
-      lds_barrier();
-      const uint32_t lo0 = score_key(__double2float_rd(L.dmisc[2]));
-      const uint32_t lo = lo0 > 1u ? lo0 : 1u;
-      const uint32_t hi = score_key(__double2float_ru(L.dmisc[3]));
+      // 5. exact band around T: [T - 2 Delta, T + 2 Delta] (Delta as kernel A took it)
+      const double t = (double)key_score(T);
+      const uint32_t blo0 = score_key(__double2float_rd(t - 2.0 * delta));
+      const uint32_t blo = blo0 > 1u ? blo0 : 1u;
+      const uint32_t hi = score_key(__double2float_ru(t + 2.0 * delta));
+      if (blo < lo) return false;  // entries below lo were not listed
       // band members among the candidates (index order) and the sure ones
       const int cseg = (M1 + TK_THREADS - 1) / TK_THREADS;
       const int ca = min(M1, tid * cseg), ce = min(M1, ca + cseg);
@@ -668,29 +744,24 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
       for (int i = ca; i < ce; i++) {
         const uint32_t kk = L.ckey[i];
         nd += kk > hi;
-        nb += (kk >= lo) && (kk <= hi);
+        nb += (kk >= blo) && (kk <= hi);
       }
       int tot;
       int bpos = block_excl_scan((nd << 16) | nb, L.sc.scan, &tot);
       bpos &= 0xffff;
       const int A = tot >> 16;
-      const int Mc = tot & 0xffff;
-      if (Mc > FBAND_CAP) return false;
+      const int M = tot & 0xffff;
+      if (M > FBAND_CAP) return false;
       for (int i = ca; i < ce; i++) {
         const uint32_t kk = L.ckey[i];
-        if ((kk >= lo) && (kk <= hi)) {
+        if (kk > hi) atomicOr(&sel[i >> 5], 1u << (i & 31));
+        if ((kk >= blo) && (kk <= hi)) {
           L.band_n[bpos] = L.cidx[i];
-          L.band_k[bpos] = kk;
+          L.binpos[bpos] = (uint16_t)i;  // the member's candidate position
           bpos++;
         }
       }
       lds_barrier();
-      int M = Mc;
-      if (lo < lkey) {  // entries below L can still sit in the band
-        const int ext = gather_range(sb, N, L.gkey, L.qlist, G, lo, lkey, L.band_k, L.band_n, Mc, FBAND_CAP, &L.sc);
-        if (ext < 0) return false;
-        M += ext;
-      }
       const int rr = k - A;
       if (rr < 1 || rr > M) {
         report_violation(P, b, ids, mask);
@@ -707,7 +778,6 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
         else
           band_scores_bcast<false>(P, b, L.qP, w_h, L.band_n, M, base + wid, nwr, L.psum[wid], L.band_s);
       }
-      for (int w = tid; w < W; w += TK_THREADS) sel[w] = 0u;
       lds_barrier();
       for (int i = tid; i < M; i += TK_THREADS) {
         const double si = L.band_s[i];
@@ -724,34 +794,187 @@ __device__ bool fast_path(const TopkParams& P, FastLds& L, int b) {
 #pragma unroll
           for (int u = 0; u < 8; u++) rank += j0 + u < M && ((sj[u] > si) || (sj[u] == si && nj[u] < ni));
         }
-        if (rank < rr) atomicOr(&sel[ni >> 5], 1u << (ni & 31));
+        if (rank < rr) {
+          const int pos = L.binpos[i];
+          atomicOr(&sel[pos >> 5], 1u << (pos & 31));
+        }
       }
-      for (int i = tid; i < M1; i += TK_THREADS)
-        if (L.ckey[i] > hi) atomicOr(&sel[L.cidx[i] >> 5], 1u << (L.cidx[i] & 31));
     }
   }
   lds_barrier();
 
-  // 6. bitmap -> ascending ids, mask, count
-  const int wseg = (W + TK_THREADS - 1) / TK_THREADS;
-  const int wa = min(W, tid * wseg), we = min(W, wa + wseg);
+  // 6. selected candidates -> ascending ids (candidates are in index order), mask, count
+  const int cseg = (M1 + TK_THREADS - 1) / TK_THREADS;
+  const int ca = min(M1, tid * cseg), ce = min(M1, ca + cseg);
   int c = 0;
-  for (int w = wa; w < we; w++) c += __popc(sel[w]);
+  for (int i = ca; i < ce; i++) c += (sel[i >> 5] >> (i & 31)) & 1u;
   int total;
   int opos = block_excl_scan(c, L.sc.scan, &total);
-  for (int w = wa; w < we; w++) {
-    uint32_t bits = sel[w];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      ids[opos++] = w * 32 + bit;
-      bits &= bits - 1u;
+  for (int i = ca; i < ce; i++)
+    if ((sel[i >> 5] >> (i & 31)) & 1u) {
+      const int n = L.cidx[i];
+      if (opos < k) ids[opos] = n;
+      opos++;
+      if (mask) mask[n] = 1;
     }
-  }
-  if (mask)
-    for (int n = tid; n < N; n += TK_THREADS) mask[n] = (sel[n >> 5] >> (n & 31)) & 1u;
+  total = min(total, k);
   for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
   if (tid == 0) P.count[b] = total;
   return true;
+}
+
+// Kernel B's fast case (exact mode; the candidates, their keys and kernel A's
+// exact scores in LDS): selects the candidates above hx and the best
+// k - (those) of the rescored ones. Returns false, having written nothing,
+// when the test on hx fails (T may lie above hx - 2 Delta).
+__device__ bool finish_rescored(const TopkParams& P, FastLds& L, int b, int M1, uint32_t lo, uint32_t hx,
+                                uint32_t c2) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int N = P.N, k = P.k;
+  const int cseg = (M1 + TK_THREADS - 1) / TK_THREADS;
+  const int ca = min(M1, tid * cseg), ce = min(M1, ca + cseg);
+  int sure = 0, resc = 0, above2 = 0;
+  for (int i = ca; i < ce; i++) {
+    const uint32_t kk = L.ckey[i];
+    sure += kk > hx;
+    resc += kk <= hx;  // every candidate is >= lo
+    above2 += kk > c2;
+  }
+  above2 = wave_sum(above2);
+  if (tid == 0) L.sc.misc[5] = 0;
+  for (int w = tid; w < CAND_CAP / 32; w += TK_THREADS) L.sel[w] = 0u;
+  int tot;
+  int rpos = block_excl_scan((sure << 16) | resc, L.sc.scan, &tot);  // (its barriers order misc[5] = 0)
+  rpos &= 0xffff;
+  if (lane == 0) atomicAdd(&L.sc.misc[5], above2);
+  const int A = tot >> 16, R = tot & 0xffff;
+  for (int i = ca; i < ce; i++) {
+    const uint32_t kk = L.ckey[i];
+    if (kk > hx) atomicOr(&L.sel[i >> 5], 1u << (i & 31));
+    if (kk <= hx && rpos < FBAND_CAP) {
+      L.band_n[rpos] = L.cidx[i];
+      L.band_s[rpos] = L.cexact[i];
+      L.binpos[rpos] = (uint16_t)i;
+      rpos++;
+    }
+  }
+  lds_barrier();
+  const int need = k - A;
+  if (L.sc.misc[5] >= k || R > FBAND_CAP || need < 1 || need > R) return false;
+  // the best `need` rescored candidates by (exact score desc, index asc): the
+  // rank of entry i counted by ballots over 64 entries at a time, one wave per entry
+  for (int i = wid; i < R; i += NWAVES) {
+    const double si = L.band_s[i];
+    int rank = 0;
+    for (int j0 = 0; j0 < R; j0 += 64) {
+      const int j = j0 + lane;
+      const double sj = j < R ? L.band_s[j] : 0.0;
+      rank += __popcll(__ballot(j < R && (sj > si || (sj == si && j < i))));  // the list is in index order
+    }
+    if (lane == 0 && rank < need) {
+      const int ps = L.binpos[i];
+      atomicOr(&L.sel[ps >> 5], 1u << (ps & 31));
+    }
+  }
+  lds_barrier();
+  // selected candidates -> ascending ids, mask, count
+  int32_t* ids = P.ids + (size_t)b * k;
+  uint8_t* mask = P.mask ? P.mask + (size_t)b * N : nullptr;
+  int c = 0;
+  for (int i = ca; i < ce; i++) c += (L.sel[i >> 5] >> (i & 31)) & 1u;
+  int total;
+  int opos = block_excl_scan(c, L.sc.scan, &total);
+  for (int i = ca; i < ce; i++)
+    if ((L.sel[i >> 5] >> (i & 31)) & 1u) {
+      const int n = L.cidx[i];
+      ids[opos++] = n;
+      if (mask) mask[n] = 1;
+    }
+  for (int j = total + tid; j < k; j += TK_THREADS) ids[j] = -1;
+  if (tid == 0) P.count[b] = total;
+  return true;
+}
+
+// Kernel B for row b. Returns false, having written nothing, when the row does
+// not fit (the caller scans every score instead).
+__device__ bool wide_finish(const TopkParams& P, FastLds& L, int b) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int S = P.wide_slices;
+  const int N = P.N;
+  const int G = (N + GROUP - 1) / GROUP;
+  const int GS = (G + S - 1) / S;
+  const int32_t* hdr = P.ws_wide + (size_t)b * WIDE_STRIDE;
+  // every load in one round trip: the slice counts, the header, and the first
+  // 64 entries of each list (wave w holds slices w, w + 16, ...; entries past
+  // a list's capacity read its last slot and are dropped below)
+  const int cword = tid < S ? hdr[WIDE_HDR + tid] : 0;
+  const uint32_t lo = (uint32_t)hdr[1];
+  const int ns = hdr[2];
+  const double delta =
+      __longlong_as_double((long long)(((uint64_t)(uint32_t)hdr[5] << 32) | (uint32_t)hdr[4]));
+  const uint32_t hx = (uint32_t)hdr[6], c2 = (uint32_t)hdr[7];
+  constexpr int SPW = WIDE_SLICES_MAX / NWAVES;  // slices per wave
+  uint32_t sk[SPW];
+  int32_t si[SPW];
+  double sx[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; u++) {
+    const int s = wid + NWAVES * u;
+    const int e0 = GROUP * min(G, s * GS), cap = min(N, GROUP * min(G, s * GS + GS)) - e0;
+    const size_t src = (size_t)b * N + e0 + (size_t)min(lane, max(cap - 1, 0));
+    sk[u] = s < S ? P.ws_ckey[src] : 0u;
+    si[u] = s < S ? P.ws_band_n[src] : 0;
+    sx[u] = s < S && P.exact ? P.ws_band_s[src] : 0.0;  // set only where kernel A rescored
+  }
+  const int cnt = cword & ~(int)WIDE_OVERFLOW;
+  int M1;
+  const int off = block_excl_scan(cnt, L.sc.scan, &M1);
+  const bool overflow = __syncthreads_or((cword & (int)WIDE_OVERFLOW) != 0);
+  if (ns == 0) {  // nothing selectable (the mask is already clear)
+    int32_t* ids = P.ids + (size_t)b * P.k;
+    for (int j = tid; j < P.k; j += TK_THREADS) ids[j] = -1;
+    if (tid == 0) P.count[b] = 0;
+    return true;
+  }
+  // more candidates than LDS holds, or fewer than k although k group maxima
+  // reach L (hints that are not these scores')
+  if (M1 > CAND_CAP || (ns >= P.k && M1 < P.k)) return false;
+  if (tid < S) {
+    L.sc.hist[tid] = (uint32_t)off;
+    L.sc.hist[WIDE_SLICES_MAX + tid] = (uint32_t)cnt;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < SPW; u++) {
+    const int s = wid + NWAVES * u;
+    if (s < S) {
+      const int o = (int)L.sc.hist[s], n = (int)L.sc.hist[WIDE_SLICES_MAX + s];
+      if (lane < n) {
+        L.ckey[o + lane] = sk[u];
+        L.cidx[o + lane] = si[u];
+        L.cexact[o + lane] = sx[u];
+      }
+      if (n > 64) {  // the rest of a long list
+        const size_t src = (size_t)b * N + GROUP * min(G, s * GS);
+        for (int j = 64 + lane; j < n; j += 64) {
+          L.ckey[o + j] = P.ws_ckey[src + j];
+          L.cidx[o + j] = P.ws_band_n[src + j];
+          L.cexact[o + j] = P.exact ? P.ws_band_s[src + j] : 0.0;
+        }
+      }
+    }
+  }
+  lds_barrier();
+  if (P.exact && !overflow && M1 > P.k) {
+    if (finish_rescored(P, L, b, M1, lo, hx, c2)) return true;
+    lds_barrier();
+  }
+  // T taken here, the band rescored here (q staged for it)
+  if (P.exact) {
+    stage_q_rows(P, L.qP, b);  // (the exact scores are no longer read)
+    lds_barrier();
+  }
+  return finish_candidates(P, L, b, M1, lo, delta);
 }
 
 // ---------------------------------------------------------------- small path
@@ -900,6 +1123,28 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
 #pragma unroll
     for (int i = 0; i < GROUP; i++) kv[i] = e0 + i < N ? score_key(sv[i / 4][i % 4]) : 0u;
   }
+  if (P.exact) {
+    // q to LDS for the rescoring: its loads landed with the scores just used,
+    // and the barrier below publishes it
+    if (lane >= P.H) w_h = 0.f;
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (BF16) {
+        x[2 * i] = bf16_lo(qraw[0][i]);
+        x[2 * i + 1] = bf16_hi(qraw[0][i]);
+      } else {
+        x[i] = __uint_as_float(qraw[0][i]);
+        x[4 + i] = __uint_as_float(qraw[1][i]);
+      }
+    }
+    if (qh >= P.H) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) x[i] = 0.f;
+    }
+    *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8] = f32x4{x[0], x[1], x[2], x[3]};
+    *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
+  }
   lds_barrier();
   uint32_t kmx = row_reduce16<false>(L.red_u[0]);
   const uint32_t glo = row_reduce16<true>(L.red_u[1]);
@@ -1041,29 +1286,7 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
   }
   int nsel = 0;  // band entries selected
   if (!all && P.exact) {
-    // q goes to LDS for the rescoring (w_h passes an empty asm first, which
-    // keeps its use, and so the wait for its load, from being hoisted to the
-    // load)
-    asm volatile("" : "+v"(w_h));
-    if (lane >= P.H) w_h = 0.f;
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      if (BF16) {
-        x[2 * i] = bf16_lo(qraw[0][i]);
-        x[2 * i + 1] = bf16_hi(qraw[0][i]);
-      } else {
-        x[i] = __uint_as_float(qraw[0][i]);
-        x[4 + i] = __uint_as_float(qraw[1][i]);
-      }
-    }
-    if (qh >= P.H) {
-#pragma unroll
-      for (int i = 0; i < 8; i++) x[i] = 0.f;
-    }
-    *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8] = f32x4{x[0], x[1], x[2], x[3]};
-    *(f32x4*)&L.rs.qP[qh * QP_STRIDE + 8 * d8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
-    lds_barrier();
+    lds_barrier();  // the band list is complete
     nsel = k - A;
     if (nsel < 1 || nsel > M) {
       report_violation(P, b, ids, mask);
@@ -1336,11 +1559,22 @@ __device__ __forceinline__ int block_row(const TopkParams& P) {
 
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkParams P) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int b = block_row(P);
-  if (P.hints && P.N <= GM_CAP * GROUP) {
-    if (fast_path(P, *reinterpret_cast<FastLds*>(smem), b)) return;
-    __syncthreads();
-  }
+  full_path(P, *reinterpret_cast<FullLds*>(smem), block_row(P));
+}
+
+// Wide path, kernel A: candidate lists of the slices (grid: rows x slices).
+__global__ __launch_bounds__(TK_THREADS) void topk_cand_kernel(TopkParams P) {
+  __shared__ WideLds L;
+  wide_candidates(P, L);
+}
+
+// Wide path, kernel B: one workgroup per row (workgroup b on XCD b % 8, as its
+// lists), which scans every score when the row does not fit.
+__global__ __launch_bounds__(TK_THREADS) void topk_finish_kernel(TopkParams P) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int b = (int)blockIdx.x;
+  if (wide_finish(P, *reinterpret_cast<FastLds*>(smem), b)) return;
+  __syncthreads();
   full_path(P, *reinterpret_cast<FullLds*>(smem), b);
 }
 
@@ -1369,7 +1603,8 @@ extern "C" size_t lit_topk_workspace_bytes(int32_t B, int32_t N, int32_t k) {
   (void)k;
   if (B < 1 || N < 1) return 0;
   const size_t per = (size_t)B * (size_t)N;
-  return round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256) + round_up(per, 256);
+  return round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256) + round_up(per, 256) +
+         round_up((size_t)B * WIDE_STRIDE * sizeof(int32_t), 256) + round_up(per * sizeof(uint32_t), 256);
 }
 
 // B rows of scores; rows kq*s .. kq*s + kq-1 share the keys of sequence s.
@@ -1413,6 +1648,11 @@ static lit_status topk_rows(const float* scores, int32_t B, int32_t kq, int32_t 
   P.ws_band_s = (double*)w8;
   P.ws_band_n = (int32_t*)(w8 + round_up(per * sizeof(double), 256));
   P.ws_band_sel = w8 + round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256);
+  P.ws_wide = (int32_t*)(w8 + round_up(per * sizeof(double), 256) + round_up(per * sizeof(int32_t), 256) +
+                         round_up(per, 256));
+  P.ws_ckey = (uint32_t*)((uint8_t*)P.ws_wide + round_up((size_t)B * WIDE_STRIDE * sizeof(int32_t), 256));
+  P.rows = B;
+  P.wide_slices = 1;
   if (N <= TK_THREADS * GROUP) {
     const size_t lds = std::max(sizeof(FullLds), sizeof(SmallLds));
     const bool bf16 = P.exact && P.dtype == LIT_BF16;
@@ -1427,9 +1667,26 @@ static lit_status topk_rows(const float* scores, int32_t B, int32_t kq, int32_t 
     return LIT_OK;
   }
   const size_t lds = std::max(sizeof(FullLds), sizeof(FastLds));
-  lit_status st = allow_lds((const void*)topk_kernel, lds, who);
+  hipStream_t hs = (hipStream_t)stream;
+  if (hints && N <= GM_CAP * GROUP) {
+    // wide path: about 512 candidate workgroups in all, at least enough
+    // slices that one slice's groups fit one workgroup
+    const int G = (int)cdiv(N, GROUP);
+    const int s_min = (int)cdiv(G, TK_THREADS);
+    P.wide_slices = std::min(WIDE_SLICES_MAX, std::max(s_min, (int)cdiv(512, B)));
+    const int64_t ga = (int64_t)B * P.wide_slices;
+    if (ga > INT32_MAX) return fail(LIT_ERR_SHAPE, "%s: %d rows too many for the candidate grid", who, B);
+    lit_status st = allow_lds((const void*)topk_finish_kernel, lds, who);
+    if (st != LIT_OK) return st;
+    topk_cand_kernel<<<dim3((unsigned)ga), dim3(TK_THREADS), 0, hs>>>(P);
+    LIT_CHECK_LAUNCH(who);
+    topk_finish_kernel<<<dim3((unsigned)B), dim3(TK_THREADS), lds, hs>>>(P);
+    LIT_CHECK_LAUNCH(who);
+    return LIT_OK;
+  }
+  lit_status st = allow_lds((const void*)topk_kernel, sizeof(FullLds), who);
   if (st != LIT_OK) return st;
-  topk_kernel<<<dim3((unsigned)B), dim3(TK_THREADS), lds, (hipStream_t)stream>>>(P);
+  topk_kernel<<<dim3((unsigned)B), dim3(TK_THREADS), sizeof(FullLds), hs>>>(P);
   LIT_CHECK_LAUNCH(who);
   return LIT_OK;
 }

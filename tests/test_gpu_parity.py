@@ -99,6 +99,10 @@ SEL_CASES = [
     ("pro_k1024", W.CTX64K, 3, 16384, 1024),
     ("ctx500k", W.CTX500K, 1, None, 512),
     ("full_scan_140k", W.CTX64K, 1, 140000, 512),
+    # the two-kernel path for long rows: several rows, and more than eight rows
+    # (the candidate grid pads each group of eight)
+    ("wide_b3_n40000", W.CTX64K, 3, 40000, 512),
+    ("wide_b9_n20000", W.CTX64K, 9, 20000, 256),
 ]
 
 
@@ -168,6 +172,37 @@ def test_gated_candidate_set():
     check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, "gated")
     assert cnt.cpu().tolist() == [300, 512]
     assert (mask.cpu() <= allowed).all()
+
+
+def test_gated_candidate_set_long_rows():
+    # the two-kernel path with a gate: a row with fewer selectable entries than
+    # k (its candidates are every selectable entry) and a row gated to 3/4
+    N = 40000
+    inp = W.layer_inputs(W.CTX64K, 0, "cpu", B=2, N=N).idx
+    allowed = torch.zeros(2, N, dtype=torch.uint8)
+    allowed[0, torch.randperm(N, generator=torch.Generator().manual_seed(3))[:300]] = 1
+    allowed[1, torch.randperm(N, generator=torch.Generator().manual_seed(4))[:30000]] = 1
+    scores, hints, ids, cnt, mask = run_select(inp, 512, allowed=allowed)
+    s64, rids, rcnt, rmask = oracle_select(inp, 512, allowed.numpy())
+    check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, "gated long rows")
+    assert cnt.cpu().tolist() == [300, 512]
+
+
+def test_long_rows_with_a_block_of_equal_top_scores():
+    # 400 entries of row 0 share the key of its best entry: their exact scores
+    # tie at the top and top-300 takes the 300 lowest indices among them. The
+    # two-kernel path cannot rescore them all in one slice and takes its
+    # in-row fallback; row 1 is ordinary
+    N, k = 40000, 300
+    inp = W.layer_inputs(W.CTX64K, 2, "cpu", B=2, N=N).idx
+    s = oracle.idx_score(inp.q_idx, inp.w, inp.k_idx)
+    best = int(np.argmax(s[0]))
+    inp.k_idx[0, 1000:1400] = inp.k_idx[0, best]
+    scores, hints, ids, cnt, mask = run_select(inp, k)
+    s64, rids, rcnt, rmask = oracle_select(inp, k)
+    check_selection(ids, cnt, mask, rids, rcnt, rmask, s64, "equal top block")
+    sel = set(ids.cpu().numpy()[0].tolist())
+    assert set(range(1000, 1300)) <= sel | {best}
 
 
 def test_topk_on_given_scores_with_heavy_ties():
