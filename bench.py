@@ -19,7 +19,7 @@ the eager result) and replayed. Besides the headline line the JSON carries:
                  streams from HBM), the LSA cold-pool fetch, the lookahead
                  golden and the recall chain (gate, gated and native top-1024,
                  vote labels) at the gate workload's shapes.
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only lookahead|prefill|offload|recall]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only lookahead|prefill|offload|recall|ctx500k]
 """
 from __future__ import annotations
 
@@ -192,7 +192,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--only", choices=["lookahead", "prefill", "offload", "recall"],
+    ap.add_argument("--only", choices=["lookahead", "prefill", "offload", "recall", "ctx500k"],
                     help="run one secondary measurement alone and print its JSON (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -224,7 +224,8 @@ def main():
     scale = 1.0 / math.sqrt(512)
     if args.only:
         fn = {"lookahead": lookahead, "prefill": lambda lit, W, dev, scale: prefill(lit, W, dev),
-              "offload": offload, "recall": gate_recall}[args.only]
+              "offload": offload, "recall": gate_recall,
+              "ctx500k": lambda lit, W, dev, scale: ctx500k(lit, W, dev, scale)[0]}[args.only]
         print(json.dumps({args.only: fn(lit, W, dev, scale)}))
         return
     wl = W.CTX64K_B
@@ -565,25 +566,12 @@ def lookahead(lit, W, dev, scale):
     return res
 
 
-def others(lit, W, dev, scale):
-    """Secondary figures: 64K batch-1 latency and the 500K batch-4 step."""
+def ctx500k(lit, W, dev, scale):
+    """The 500K batch-4 figures: one CSA layer step and one HCA layer; returns
+    them with the layers' inputs (for the token step)."""
     import torch
     from lightning_indexer_top_idx_amd.step import CsaLayer
 
-    res = {}
-    # 64K, batch 1: 32 independent layers rotated so the data exceeds the 256 MB cache
-    wl = W.CTX64K
-    n_rot = 32
-    layers = [W.layer_inputs(wl, 100 + l, dev) for l in range(n_rot)]
-    paths = [CsaLayer(L, wl.k, wl.window, scale, dev) for L in layers]
-    g = capture(lambda s: [P.run(s) for P in paths])
-    g.replay()
-    sec = time_graph(g, 5)
-    per_q = sec / (5 * n_rot)
-    res["ctx64k_b1"] = {"us_per_query": round(per_q * 1e6, 2), "queries_per_s": round(1 / per_q, 1),
-                        "note": "batch 1, one query per step; 32 distinct layers replayed back to back in a graph"}
-    del g, paths, layers
-    torch.cuda.empty_cache()
     # 500K, batch 4: one CSA layer (N=125000) + one HCA layer (3907 rows read
     # densely). Distinct layers are rotated (3 CSA layers, 384 MB of keys; 24
     # copies of the HCA rows, 384 MB) so that no replay finds its data in the
@@ -609,11 +597,34 @@ def others(lit, W, dev, scale):
     csa_s = time_graph(gc, 10) / (10 * n_csa)
     hca_s = time_graph(gh, 10) / (10 * n_hca)
     per_query = algo_bytes_per_query(wl.N, wl.H, wl.k, wl.window, wl.Hq)
-    res["ctx500k_b4"] = {"csa_step_us": round(csa_s * 1e6, 2), "queries_per_s": round(wl.B / csa_s, 1),
-                         "hbm_frac": round(per_query * wl.B / csa_s / 1e9 / HBM_PEAK_GBS, 4),
-                         "hca_layer_us": round(hca_s * 1e6, 2),
-                         "hca_hbm_frac": round(wl.B * wl.hca_N * 1024 / hca_s / 1e9 / HBM_PEAK_GBS, 4)}
+    r = {"csa_step_us": round(csa_s * 1e6, 2), "queries_per_s": round(wl.B / csa_s, 1),
+         "hbm_frac": round(per_query * wl.B / csa_s / 1e9 / HBM_PEAK_GBS, 4),
+         "hca_layer_us": round(hca_s * 1e6, 2),
+         "hca_hbm_frac": round(wl.B * wl.hca_N * 1024 / hca_s / 1e9 / HBM_PEAK_GBS, 4)}
     del gc, gh, hout, hws
+    return r, csa_paths, hq, hkvs
+
+
+def others(lit, W, dev, scale):
+    """Secondary figures: 64K batch-1 latency and the 500K batch-4 step."""
+    import torch
+    from lightning_indexer_top_idx_amd.step import CsaLayer
+
+    res = {}
+    # 64K, batch 1: 32 independent layers rotated so the data exceeds the 256 MB cache
+    wl = W.CTX64K
+    n_rot = 32
+    layers = [W.layer_inputs(wl, 100 + l, dev) for l in range(n_rot)]
+    paths = [CsaLayer(L, wl.k, wl.window, scale, dev) for L in layers]
+    g = capture(lambda s: [P.run(s) for P in paths])
+    g.replay()
+    sec = time_graph(g, 5)
+    per_q = sec / (5 * n_rot)
+    res["ctx64k_b1"] = {"us_per_query": round(per_q * 1e6, 2), "queries_per_s": round(1 / per_q, 1),
+                        "note": "batch 1, one query per step; 32 distinct layers replayed back to back in a graph"}
+    del g, paths, layers
+    torch.cuda.empty_cache()
+    res["ctx500k_b4"], csa_paths, hq, hkvs = ctx500k(lit, W, dev, scale)
     # the whole attention step of a token at 500K: the three CSA layers above
     # in turn, the 24 copies of the HCA rows in turn
     print("[bench] token step at 500K", file=sys.stderr, flush=True)

@@ -66,24 +66,28 @@ __device__ __forceinline__ float e8m0_f32(uint32_t b) {
   return __uint_as_float(b << 23);
 }
 
-// Row index of list position p for sequence b; -1 = skip (window row that is
-// already among the ids, or past the end).
+typedef const __attribute__((address_space(3))) int32_t* lds_ids_t;
+
 struct RowList {
   const int32_t* ids;
+  lds_ids_t lids;  // the ids' copy in LDS, or null: read as LDS, not through a generic pointer
   int c, N, Wc, total;
   bool dense;
-  const uint32_t* dup;  // LDS bitmap over the window rows
-  // The global read behind list position p (any p: the index is clamped into
-  // the ids, so the load needs no branch and can be issued ahead of its use).
-  __device__ __forceinline__ int fetch(int p) const { return (!dense && c > 0) ? ids[max(min(p, c - 1), 0)] : 0; }
-  // The row of list position p, given f = fetch(p).
+  // The read behind list position p (any p: the index is clamped into the
+  // ids, so the load needs no branch and can be issued ahead of its use).
+  __device__ __forceinline__ int fetch(int p) const {
+    if (dense || c <= 0) return 0;
+    const int j = max(min(p - Wc, c - 1), 0);
+    return lids ? lids[j] : ids[j];
+  }
+  // The row of list position p, given f = fetch(p): positions 0 .. Wc-1 are
+  // the window rows N-Wc .. N-1, then the ids follow; an id inside the window
+  // (already attended) or outside the rows is skipped.
   __device__ __forceinline__ int resolve(int p, int f) const {
     if (p >= total) return -1;
     if (dense) return p;
-    if (p < c) return (f >= 0 && f < N) ? f : -1;  // ids outside the rows are skipped
-    const int j = p - c;
-    if ((dup[j >> 5] >> (j & 31)) & 1u) return -1;
-    return N - Wc + j;
+    if (p < Wc) return N - Wc + p;
+    return (f >= 0 && f < N - Wc) ? f : -1;
   }
   __device__ __forceinline__ int row(int p) const { return resolve(p, fetch(p)); }
 };
@@ -194,7 +198,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
                                                        float scale, float* __restrict__ out, float* __restrict__ lse) {
   __shared__ float xs[1024];
   __shared__ int rs[1024];
-  __shared__ uint32_t dup[LIT_MAX_WINDOW / 32];
   __shared__ float red[8];
   const int b = blockIdx.x / Hq, h = blockIdx.x % Hq;
   const int tid = threadIdx.x;
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
   RowList RL;
   RL.dense = ids == nullptr;
   RL.N = N;
-  RL.dup = dup;
+  RL.lids = nullptr;
   if (RL.dense) {
     RL.ids = nullptr;
     RL.c = 0;
@@ -217,14 +220,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
     RL.c = c;
     RL.Wc = window;
     RL.total = c + window;
-    for (int i = tid; i < (window + 31) / 32; i += 256) dup[i] = 0u;
-    __syncthreads();
-    for (int j = tid; j < c; j += 256) {
-      const int id = RL.ids[j];
-      if (id >= N - window && id < N) atomicOr(&dup[(id - (N - window)) >> 5], 1u << ((id - (N - window)) & 31));
-    }
   }
-  __syncthreads();
   const float* qh = q + ((size_t)b * Hq + h) * LIT_KV_DIM;
   const float* kvb = kv + (size_t)b * N * LIT_KV_DIM;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
@@ -325,6 +321,9 @@ __device__ __forceinline__ void mh_issue_q(const AttnParams& P, int b, int hg, M
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// vmcnt(16): all but the last 16 loads (one tile's rows of this wave) have landed
+__device__ __forceinline__ void wait_vm_tile() { __builtin_amdgcn_s_waitcnt(0x4F70); }
+static_assert(MH_ROWS_PER_WAVE == 16, "wait_vm_tile counts one load per row");
 
 struct MhState {
   f32x4 o[8];   // O[head c16][dim 128 w + 16 nt + 4g + i]
@@ -547,7 +546,6 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   __shared__ MhTile TA, TB;
   __shared__ __align__(16) uint16_t pbuf[MH_HEADS * MH_PS];
   __shared__ __align__(16) int rows_all[MH_ROWS_CAP];  // the slice's rows, or a ring of 4 tiles for long dense slices
-  __shared__ uint32_t dup[LIT_MAX_WINDOW / 32];
   __shared__ float smax[MH_WAVES][16];
   __shared__ float ssum[MH_WAVES][16];
   __shared__ int part[16];
@@ -559,86 +557,142 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int Hq = P.Hq;
+  const size_t seq_rows = (size_t)b * P.N;
+  // the count as a scalar load (issued first: its wait does not hold the
+  // vector loads below)
+  const int count_b = P.ids ? *(const __attribute__((address_space(4))) int32_t*)(P.count + b) : 0;
   // the queries travel first, into the second tile buffer, while the row list is built
   mh_issue_q(P, b, hg, TB);
   // The sequence's ids travel with them (all k_cap, so that their copy does not
   // wait for the count), into the same buffer after the 16 query rows; the
-  // duplicate test and the row list then read LDS, and the count's load and
-  // the ids' copy are one round trip instead of three dependent ones.
+  // row list then reads LDS, and the count's load and the ids' copy are one
+  // round trip instead of two dependent ones.
   int* ids_l = reinterpret_cast<int*>(TB.v + MH_HEADS * MH_RS);
   const bool ids_cached = P.ids != nullptr && P.k_cap <= MH_IDS_CACHE;
   if (ids_cached) {
+    // a fixed count of copies per wave (slots past k_cap repeat the last id and
+    // are never read), so that the loads issued after them are counted exactly
     const int32_t* src = P.ids + (size_t)b * P.k_cap;
-    for (int j0 = 64 * wid; j0 < P.k_cap; j0 += 64 * MH_WAVES)
+#pragma unroll
+    for (int it = 0; it < MH_IDS_CACHE / (64 * MH_WAVES); it++) {
+      const int j0 = 64 * (wid + MH_WAVES * it);
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + min(j0 + lane, P.k_cap - 1)),
                                        (__attribute__((address_space(3))) void*)(ids_l + j0), 4, 0, 0);
+    }
   }
+  // A selection's list holds the window rows first, and slice s takes the
+  // list's tiles s, s + splits, ...: when its first tile is window rows (BF16),
+  // their rows are known now and their loads go out behind the ids', into
+  // registers, so that they land while the ids are read and the row list is
+  // built (loads into registers, not LDS: reads of LDS would otherwise wait
+  // for them). They are stored to the first tile buffer before the tile loop.
+  const bool early = !FP8 && P.ids != nullptr && P.window >= MH_TR * (s + 1);
+  u32x4 t0[MH_ROWS_PER_WAVE];
+  __builtin_amdgcn_sched_barrier(0);  // the ids' copy is issued before these loads
+  if (early) {
+#pragma unroll
+    for (int i = 0; i < MH_ROWS_PER_WAVE; i++) {
+      const size_t rr = seq_rows + (size_t)(P.N - P.window + MH_TR * s + MH_ROWS_PER_WAVE * wid + i);
+      t0[i] = *(const u32x4*)((const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
   bool bad = false;  // count[b] < 0: the selection failed; the outputs say so with NaN
   RowList RL;
   RL.dense = P.ids == nullptr;
   RL.N = P.N;
-  RL.dup = dup;
+  RL.lids = ids_cached ? (lds_ids_t)ids_l : nullptr;
   if (RL.dense) {
     RL.ids = nullptr;
     RL.c = 0;
     RL.Wc = 0;
     RL.total = P.N;
   } else {
-    RL.ids = ids_cached ? ids_l : P.ids + (size_t)b * P.k_cap;
+    RL.ids = P.ids + (size_t)b * P.k_cap;
     const int cap = min(P.k_cap, P.N);
-    int c = P.count[b];
+    int c = count_b;
     bad = c < 0;
     c = c < 0 ? 0 : (c > cap ? cap : c);
     RL.c = c;
     RL.Wc = P.window;
     RL.total = c + P.window;
   }
-  if (ids_cached) wait_vm0();  // this wave's share of the ids (and queries) has landed
-  lds_barrier();               // ... and every wave's
-  const int p0 = s * P.rows_per_split;
-  const int p1 = min(RL.total, p0 + P.rows_per_split);
-  if (!RL.dense && p1 > RL.c && RL.Wc > 0) {
-    for (int i = tid; i < (RL.Wc + 31) / 32; i += MH_THREADS) dup[i] = 0u;
-    lds_barrier();
-    const int lo = P.N - RL.Wc;
-    for (int j = tid; j < RL.c; j += MH_THREADS) {
-      const int id = RL.ids[j];
-      if (id >= lo && id < P.N) atomicOr(&dup[(id - lo) >> 5], 1u << ((id - lo) & 31));
-    }
+  if (ids_cached) {
+    // this wave's share of the ids (and queries) has landed; the first tile's
+    // loads, issued after them, may still be in flight
+    if (early)
+      wait_vm_tile();
+    else
+      wait_vm0();
   }
-  lds_barrier();
+  lds_barrier();  // ... and every wave's
   // Every row of a selection slice is resolved here (the planner keeps those
   // slices within MH_ROWS_CAP) and compacted, so the attended rows are list
   // positions 0 .. n-1 and the tile loop reads nothing but the tiles. Longer
   // slices are dense: their rows are their positions, computed per tile.
-  const int nrows = max(p1 - p0, 0);
-  const bool all_rows = !RL.dense && nrows <= MH_ROWS_CAP;  // dense slices: rows are positions
-  int n = nrows;  // attended rows of the slice
+  const bool all_rows = !RL.dense;
+  int n;                        // attended rows of the slice
+  int p0 = 0, p1 = 0;           // a dense slice's positions
   if (all_rows) {
+    // slice-local index i -> list position: tile s + splits * (i / MH_TR)
+    const int T = (RL.total + MH_TR - 1) / MH_TR;
+    const int ntile = T > s ? (T - s + P.splits - 1) / P.splits : 0;
+    const int i0 = early ? MH_TR : 0;  // an early first tile is complete: 64 window rows
+    const int nloc = ntile * MH_TR;
     constexpr int PER = (MH_ROWS_CAP + MH_THREADS - 1) / MH_THREADS;
-    int r[PER];
+    static_assert(PER == 5, "the LDS reads below are written out for five positions per thread");
+    int r[PER], p[PER], f[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int i = i0 + tid + MH_THREADS * k;
+      p[k] = i < nloc ? MH_TR * (s + P.splits * (i / MH_TR)) + i % MH_TR : RL.total;
+    }
+    if (RL.lids && RL.c > 0) {
+      // the ids from LDS in one asm block that waits for its own reads: the
+      // compiler would otherwise make each read wait for every load in flight
+      // (it cannot tell this copy, which has landed, from the tile loads)
+      uint32_t a[PER];
+#pragma unroll
+      for (int k = 0; k < PER; k++)
+        a[k] = (uint32_t)(uintptr_t)(RL.lids + max(min(p[k] - RL.Wc, RL.c - 1), 0));
+      asm volatile(
+          "ds_read_b32 %0, %5\n\tds_read_b32 %1, %6\n\tds_read_b32 %2, %7\n\tds_read_b32 %3, %8\n\t"
+          "ds_read_b32 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+          : "=v"(f[0]), "=v"(f[1]), "=v"(f[2]), "=v"(f[3]), "=v"(f[4])
+          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+          : "memory");
+    } else {
+#pragma unroll
+      for (int k = 0; k < PER; k++) f[k] = RL.fetch(p[k]);
+      // (their loads waited for here, on this path only: where the two paths
+      // meet, f holds nothing in flight)
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < PER; k++) {
-      const int i = tid + MH_THREADS * k;
-      r[k] = i < nrows ? RL.row(p0 + i) : -1;
+      r[k] = RL.resolve(p[k], f[k]);
       cnt += r[k] >= 0;
     }
     int pos = block_excl_scan1<MH_WAVES>(cnt, part, &n);
+    pos += i0;
 #pragma unroll
     for (int k = 0; k < PER; k++)
       if (r[k] >= 0) rows_all[pos++] = r[k];
+    n += i0;
     lds_barrier();
     const int upto = (n + MH_TR - 1) / MH_TR * MH_TR;
-    for (int i = n + tid; i < upto; i += MH_THREADS) rows_all[i] = -1;
+    for (int i = max(n, i0) + tid; i < upto; i += MH_THREADS) rows_all[i] = -1;
   } else {
+    p0 = s * P.rows_per_split;
+    p1 = min(RL.total, p0 + P.rows_per_split);
+    n = max(p1 - p0, 0);
     for (int i = tid; i < 2 * MH_TR; i += MH_THREADS) {
       const int p = p0 + i;
       rows_all[i] = p < p1 ? p : -1;
     }
   }
-  const size_t seq_rows = (size_t)b * P.N;
   // (one LDS array, so that the compiler can tell its reads from the tile loads in flight)
   auto tile_rows = [&](int tt) -> const int* { return rows_all + MH_TR * (all_rows ? tt : (tt & 3)); };
   // a dense slice's first tile needs no row list: its loads go out now,
@@ -649,13 +703,20 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   }
   // the queries as B operands, from the second tile buffer: K-step j, lane
   // (g, c16) holds dims 32j + 8g .. +7 of head c16 of the group
-  wait_vm0();
+  if (early)
+    wait_vm_tile();
+  else
+    wait_vm0();
   lds_barrier();
   u32x4 qreg[16];
 #pragma unroll
   for (int j = 0; j < 16; j++) qreg[j] = *(const u32x4*)(TB.v + c16 * MH_RS + 32 * j + 8 * g);
+  if (early) {
+#pragma unroll
+    for (int i = 0; i < MH_ROWS_PER_WAVE; i++) *(u32x4*)(TA.v + (MH_ROWS_PER_WAVE * wid + i) * MH_RS + 8 * lane) = t0[i];
+  }
   lds_barrier();
-  if (all_rows && 0 < n) mh_issue<FP8>(P, seq_rows, tile_rows(0), TA);
+  if (all_rows && !early && 0 < n) mh_issue<FP8>(P, seq_rows, tile_rows(0), TA);
 
   MhState S;
 #pragma unroll
