@@ -222,3 +222,32 @@ def test_attn_noalloc_validation(L):
                                             p(0x2000), None, None) == 3
     assert L.lit_sparse_attn_decode_noalloc(p(0x3000), 1, 64, ctypes.byref(kv), 4, p(0x4000), None, 512, 128, 0.04,
                                             p(0x2000), None, None) == 1  # ids without count
+
+
+def _gpu_visible():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:  # no torch: count as no GPU
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="would launch kernels on made-up addresses where a GPU is present")
+def test_launch_failure_is_reported_without_a_device(L):
+    # valid arguments reach the launch; with no GPU the runtime refuses it and
+    # every entry point returns LIT_ERR_LAUNCH (6) with the runtime's reason
+    p = ctypes.c_void_p
+    st = L.lit_recall(p(0x1000), p(0x2000), 1, 100, p(0x3000), None, None, None)
+    assert st == 6 and "launch failed" in lit.last_error(), lit.last_error()
+    desc = _idx()
+    st = L.lit_idx_score(ctypes.byref(desc), None, 1, 1000, p(0x5000), None, None)
+    assert st == 6 and "launch failed" in lit.last_error(), lit.last_error()
+    kv = lit.KVDesc(1, 1000, 0x1000, None, None)
+    st = L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv), 1, None, None, 0, 0, 0.04, p(0x2000), None,
+                                  p(0x7000), 1 << 30, None)
+    assert st == 6 and "launch failed" in lit.last_error(), lit.last_error()
+    # the allocation-free call finds no device to look its scratch array up on
+    st = L.lit_sparse_attn_decode_noalloc(p(0x3000), 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04, p(0x2000),
+                                          None, None)
+    assert st == 6, lit.last_error()

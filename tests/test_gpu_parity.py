@@ -251,6 +251,19 @@ def test_topk_with_hints_of_other_scores_falls_back():
             check_selection(ids, cnt, mask, rids, rcnt, rmask, None, f"other hints N={N} x{scale}")
 
 
+def test_score_launch_arrangements_agree_bit_for_bit():
+    # the headline batch (32 sequences, four chunks per workgroup, workgroups
+    # paired) and sequences of it scored in smaller batches (one chunk per
+    # workgroup, unpaired) run the same per-entry arithmetic
+    inp = W.layer_inputs(W.CTX64K_B, 3, "cuda").idx
+    s32, h32 = lit.idx_score(inp.q_idx, inp.w, inp.k_idx)
+    for lo, hi in ((0, 8), (16, 24), (29, 30)):
+        s, h = lit.idx_score(inp.q_idx[lo:hi].contiguous(), inp.w[lo:hi].contiguous(), inp.k_idx[lo:hi].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(s, s32[lo:hi]), (lo, hi)
+        assert torch.equal(h.view(torch.int32), h32[lo:hi].view(torch.int32)), (lo, hi)
+
+
 def test_idx_score_exact_matches_oracle_bit_for_bit():
     for wl, B, N in ((W.TINY, None, None), (W.CTX64K, 2, 3001)):
         inp = W.layer_inputs(wl, 0, "cpu", B=B, N=N).idx
@@ -286,6 +299,26 @@ def test_sparse_attention(name, wl, B, N, k, window):
     ref, rlse = oracle.attend(L.q, L.kv, rids, rcnt, window, SCALE)
     assert_attn_close(out, ref)
     np.testing.assert_allclose(lse.double().cpu().numpy(), rlse, atol=2e-3, rtol=0)
+
+
+def test_attention_head_counts():
+    # one head block per workgroup (Hq <= 16), two (Hq > 16), and a partial
+    # second block (Hq = 48: heads 48..63 of the last group are not written)
+    L = W.layer_inputs(W.CTX64K, 1, "cpu", B=3, N=2500)
+    rids, rcnt, _ = oracle_ids(L.idx, 512)
+    for Hq in (8, 16, 48, 64):
+        print(f"case attention Hq={Hq}", flush=True)
+        q = synth.make_q(3, Hq, "bf16", torch.Generator().manual_seed(40 + Hq), "cpu")
+        out, lse = lit.sparse_attn_decode(q.cuda(), kv_dev(L.kv), dev(torch.from_numpy(rids)),
+                                          dev(torch.from_numpy(rcnt)), 128, SCALE)
+        dense, dlse = lit.sparse_attn_decode(q.cuda(), kv_dev(L.kv), None, None, 0, SCALE)
+        torch.cuda.synchronize()
+        ref, rlse = oracle.attend(q, L.kv, rids, rcnt, 128, SCALE)
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(lse.double().cpu().numpy(), rlse, atol=2e-3, rtol=0)
+        dref, drlse = oracle.attend(q, L.kv, None, None, 0, SCALE)
+        assert_attn_close(dense, dref)
+        np.testing.assert_allclose(dlse.double().cpu().numpy(), drlse, atol=2e-3, rtol=0)
 
 
 def test_attention_counts_below_cap_duplicates_and_empty():
