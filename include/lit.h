@@ -102,7 +102,11 @@ typedef enum {
   LIT_BF16 = 1,
   /* [ARCH] KV precision: dims 0..447 are OCP E4M3FN bytes, one E8M0 power-of-two
    * scale byte per 64-dim group (value 2^(byte-127)); dims 448..511 are BF16. */
-  LIT_FP8E4M3_G64_ROPE_BF16 = 2
+  LIT_FP8E4M3_G64_ROPE_BF16 = 2,
+  /* Not a dtype: spans the enum over every int32 value, so that a value a C
+   * caller passes outside the list above reaches the library as an ordinary
+   * value (refused with LIT_ERR_DTYPE) rather than one C++ may assume away. */
+  LIT_DTYPE_INT32_RANGE_ = 0x7fffffff
 } lit_dtype;
 
 /* Inputs of the lightning indexer ([ARCH] (B); score form from [LSA] reply

@@ -19,7 +19,9 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblit.so")
+# LIT_LIBRARY names another build of the same library (the tests' sanitized
+# host build); there is no other implementation behind this binding
+LIB_PATH = os.environ.get("LIT_LIBRARY", os.path.join(_HERE, "liblit.so"))
 
 LIT_F32, LIT_BF16, LIT_FP8 = 0, 1, 2
 IDX_DIM = 128

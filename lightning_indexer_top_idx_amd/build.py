@@ -31,28 +31,38 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# The host code checked by AddressSanitizer and UndefinedBehaviorSanitizer
+# (argument validation, planning, error reporting); the GPU code is built as
+# usual. Loaded only with the sanitizer runtime preloaded (a CPU test does so).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+LIB_SANITIZED = os.path.join(BUILD, "liblit_sanitized.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + (".san.o" if sanitize else ".o"))
+    cmd = [HIPCC, *FLAGS, *(SANITIZE if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Builds liblit.so, or with sanitize=True the host-sanitized copy in _build/."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
-                       capture_output=True, text=True)
+        objs = list(ex.map(lambda f: _compile(f, sanitize), SOURCES))
+    out = LIB_SANITIZED if sanitize else LIB
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(SANITIZE if sanitize else []), "-o", tmp,
+                        *objs], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

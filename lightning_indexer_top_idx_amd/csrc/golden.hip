@@ -467,17 +467,20 @@ struct GoldenWs {
   size_t bytes;
 };
 
+// Byte `off` of a workspace, or NULL when only its size is being measured
+// (base NULL: no pointer is formed from it).
+uint8_t* ws_at(void* base, size_t off) { return base ? (uint8_t*)base + off : nullptr; }
+
 GoldenWs golden_ws(void* base, int B, int Hq, int N) {
   GoldenWs w;
-  uint8_t* p = (uint8_t*)base;
   size_t off = 0;
-  w.X = (double*)(p + off);
+  w.X = (double*)ws_at(base, off);
   off += round_up((size_t)B * Hq * N * sizeof(double), 256);
-  w.stats = (double*)(p + off);
+  w.stats = (double*)ws_at(base, off);
   off += round_up((size_t)B * Hq * 2 * sizeof(double), 256);
-  w.pbar = (double*)(p + off);
+  w.pbar = (double*)ws_at(base, off);
   off += round_up((size_t)B * N * sizeof(double), 256);
-  w.sel = p + off;
+  w.sel = ws_at(base, off);
   off += round_up((size_t)B * N, 256);
   w.bytes = off;
   return w;
@@ -591,15 +594,14 @@ struct LookaheadWs {
 LookaheadWs lookahead_ws(void* base, int B, int T, int Hq, int N, int k) {
   LookaheadWs w;
   w.g = golden_ws(base, B * T, Hq, N);
-  uint8_t* p = (uint8_t*)base;
   size_t off = w.g.bytes;
-  w.ids = (int32_t*)(p + off);
+  w.ids = (int32_t*)ws_at(base, off);
   off += round_up((size_t)B * T * k * sizeof(int32_t), 256);
-  w.cnt = (int32_t*)(p + off);
+  w.cnt = (int32_t*)ws_at(base, off);
   off += round_up((size_t)B * T * sizeof(int32_t), 256);
-  w.mask = p + off;
+  w.mask = ws_at(base, off);
   off += round_up((size_t)B * T * N, 256);
-  w.umask = p + off;
+  w.umask = ws_at(base, off);
   off += round_up((size_t)B * N, 256);
   w.bytes = off;
   return w;

@@ -22,6 +22,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZED=1: the same source built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (loaded with the sanitizer runtime preloaded)
+_SANITIZED = os.environ.get("ORACLE_SANITIZED") == "1"
+if _SANITIZED:
+    _LIB_PATH = os.path.join(_HERE, "..", "_build", "liboracle_sanitized.so")
 
 F32, BF16, FP8 = 0, 1, 2
 IDX_DIM = 128
@@ -37,9 +42,11 @@ def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (no FP contraction, no fast-math)."""
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+        os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
         subprocess.run(
             ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-             "-o", tmp, _SRC, "-lm"],
+             *(san if _SANITIZED else []), "-o", tmp, _SRC, "-lm"],
             check=True,
         )
         os.replace(tmp, _LIB_PATH)
