@@ -322,6 +322,91 @@ __device__ __forceinline__ void band_scores_bcast(const TopkParams& P, int b, co
   }
   wave_sync();  // psum is refilled by the next round
 }
+
+// The same fp64 canonical scores with one entry per wave and round: entry
+// band_n[w + nw * j] in round j of wave w (w < nw), so that no wave computes a
+// padding slot and a short band spreads over all nw waves (fp64 issue runs at
+// one instruction per ~8 cycles for a lone wave on its SIMD, ~4.5 with four).
+// For M <= nw * BW. The key dwords of every round are requested first, in one
+// round trip; the rounds' head terms go to psum[j], and lane j adds round j's
+// in head order at the end.
+#define LIT_FMAC1(N, A, KA, KB, QA, QB)                                                   \
+  asm volatile("s_nop 1\n\t" LIT_FMAC_LINE(0, 1, 3, N) LIT_FMAC_LINE(0, 2, 4, N)          \
+               : "+v"(A)                                                                  \
+               : "v"(KA), "v"(KB), "v"(QA), "v"(QB))
+#define LIT_ROUND_STEP(N)                                               \
+  {                                                                     \
+    const double q0 = (double)qv[((N) >> 1) & 1][2 * ((N)&1)];          \
+    const double q1 = (double)qv[((N) >> 1) & 1][2 * ((N)&1) + 1];      \
+    LIT_FMAC1(N, acc, kA, kB, q0, q1);                                  \
+  }
+#define LIT_ROUND_QUARTER(U, S0, S1, S2, S3)                                            \
+  {                                                                                     \
+    qv[0] = qn[0];                                                                      \
+    qv[1] = qn[1];                                                                      \
+    if (32 * c + 8 * (U) + 8 < LIT_IDX_DIM) {                                           \
+      qn[0] = *(const f32x4*)(qr + 32 * c + 8 * (U) + 8);                               \
+      qn[1] = *(const f32x4*)(qr + 32 * c + 8 * (U) + 12);                              \
+    }                                                                                   \
+    LIT_ROUND_STEP(S0) LIT_ROUND_STEP(S1) LIT_ROUND_STEP(S2) LIT_ROUND_STEP(S3)         \
+  }
+template <bool BF16>
+__device__ __forceinline__ void band_scores_rounds(const TopkParams& P, int b, const float* qP, float w_h,
+                                                   const int32_t* band_n, int M, int nw,
+                                                   double (*psum)[PSUM_LD], double* band_s) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nl = lane & 15;
+  const int R = wid < nw && wid < M ? (M - wid + nw - 1) / nw : 0;  // rounds of this wave (<= BW)
+  if (R == 0) return;
+  const float* qr = qP + lane * QP_STRIDE;
+  const size_t kbase = (size_t)(b / P.kq) * P.N * LIT_IDX_DIM;
+  // the key values of every round (rounds past R repeat round 0's entry and
+  // are not computed): lane nl of each row holds dims 32c + 2nl, +1
+  float2 kp[BW][4];
+#pragma unroll
+  for (int j = 0; j < BW; j++) {
+    const uint32_t roff = (uint32_t)band_n[wid + nw * (j < R ? j : 0)] * LIT_IDX_DIM + 2 * nl;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      if constexpr (BF16) {
+        const uint32_t kr = *(const uint32_t*)((const uint16_t*)P.kidx + kbase + roff + 32 * c);
+        kp[j][c] = make_float2(bf16_lo(kr), bf16_hi(kr));
+      } else {
+        kp[j][c] = *(const float2*)((const float*)P.kidx + kbase + roff + 32 * c);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < BW; j++) {
+    if (j < R) {
+      double acc = 0.0;
+      f32x4 qv[2], qn[2];
+      qn[0] = *(const f32x4*)qr;
+      qn[1] = *(const f32x4*)(qr + 4);
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const double kA = (double)kp[j][c].x, kB = (double)kp[j][c].y;
+        LIT_ROUND_QUARTER(0, 0, 1, 2, 3)
+        LIT_ROUND_QUARTER(1, 4, 5, 6, 7)
+        LIT_ROUND_QUARTER(2, 8, 9, 10, 11)
+        LIT_ROUND_QUARTER(3, 12, 13, 14, 15)
+      }
+      const double a = acc > 0.0 ? acc : 0.0;
+      psum[j][lane] = lane < P.H ? (double)w_h * a : 0.0;
+    }
+  }
+  wave_sync();
+  if (lane < R) {
+    const double* pr = psum[lane];
+    double s = 0.0;
+#pragma unroll 16
+    for (int h = 0; h < 64; h++) s = s + pr[h];
+    band_s[wid + nw * lane] = s;
+  }
+}
+#undef LIT_ROUND_QUARTER
+#undef LIT_ROUND_STEP
+#undef LIT_FMAC1
 #undef LIT_BAND_QUARTER
 #undef LIT_BAND_STEP
 #undef LIT_FMAC_BCAST
@@ -643,12 +728,21 @@ __device__ void wide_candidates(const TopkParams& P, WideLds& L) {
   if (P.exact && rtot > 0 && rtot <= WIDE_RCAP) {
     lds_barrier();  // the list, q and the last reads of the group keys
     const int M = rtot;
-    const int nwr = min(WIDE_RWAVES, max(4, ((M + BW - 1) / BW + 3) & ~3));
-    for (int e = 0; e + wid < M && wid < nwr; e += nwr * BW) {
-      if (P.dtype == LIT_BF16)
-        band_scores_bcast<true>(P, b, L.qP, w_h, L.rl_n, M, e + wid, nwr, L.psum[wid], L.rl_s);
-      else
-        band_scores_bcast<false>(P, b, L.qP, w_h, L.rl_n, M, e + wid, nwr, L.psum[wid], L.rl_s);
+    if (M <= WIDE_RWAVES * BW) {
+      if (wid < WIDE_RWAVES) {
+        if (P.dtype == LIT_BF16)
+          band_scores_rounds<true>(P, b, L.qP, w_h, L.rl_n, M, WIDE_RWAVES, L.psum[wid], L.rl_s);
+        else
+          band_scores_rounds<false>(P, b, L.qP, w_h, L.rl_n, M, WIDE_RWAVES, L.psum[wid], L.rl_s);
+      }
+    } else {
+      const int nwr = WIDE_RWAVES;
+      for (int e = 0; e + wid < M && wid < nwr; e += nwr * BW) {
+        if (P.dtype == LIT_BF16)
+          band_scores_bcast<true>(P, b, L.qP, w_h, L.rl_n, M, e + wid, nwr, L.psum[wid], L.rl_s);
+        else
+          band_scores_bcast<false>(P, b, L.qP, w_h, L.rl_n, M, e + wid, nwr, L.psum[wid], L.rl_s);
+      }
     }
     lds_barrier();
     double* cs = P.ws_band_s + base;
@@ -1295,9 +1389,13 @@ __device__ bool small_path(const TopkParams& P, SmallLds& L, int b) {
     // exact scores of the band, BW entries per wave and round (each wave
     // reads its q rows once per round): as many waves as the band needs, a
     // multiple of four (one more per SIMD), at least eight
-    const int nwr = min(NWAVES, max(8, ((M + BW - 1) / BW + 3) & ~3));  // 8, 12 or 16 waves
-    for (int base = 0; base + wid < M && wid < nwr; base += nwr * BW)
-      band_scores_bcast<BF16>(P, b, L.rs.qP, w_h, L.bd.band_n, M, base + wid, nwr, L.rs.psum[wid], L.bd.band_s);
+    if (M <= NWAVES * BW) {
+      band_scores_rounds<BF16>(P, b, L.rs.qP, w_h, L.bd.band_n, M, NWAVES, L.rs.psum[wid], L.bd.band_s);
+    } else {
+      const int nwr = NWAVES;
+      for (int base = 0; base + wid < M; base += nwr * BW)
+        band_scores_bcast<BF16>(P, b, L.rs.qP, w_h, L.bd.band_n, M, base + wid, nwr, L.rs.psum[wid], L.bd.band_s);
+    }
     lds_barrier();
     // the nsel best of the band by (score desc, index asc): the rank of slot i
     // counted by ballots over 64 slots at a time, one wave per slot
