@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LIT_ABI_VERSION 1
+#define LIT_ABI_VERSION 2
 
 /* Width of an index key ([ARCH] (B): each compressed entry has its own 128-dim key). */
 #define LIT_IDX_DIM 128
@@ -128,13 +128,24 @@ typedef struct {
  *   LIT_F32 / LIT_BF16: data = [B][N][512], 16-B aligned; rope, scale unused.
  *   LIT_FP8E4M3_G64_ROPE_BF16: data = [B][N][448] E4M3 bytes (16-B aligned),
  *     rope = [B][N][64] BF16 (16-B aligned), scale = [B][N][8] E8M0 bytes (byte 7
- *     unused; 4-B aligned). */
+ *     unused; 4-B aligned).
+ * Strides: row n of sequence b of an array X starts X_seq_stride * b +
+ * X_row_stride * n bytes past X, so that a cache whose sequences hold more rows
+ * than N, or whose rows sit inside wider records, is read in place. A row
+ * stride of 0 takes the dense layout's: 2048 B (F32), 1024 B (BF16) or 448 B
+ * (FP8 data), 128 B (rope), 8 B (scale); a sequence stride of 0 is N times the
+ * array's row stride. Strides
+ * are non-negative multiples of 16 B (data, rope) and of 4 B (scale): anything
+ * else is refused with LIT_ERR_ALIGN, a negative one with LIT_ERR_SHAPE. */
 typedef struct {
   lit_dtype dtype;
   int32_t n_rows; /* N */
   const void* data;
   const void* rope;
   const uint8_t* scale;
+  int64_t seq_stride, row_stride;             /* of data, bytes (0 = dense) */
+  int64_t rope_seq_stride, rope_row_stride;   /* of rope, bytes (0 = dense) */
+  int64_t scale_seq_stride, scale_row_stride; /* of scale, bytes (0 = dense) */
 } lit_kv;
 
 /* Inputs of one FlashMemory/LSA gate layer ([LSA] 2.2, 4.1; projections named in

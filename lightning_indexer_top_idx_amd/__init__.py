@@ -54,7 +54,10 @@ class IdxIn(ctypes.Structure):
 
 class KVDesc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("n_rows", ctypes.c_int32), ("data", ctypes.c_void_p),
-                ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+                ("rope", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("seq_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64),
+                ("rope_seq_stride", ctypes.c_int64), ("rope_row_stride", ctypes.c_int64),
+                ("scale_seq_stride", ctypes.c_int64), ("scale_row_stride", ctypes.c_int64)]
 
 
 class GateLayerDesc(ctypes.Structure):
@@ -175,12 +178,34 @@ def idx_in(q_idx, w, k_idx) -> IdxIn:
     return IdxIn(q_idx.data_ptr(), w.data_ptr(), k_idx.data_ptr(), _dtype_code(q_idx), q_idx.shape[1])
 
 
+def _row_strides(t):
+    """Byte strides (sequence, row) of a [B][N][row] tensor whose rows are contiguous;
+    (0, 0) for none. A dimension of size one takes 0 (the dense value)."""
+    if t is None:
+        return 0, 0
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise ValueError("KV arrays must be [B][N][row] with contiguous rows")
+    out = []
+    for d in (0, 1):
+        if t.shape[d] == 1:
+            out.append(0)
+        elif t.stride(d) <= 0:
+            raise ValueError("KV arrays cannot be broadcast over sequences or rows")
+        else:
+            out.append(t.stride(d) * t.element_size())
+    return tuple(out)
+
+
 def kv_desc(kv) -> KVDesc:
-    """kv: object with dtype in {"f32","bf16","fp8"} and data/rope/scale tensors."""
+    """kv: object with dtype in {"f32","bf16","fp8"} and data/rope/scale tensors of shape
+    [B][N][row]; a view (N rows of a longer cache, rows inside wider records) is described
+    by its strides and read in place."""
     code = {"f32": LIT_F32, "bf16": LIT_BF16, "fp8": LIT_FP8}[kv.dtype]
-    _need_cuda(kv.data, getattr(kv, "rope", None), getattr(kv, "scale", None))
-    return KVDesc(code, kv.data.shape[1], kv.data.data_ptr(), _ptr(getattr(kv, "rope", None)),
-                  _ptr(getattr(kv, "scale", None)))
+    rope, scale = getattr(kv, "rope", None), getattr(kv, "scale", None)
+    strides = _row_strides(kv.data) + _row_strides(rope) + _row_strides(scale)
+    return KVDesc(code, kv.data.shape[1], kv.data.data_ptr(), _ptr(rope), _ptr(scale), *strides)
 
 
 # ---------------------------------------------------------------------------

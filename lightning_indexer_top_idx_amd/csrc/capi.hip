@@ -51,6 +51,31 @@ lit_status allow_lds(const void* kernel, size_t bytes, const char* what) {
   return LIT_OK;
 }
 
+lit_status kv_arrays(const lit_kv* kv, KvArr* data, KvArr* rope, KvArr* scale, const char* who) {
+  const int64_t st[6] = {kv->seq_stride,      kv->row_stride,       kv->rope_seq_stride,
+                         kv->rope_row_stride, kv->scale_seq_stride, kv->scale_row_stride};
+  for (int i = 0; i < 6; i++)
+    if (st[i] < 0) return fail(LIT_ERR_SHAPE, "%s: kv stride %lld is negative", who, (long long)st[i]);
+  for (int i = 0; i < 4; i++)
+    if (st[i] % 16) return fail(LIT_ERR_ALIGN, "%s: kv data and rope strides must be multiples of 16 bytes", who);
+  for (int i = 4; i < 6; i++)
+    if (st[i] % 4) return fail(LIT_ERR_ALIGN, "%s: kv scale strides must be multiples of 4 bytes", who);
+  const int64_t N = kv->n_rows;
+  const int64_t drow = kv->dtype == LIT_F32 ? LIT_KV_DIM * 4
+                                            : (kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 ? LIT_KV_FP8_DIMS : LIT_KV_DIM * 2);
+  auto arr = [N](const void* base, int64_t seq, int64_t row, int64_t dense_row) {
+    KvArr a;
+    a.base = (const uint8_t*)base;
+    a.row = row ? row : dense_row;
+    a.seq = seq ? seq : N * a.row;
+    return a;
+  };
+  *data = arr(kv->data, st[0], st[1], drow);
+  *rope = arr(kv->rope, st[2], st[3], LIT_KV_ROPE_DIMS * 2);
+  *scale = arr(kv->scale, st[4], st[5], LIT_KV_SCALE_STRIDE);
+  return LIT_OK;
+}
+
 }  // namespace lit
 
 extern "C" int lit_abi_version(void) { return LIT_ABI_VERSION; }

@@ -27,13 +27,17 @@ constexpr int GT = 16;      // rows and heads per logits tile
 constexpr int HALF = 256;   // dims staged per pass
 constexpr int LSTR = HALF + 1;
 
-__device__ __forceinline__ float kv_elem_f32(int dtype, const void* data, const uint16_t* rope, const uint8_t* scale,
-                                             size_t row, int d) {
-  if (dtype == LIT_F32) return ((const float*)data)[row * LIT_KV_DIM + d];
-  if (dtype == LIT_BF16) return bf16_to_f32(((const uint16_t*)data)[row * LIT_KV_DIM + d]);
-  if (d >= LIT_KV_FP8_DIMS) return bf16_to_f32(rope[row * LIT_KV_ROPE_DIMS + d - LIT_KV_FP8_DIMS]);
-  const uint32_t byte = ((const uint8_t*)data)[row * LIT_KV_FP8_DIMS + d];
-  const uint32_t sb = scale[row * LIT_KV_SCALE_STRIDE + d / LIT_KV_FP8_GROUP];
+// The KV arrays of a call (data, rope, scale rows), passed by value to kernels.
+struct KvRows {
+  KvArr d, r, s;
+};
+
+__device__ __forceinline__ float kv_elem_f32(int dtype, const KvRows& kv, int b, int n, int d) {
+  if (dtype == LIT_F32) return ((const float*)kv.d.at(b, n))[d];
+  if (dtype == LIT_BF16) return bf16_to_f32(((const uint16_t*)kv.d.at(b, n))[d]);
+  if (d >= LIT_KV_FP8_DIMS) return bf16_to_f32(((const uint16_t*)kv.r.at(b, n))[d - LIT_KV_FP8_DIMS]);
+  const uint32_t byte = kv.d.at(b, n)[d];
+  const uint32_t sb = kv.s.at(b, n)[d / LIT_KV_FP8_GROUP];
   const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
   float v;
   if (e == 15u && m == 7u)
@@ -52,10 +56,8 @@ __device__ __forceinline__ float q_elem_f32(int dtype, const void* q, size_t off
 }
 
 // X[b][h][n] = scale * sum_d q[b][h][d] kv[b][n][d], fp64, d ascending.
-__global__ __launch_bounds__(256) void golden_logits_kernel(const void* q, int q_dtype, int Hq, int kv_dtype,
-                                                            const void* data, const uint16_t* rope,
-                                                            const uint8_t* scale, int N, double sc,
-                                                            double* __restrict__ X) {
+__global__ __launch_bounds__(256) void golden_logits_kernel(const void* q, int q_dtype, int Hq, int kv_dtype, KvRows kv,
+                                                            int N, double sc, double* __restrict__ X) {
   __shared__ float qs[GT][LSTR];
   __shared__ float ks[GT][LSTR];
   const int b = blockIdx.z, h0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void golden_logits_kernel(const void* q, int q
       const int rr = u / HALF, d = u % HALF;
       const int h = h0 + rr, n = n0 + rr;
       qs[rr][d] = h < Hq ? q_elem_f32(q_dtype, q, ((size_t)b * Hq + h) * LIT_KV_DIM + d0 + d) : 0.f;
-      ks[rr][d] = n < N ? kv_elem_f32(kv_dtype, data, rope, scale, (size_t)b * N + n, d0 + d) : 0.f;
+      ks[rr][d] = n < N ? kv_elem_f32(kv_dtype, kv, b, n, d0 + d) : 0.f;
     }
     __syncthreads();
     for (int d = 0; d < HALF; d++) acc = fma((double)qs[hh][d], (double)ks[r][d], acc);
@@ -311,22 +313,22 @@ __device__ __forceinline__ Raw8 load_q8(int q_dtype, const void* q, size_t off, 
   return r;
 }
 
-__device__ __forceinline__ Raw8 load_kv8(int kv_dtype, const void* data, const uint16_t* rope, const uint8_t* scale,
-                                         size_t row, int d, bool live) {
+__device__ __forceinline__ Raw8 load_kv8(int kv_dtype, const KvRows& kv, int b, int n, int d, bool live) {
   Raw8 r{};
   if (!live) return r;
   if (kv_dtype == LIT_F32) {
-    r.w[0] = *(const u32x4*)((const float*)data + row * LIT_KV_DIM + d);
-    r.w[1] = *(const u32x4*)((const float*)data + row * LIT_KV_DIM + d + 4);
+    const float* row = (const float*)kv.d.at(b, n);
+    r.w[0] = *(const u32x4*)(row + d);
+    r.w[1] = *(const u32x4*)(row + d + 4);
   } else if (kv_dtype == LIT_BF16) {
-    r.w[0] = *(const u32x4*)((const uint16_t*)data + row * LIT_KV_DIM + d);
+    r.w[0] = *(const u32x4*)((const uint16_t*)kv.d.at(b, n) + d);
   } else if (d >= LIT_KV_FP8_DIMS) {
-    r.w[0] = *(const u32x4*)(rope + row * LIT_KV_ROPE_DIMS + d - LIT_KV_FP8_DIMS);
+    r.w[0] = *(const u32x4*)((const uint16_t*)kv.r.at(b, n) + d - LIT_KV_FP8_DIMS);
   } else {
-    const u32x2 v = *(const u32x2*)((const uint8_t*)data + row * LIT_KV_FP8_DIMS + d);
+    const u32x2 v = *(const u32x2*)(kv.d.at(b, n) + d);
     r.w[0][0] = v[0];
     r.w[0][1] = v[1];
-    r.sb = scale[row * LIT_KV_SCALE_STRIDE + d / LIT_KV_FP8_GROUP];
+    r.sb = kv.s.at(b, n)[d / LIT_KV_FP8_GROUP];
   }
   return r;
 }
@@ -370,9 +372,7 @@ __device__ __forceinline__ void widen8(int dtype, bool fp8_part, const Raw8& r, 
 }
 
 __global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, int q_dtype, int M, int kv_dtype,
-                                                               const void* data, const uint16_t* rope,
-                                                               const uint8_t* scale, int N, double sc,
-                                                               double* __restrict__ X) {
+                                                               KvRows kv, int N, double sc, double* __restrict__ X) {
   __shared__ double As[LA_KC][LA_TILE + 1];  // [dim][row]
   __shared__ double Bs[LA_KC][LA_TILE + 1];  // [dim][entry]
   const int b = blockIdx.z, m0 = blockIdx.y * LA_TILE, n0 = blockIdx.x * LA_TILE;
@@ -383,7 +383,6 @@ __global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, in
   const int rr = tid >> 2, d0 = (tid & 3) * 8;
   const int m = m0 + rr, n = n0 + rr;
   const size_t qoff = ((size_t)b * M + m) * LIT_KV_DIM + d0;
-  const size_t krow = (size_t)b * N + n;
   const bool fp8 = kv_dtype == LIT_FP8E4M3_G64_ROPE_BF16;
   f64x4 acc[2][2];
 #pragma unroll
@@ -392,7 +391,7 @@ __global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, in
     for (int j = 0; j < 2; j++) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
   // the next stage's raw operands are loaded while this stage multiplies
   Raw8 ra = load_q8(q_dtype, q, qoff, m < M);
-  Raw8 rb = load_kv8(kv_dtype, data, rope, scale, krow, d0, n < N);
+  Raw8 rb = load_kv8(kv_dtype, kv, b, n, d0, n < N);
   for (int k0 = 0; k0 < LIT_KV_DIM; k0 += LA_KC) {
     double xa[8], xb[8];
     widen8(q_dtype, false, ra, xa);
@@ -406,7 +405,7 @@ __global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, in
     __syncthreads();
     if (k0 + LA_KC < LIT_KV_DIM) {
       ra = load_q8(q_dtype, q, qoff + k0 + LA_KC, m < M);
-      rb = load_kv8(kv_dtype, data, rope, scale, krow, k0 + LA_KC + d0, n < N);
+      rb = load_kv8(kv_dtype, kv, b, n, k0 + LA_KC + d0, n < N);
     }
 #pragma unroll
     for (int kk = 0; kk < LA_KC; kk += 4) {
@@ -517,6 +516,9 @@ extern "C" lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t 
     return fail(LIT_ERR_DTYPE, "%s: kv dtype %d unsupported", who, (int)kv->dtype);
   if (kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 && (!kv->rope || !kv->scale))
     return fail(LIT_ERR_NULL, "%s: FP8 rows need rope and scale arrays", who);
+  KvRows kvr;
+  const lit_status kst = kv_arrays(kv, &kvr.d, &kvr.r, &kvr.s, who);
+  if (kst != LIT_OK) return kst;
   const int N = kv->n_rows;
   GoldenWs W = golden_ws(ws, B, Hq, N);
   if (!ws || ws_bytes < W.bytes)
@@ -526,8 +528,7 @@ extern "C" lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t 
   hipStream_t st = (hipStream_t)stream;
   double* pb = pbar ? pbar : W.pbar;
   dim3 g1((unsigned)cdiv(N, GT), (unsigned)cdiv(Hq, GT), (unsigned)B);
-  golden_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, Hq, (int)kv->dtype, kv->data, (const uint16_t*)kv->rope,
-                                           kv->scale, N, (double)scale, W.X);
+  golden_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, Hq, (int)kv->dtype, kvr, N, (double)scale, W.X);
   LIT_CHECK_LAUNCH(who);
   golden_stats_kernel<<<dim3((unsigned)(B * Hq)), 1024, 0, st>>>(W.X, N, W.stats);
   LIT_CHECK_LAUNCH(who);
@@ -633,6 +634,9 @@ extern "C" lit_status lit_lookahead_golden(const void* q, lit_dtype q_dtype, int
   if (!aligned(q, 16) || !aligned(kv->data, kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 ? 8 : 16) ||
       (kv->rope && !aligned(kv->rope, 16)))
     return fail(LIT_ERR_ALIGN, "%s: q and the rows must be 16-byte aligned (FP8 row bytes 8-byte)", who);
+  KvRows kvr;
+  const lit_status kst = kv_arrays(kv, &kvr.d, &kvr.r, &kvr.s, who);
+  if (kst != LIT_OK) return kst;
   const int N = kv->n_rows;
   LookaheadWs W = lookahead_ws(ws, B, T, Hq, N, k);
   if (!ws || ws_bytes < W.bytes)
@@ -645,8 +649,7 @@ extern "C" lit_status lit_lookahead_golden(const void* q, lit_dtype q_dtype, int
   double* pb = pbar ? pbar : W.g.pbar;
   int32_t* ids = step_ids ? step_ids : W.ids;
   dim3 g1((unsigned)cdiv(N, LA_TILE), (unsigned)cdiv(M, LA_TILE), (unsigned)B);
-  lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, M, (int)kv->dtype, kv->data,
-                                              (const uint16_t*)kv->rope, kv->scale, N, (double)scale, W.g.X);
+  lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, M, (int)kv->dtype, kvr, N, (double)scale, W.g.X);
   LIT_CHECK_LAUNCH(who);
   // each (sequence, step) row is one a6 golden: softmax per head, head average, top-k
   golden_stats_kernel<<<dim3((unsigned)(BT * Hq)), 1024, 0, st>>>(W.g.X, N, W.g.stats);

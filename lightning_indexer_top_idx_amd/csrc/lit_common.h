@@ -26,6 +26,18 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Opt a kernel in to more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
 lit_status allow_lds(const void* kernel, size_t bytes, const char* what);
 
+// One array of a KV descriptor as the kernels read it: row n of sequence b
+// starts seq * b + row * n bytes past base.
+struct KvArr {
+  const uint8_t* base;
+  int64_t seq, row;
+  __host__ __device__ const uint8_t* at(int b, int n) const { return base + seq * b + row * (int64_t)n; }
+};
+// The data, rope and scale arrays of a descriptor with every stride of 0
+// replaced by the dense layout's; a negative stride is refused with
+// LIT_ERR_SHAPE, one that breaks the arrays' alignment with LIT_ERR_ALIGN.
+lit_status kv_arrays(const lit_kv* kv, KvArr* data, KvArr* rope, KvArr* scale, const char* who);
+
 // ---------------------------------------------------------------- device side
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));

@@ -45,9 +45,7 @@ struct AttnParams {
   const uint16_t* q;  // [B][Hq][512] bf16
   int Hq;
   int kv_dtype;
-  const uint8_t* data;
-  const uint16_t* rope;
-  const uint8_t* scale;
+  KvArr kd, kr, ks;  // data, rope and scale rows
   int N;
   const int32_t* ids;
   const int32_t* count;
@@ -192,7 +190,7 @@ void launch_combine(const float* part, int B, int splits, int Hq, const int32_t*
 
 // FP32 rows and queries: one workgroup per (sequence, head), fp32 VALU with an
 // online softmax over chunks of 1024 list positions.
-__global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ q, int Hq, const float* __restrict__ kv,
+__global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ q, int Hq, KvArr kv,
                                                        int N, const int32_t* __restrict__ ids,
                                                        const int32_t* __restrict__ count, int k_cap, int window,
                                                        float scale, float* __restrict__ out, float* __restrict__ lse) {
@@ -222,7 +220,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
     RL.total = c + window;
   }
   const float* qh = q + ((size_t)b * Hq + h) * LIT_KV_DIM;
-  const float* kvb = kv + (size_t)b * N * LIT_KV_DIM;
+  const uint8_t* kvb = kv.at(b, 0);
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   for (int c0 = 0; c0 < RL.total; c0 += 1024) {
     const int len = min(1024, RL.total - c0);
@@ -231,7 +229,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
       const int r = RL.row(c0 + p);
       float xv = -INFINITY;
       if (r >= 0) {
-        const float* kr = kvb + (size_t)r * LIT_KV_DIM;
+        const float* kr = (const float*)(kvb + kv.row * r);
         float dot = 0.f;
         for (int d = 0; d < LIT_KV_DIM; d++) dot = fmaf(qh[d], kr[d], dot);
         xv = dot * scale;
@@ -254,7 +252,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
       if (r < 0) continue;
       const float e = expf(xs[p] - m_use);
       ls += e;
-      const float* kr = kvb + (size_t)r * LIT_KV_DIM;
+      const float* kr = (const float*)(kvb + kv.row * r);
       a0 = fmaf(e, kr[tid], a0);
       a1 = fmaf(e, kr[tid + 256], a1);
     }
@@ -350,26 +348,32 @@ __device__ __forceinline__ void mh_row_ids(const int* rws, int (&rid)[MH_ROWS_PE
 // mh_widen_fp8): bytes 0..447 the E4M3 dims (lanes 0-27), 448..575 the BF16
 // RoPE dims (lanes 28-35), 576..583 the E8M0 scale bytes (a second, 4-byte
 // load by lanes 0-1); the other lanes load nothing.
+// The row arrays of one sequence (row n of each at its base + its row stride * n).
+struct KvSeq {
+  const uint8_t* d;
+  const uint8_t* r;
+  const uint8_t* s;
+};
+
 template <bool FP8>
-__device__ __forceinline__ void mh_issue_row(const AttnParams& P, size_t seq_rows, int r, int i, MhTile& T) {
+__device__ __forceinline__ void mh_issue_row(const AttnParams& P, const KvSeq& K, int r, int i, MhTile& T) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const size_t rr = seq_rows + (size_t)(r >= 0 ? r : 0);
+  const int64_t n = r >= 0 ? r : 0;
   uint16_t* dst = T.v + (MH_ROWS_PER_WAVE * wid + i) * MH_RS;
   if (!FP8) {
-    const uint16_t* src = (const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane;
+    const uint8_t* src = K.d + P.kd.row * n + 16 * lane;
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   } else {
     if (lane < 36) {
-      const uint8_t* src = lane < 28 ? P.data + rr * LIT_KV_FP8_DIMS + 16 * lane
-                                     : reinterpret_cast<const uint8_t*>(P.rope + rr * LIT_KV_ROPE_DIMS) + 16 * (lane - 28);
+      const uint8_t* src = lane < 28 ? K.d + P.kd.row * n + 16 * lane : K.r + P.kr.row * n + 16 * (lane - 28);
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
     if (lane < 2)
-      __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void*)(P.scale + rr * LIT_KV_SCALE_STRIDE + 4 * lane),
-          (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(dst) + 576), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(K.s + P.ks.row * n + 4 * lane),
+                                       (__attribute__((address_space(3))) void*)(reinterpret_cast<uint8_t*>(dst) + 576),
+                                       4, 0, 0);
   }
 }
 
@@ -409,11 +413,11 @@ __device__ __forceinline__ void mh_widen_fp8(MhTile& T) {
 
 // This wave's share of a whole tile.
 template <bool FP8>
-__device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, const int* rws, MhTile& T) {
+__device__ __forceinline__ void mh_issue(const AttnParams& P, const KvSeq& K, const int* rws, MhTile& T) {
   int rid[MH_ROWS_PER_WAVE];
   mh_row_ids(rws, rid);
 #pragma unroll
-  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) mh_issue_row<FP8>(P, seq_rows, rid[i], i, T);
+  for (int i = 0; i < MH_ROWS_PER_WAVE; i++) mh_issue_row<FP8>(P, K, rid[i], i, T);
 }
 
 // nvalid: rows 0 .. nvalid-1 of the tile are attended, the rest are padding.
@@ -421,7 +425,7 @@ __device__ __forceinline__ void mh_issue(const AttnParams& P, size_t seq_rows, c
 // one per K-step of the scores, so that their issue overlaps the multiplies.
 template <bool FP8>
 __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, int nvalid, const u32x4 (&qreg)[16],
-                                        MhState& S, float (*smax)[16], uint16_t* pbuf, MhTile* NT, size_t seq_rows,
+                                        MhState& S, float (*smax)[16], uint16_t* pbuf, MhTile* NT, const KvSeq& K,
                                         const int (&nrid)[MH_ROWS_PER_WAVE]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -439,7 +443,7 @@ __device__ __forceinline__ void mh_tile(const AttnParams& P, const MhTile& T, in
   for (int j = 0; j < 16; j++) {
     const u32x4 ka = kq[j % KD];
     if (j + KD < 16) kq[j % KD] = *(const u32x4*)(krow + 32 * (j + KD));
-    if (NT) mh_issue_row<FP8>(P, seq_rows, nrid[j], j, *NT);
+    if (NT) mh_issue_row<FP8>(P, K, nrid[j], j, *NT);
     acc[j & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qreg[j]),
                                                          acc[j & 3], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -557,7 +561,10 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int Hq = P.Hq;
-  const size_t seq_rows = (size_t)b * P.N;
+  KvSeq K;
+  K.d = P.kd.at(b, 0);
+  K.r = FP8 ? P.kr.at(b, 0) : nullptr;
+  K.s = FP8 ? P.ks.at(b, 0) : nullptr;
   // the count as a scalar load (issued first: its wait does not hold the
   // vector loads below)
   const int count_b = P.ids ? *(const __attribute__((address_space(4))) int32_t*)(P.count + b) : 0;
@@ -592,8 +599,8 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   if (early) {
 #pragma unroll
     for (int i = 0; i < MH_ROWS_PER_WAVE; i++) {
-      const size_t rr = seq_rows + (size_t)(P.N - P.window + MH_TR * s + MH_ROWS_PER_WAVE * wid + i);
-      t0[i] = *(const u32x4*)((const uint16_t*)P.data + rr * LIT_KV_DIM + 8 * lane);
+      const int64_t n = P.N - P.window + MH_TR * s + MH_ROWS_PER_WAVE * wid + i;
+      t0[i] = *(const u32x4*)(K.d + P.kd.row * n + 16 * lane);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -699,7 +706,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
   // alongside the queries'
   if (!all_rows) {
     lds_barrier();
-    if (0 < n) mh_issue<FP8>(P, seq_rows, tile_rows(0), TA);
+    if (0 < n) mh_issue<FP8>(P, K, tile_rows(0), TA);
   }
   // the queries as B operands, from the second tile buffer: K-step j, lane
   // (g, c16) holds dims 32j + 8g .. +7 of head c16 of the group
@@ -716,7 +723,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
     for (int i = 0; i < MH_ROWS_PER_WAVE; i++) *(u32x4*)(TA.v + (MH_ROWS_PER_WAVE * wid + i) * MH_RS + 8 * lane) = t0[i];
   }
   lds_barrier();
-  if (all_rows && !early && 0 < n) mh_issue<FP8>(P, seq_rows, tile_rows(0), TA);
+  if (all_rows && !early && 0 < n) mh_issue<FP8>(P, K, tile_rows(0), TA);
 
   MhState S;
 #pragma unroll
@@ -744,7 +751,7 @@ __global__ __launch_bounds__(MH_THREADS, 1) void attn_mh_kernel(AttnParams P) {
       const bool more = q0 + MH_TR < n;
       int nrid[MH_ROWS_PER_WAVE];
       if (more) mh_row_ids(tile_rows(tt + 1), nrid);
-      mh_tile<FP8>(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf, more ? (ab == 0 ? &TB : &TA) : nullptr, seq_rows,
+      mh_tile<FP8>(P, ab == 0 ? TA : TB, n - q0, qreg, S, smax, pbuf, more ? (ab == 0 ? &TB : &TA) : nullptr, K,
               nrid);
       // no barrier here: the next tile's opening barrier orders this tile's
       // reads of its buffer, pbuf and smax before anything rewrites them
@@ -860,9 +867,12 @@ lit_status attn_decode(const char* who, bool from_scratch, const void* q, lit_dt
   if (!aligned(q, 16) || !aligned(kv->data, 16) || (kv->rope && !aligned(kv->rope, 16)) || !aligned(out, 16) ||
       (kv->scale && !aligned(kv->scale, 4)))
     return fail(LIT_ERR_ALIGN, "%s: q, kv->data, kv->rope and out must be 16-byte aligned, kv->scale 4-byte", who);
+  KvArr kd, kr, ks;
+  const lit_status kst = kv_arrays(kv, &kd, &kr, &ks, who);
+  if (kst != LIT_OK) return kst;
   hipStream_t st = (hipStream_t)stream;
   if (kv->dtype == LIT_F32) {
-    attn_f32_kernel<<<dim3((unsigned)(B * Hq)), dim3(256), 0, st>>>((const float*)q, Hq, (const float*)kv->data, N,
+    attn_f32_kernel<<<dim3((unsigned)(B * Hq)), dim3(256), 0, st>>>((const float*)q, Hq, kd, N,
                                                                      ids, count, k_cap, Wc, scale, out, lse);
     LIT_CHECK_LAUNCH(who);
     return LIT_OK;
@@ -889,9 +899,9 @@ lit_status attn_decode(const char* who, bool from_scratch, const void* q, lit_dt
   P.q = (const uint16_t*)q;
   P.Hq = Hq;
   P.kv_dtype = (int)kv->dtype;
-  P.data = (const uint8_t*)kv->data;
-  P.rope = (const uint16_t*)kv->rope;
-  P.scale = kv->scale;
+  P.kd = kd;
+  P.kr = kr;
+  P.ks = ks;
   P.N = N;
   P.ids = ids;
   P.count = count;

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version(L):
-    assert L.lit_abi_version() == 1
+    assert L.lit_abi_version() == 2
 
 
 def _idx(q=0x1000, w=0x2000, k=0x3000, dtype=1, H=64):
@@ -103,6 +103,18 @@ def test_attention_validation(L):
     kv8m = lit.KVDesc(2, 1000, 0x1000, 0x8000, 0x9002)
     assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv8m), 1, None, None, 0, 0, 0.04, p(0x2000), None,
                                     None, 0, None) == 3
+    # row strides: negative refused as a shape, off a 16-byte (data, rope) or 4-byte
+    # (scale) multiple as an alignment; nothing is launched
+    for fields, want in ((dict(row_stride=-1024), 2), (dict(seq_stride=-16), 2), (dict(row_stride=1032), 3),
+                         (dict(seq_stride=1024 * 1000 + 8), 3)):
+        kvs = lit.KVDesc(1, 1000, 0x1000, None, None, **fields)
+        assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kvs), 1, None, None, 0, 0, 0.04, p(0x2000),
+                                        None, None, 0, None) == want, fields
+        assert "stride" in lit.last_error()
+    for fields in (dict(rope_row_stride=136), dict(scale_row_stride=10), dict(scale_seq_stride=8002)):
+        kvs = lit.KVDesc(2, 1000, 0x1000, 0x8000, 0x9000, **fields)
+        assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kvs), 1, None, None, 0, 0, 0.04, p(0x2000),
+                                        None, None, 0, None) == 3, fields
     # a workspace off a 16-byte boundary is refused before any planning
     assert L.lit_attn_workspace_bytes(4, 64, 125000) > 256
     assert L.lit_sparse_attn_decode(p(0x3000), 1, 64, ctypes.byref(kv), 4, None, None, 0, 0, 0.04, p(0x2000), None,
@@ -116,6 +128,10 @@ def test_other_entry_points_validation(L):
     kv = lit.KVDesc(1, 100, 0x1000, None, None)
     assert L.lit_golden_topk(p(0x2000), 1, 64, ctypes.byref(kv), 1, 0.04, 0, p(0x3000), p(0x4000), None, None,
                              p(0x5000), 1 << 30, None) == 2
+    kvs = lit.KVDesc(1, 100, 0x1000, None, None, row_stride=1030)
+    assert L.lit_golden_topk(p(0x2000), 1, 64, ctypes.byref(kvs), 1, 0.04, 10, p(0x3000), p(0x4000), None, None,
+                             p(0x5000), 1 << 30, None) == 3
+    assert "stride" in lit.last_error()
     assert L.lit_golden_topp_vote(p(0x1000), 0, 21, 1, 100, 1.5, 3, p(0x2000), p(0x3000), None, p(0x4000), 1 << 30,
                                   None) == 2
     assert L.lit_golden_topp_vote(p(0x1000), 0, 21, 1, 100, 0.6, 3, p(0x2000), p(0x3000), None, p(0x4000), 16,
@@ -194,6 +210,10 @@ def test_lookahead_validation(L):
     assert L.lit_lookahead_golden(*args(8, 1, need - 1)) == 5  # workspace too small
     assert L.lit_lookahead_golden(None, 1, 8, 16, ctypes.byref(kv), 2, 0.04, 10, None, None, None, p(0x3000), None,
                                   p(0x4000), need, None) == 1
+    kvs = lit.KVDesc(1, 100, 0x1000, None, None, seq_stride=-2048)
+    assert L.lit_lookahead_golden(p(0x2000), 1, 8, 16, ctypes.byref(kvs), 2, 0.04, 10, None, None, None, p(0x3000),
+                                  None, p(0x4000), need, None) == 2
+    assert "stride" in lit.last_error()
 
 
 def test_bench_refuses_more_than_one_gpu():
