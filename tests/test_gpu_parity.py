@@ -252,12 +252,13 @@ def test_topk_with_hints_of_other_scores_falls_back():
 
 
 def test_score_launch_arrangements_agree_bit_for_bit():
-    # the headline batch (32 sequences, four chunks per workgroup, workgroups
-    # paired) and sequences of it scored in smaller batches (one chunk per
-    # workgroup, unpaired) run the same per-entry arithmetic
+    # the headline batch (32 sequences, four chunks per workgroup, each
+    # sequence on one XCD) and sequences of it scored in smaller batches (one
+    # chunk per workgroup; or four chunks on a two-dimensional grid, 20
+    # sequences) run the same per-entry arithmetic
     inp = W.layer_inputs(W.CTX64K_B, 3, "cuda").idx
     s32, h32 = lit.idx_score(inp.q_idx, inp.w, inp.k_idx)
-    for lo, hi in ((0, 8), (16, 24), (29, 30)):
+    for lo, hi in ((0, 8), (16, 24), (29, 30), (5, 25)):
         s, h = lit.idx_score(inp.q_idx[lo:hi].contiguous(), inp.w[lo:hi].contiguous(), inp.k_idx[lo:hi].contiguous())
         torch.cuda.synchronize()
         assert torch.equal(s, s32[lo:hi]), (lo, hi)
