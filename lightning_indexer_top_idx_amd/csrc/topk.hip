@@ -589,22 +589,36 @@ __device__ void wide_candidates(const TopkParams& P, WideLds& L) {
   const float* hb = P.hints + (size_t)b * P.hints_len;
   const float* gmx = hb + P.nchunks;
 
-  // 1. group keys (+ the largest key-norm bound, q and w in exact mode)
+  // 1. group keys (+ the largest key-norm bound, q and w in exact mode). The
+  //    group maxima (at most GM_CAP / TK_THREADS per thread, at clamped
+  //    addresses) are requested before anything waits, so that they and the
+  //    exact mode's reads come back in one round trip instead of one per
+  //    thousand groups
+  constexpr int GPT = GM_CAP / TK_THREADS;
+  static_assert(GPT * TK_THREADS == GM_CAP && GM_CAP * GROUP / LIT_KNORM_CHUNK <= TK_THREADS, "one pass of loads");
+  float gv[GPT];
+#pragma unroll
+  for (int j = 0; j < GPT; j++) gv[j] = gmx[min(tid + TK_THREADS * j, G - 1)];
   float knorm = 0.f, w_h = 0.f;
   if (P.exact) {
-    for (int j = tid; j < P.nchunks; j += TK_THREADS) knorm = fmaxf(knorm, hb[j]);
+    const float kn = hb[min(tid, P.nchunks - 1)];  // at most TK_THREADS chunks on this path
+    knorm = tid < P.nchunks ? kn : 0.f;
     w_h = lane < P.H ? P.w[(size_t)b * P.H + lane] : 0.f;
     stage_q_rows(P, L.qP, b);
   }
   int ns = 0;
   uint32_t kmin = 0xffffffffu, kmx = 0u;
-  for (int g = tid; g < G; g += TK_THREADS) {
-    const uint32_t kk = score_key(gmx[g]);
-    L.gkey[g] = kk;
-    if (kk) {
-      ns++;
-      kmin = min(kmin, kk);
-      kmx = max(kmx, kk);
+#pragma unroll
+  for (int j = 0; j < GPT; j++) {
+    const int g = tid + TK_THREADS * j;
+    if (g < G) {
+      const uint32_t kk = score_key(gv[j]);
+      L.gkey[g] = kk;
+      if (kk) {
+        ns++;
+        kmin = min(kmin, kk);
+        kmx = max(kmx, kk);
+      }
     }
   }
   block_sum_min_max(ns, kmin, kmx, knorm, &L.sc);
