@@ -371,8 +371,12 @@ __device__ __forceinline__ void widen8(int dtype, bool fp8_part, const Raw8& r, 
   }
 }
 
+// part (when given): for every row and 32-entry block of the row, the block's
+// maximum logit m and sum of exp(x - m), so that the softmax statistics need
+// no further pass over the logits.
 __global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, int q_dtype, int M, int kv_dtype,
-                                                               KvRows kv, int N, double sc, double* __restrict__ X) {
+                                                               KvRows kv, int N, double sc, double* __restrict__ X,
+                                                               double* __restrict__ part) {
   __shared__ double As[LA_KC][LA_TILE + 1];  // [dim][row]
   __shared__ double Bs[LA_KC][LA_TILE + 1];  // [dim][entry]
   const int b = blockIdx.z, m0 = blockIdx.y * LA_TILE, n0 = blockIdx.x * LA_TILE;
@@ -431,6 +435,56 @@ __global__ __launch_bounds__(256) void lookahead_logits_kernel(const void* q, in
         if (mm < M && nn < N) X[((size_t)b * M + mm) * N + nn] = sc * acc[i][j][r];
       }
     }
+  if (part) {
+    // this wave holds 32 entries (j, r16) of each of its rows: the sixteen
+    // lanes of a row group (same k4) reduce them
+    const int nb = (N + 31) / 32, blk = (n0 + wn) / 32;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int mm = m0 + wm + 16 * i + k4 + 4 * r;
+        const int nn0 = n0 + wn + r16, nn1 = nn0 + 16;
+        const double v0 = nn0 < N ? sc * acc[i][0][r] : -INFINITY;
+        const double v1 = nn1 < N ? sc * acc[i][1][r] : -INFINITY;
+        double mx = fmax(v0, v1);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o));
+        double sm = mx == -INFINITY ? 0.0 : exp(v0 - mx) + exp(v1 - mx);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
+        if (r16 == 0 && mm < M && blk < nb) {
+          double* pp = part + (((size_t)b * M + mm) * nb + blk) * 2;
+          pp[0] = mx;
+          pp[1] = sm;
+        }
+      }
+  }
+}
+
+// Softmax statistics of each row from its blocks' (maximum, sum): one wave per
+// row, m = the largest block maximum, Z = sum of the blocks' sums scaled by
+// exp(m_block - m).
+__global__ __launch_bounds__(256) void golden_stats_parts_kernel(const double* __restrict__ part, int nb, int rows,
+                                                                 double* __restrict__ stats) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (row >= rows) return;  // (the whole wave)
+  const double* p = part + (size_t)row * nb * 2;
+  double m = -INFINITY;
+  for (int i = lane; i < nb; i += 64) m = fmax(m, p[2 * i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  double z = 0.0;
+  for (int i = lane; i < nb; i += 64) {
+    const double mi = p[2 * i];
+    if (mi != -INFINITY) z += p[2 * i + 1] * exp(mi - m);
+  }
+  z = wave_sum_f64(z);
+  if (lane == 0) {
+    stats[2 * row] = m;
+    stats[2 * row + 1] = z;
+  }
 }
 
 // hits[b][n] = number of the T steps whose golden set holds n (t ascending);
@@ -585,6 +639,7 @@ extern "C" lit_status lit_golden_topp_vote(const double* x, int32_t is_logits, i
 namespace {
 struct LookaheadWs {
   GoldenWs g;  // logits / stats / pbar / selection scratch of the B*T (sequence, step) rows
+  double* part;  // per row and 32-entry block: maximum logit and its sum of exponentials
   int32_t* ids;
   int32_t* cnt;
   uint8_t* mask;
@@ -596,6 +651,8 @@ LookaheadWs lookahead_ws(void* base, int B, int T, int Hq, int N, int k) {
   LookaheadWs w;
   w.g = golden_ws(base, B * T, Hq, N);
   size_t off = w.g.bytes;
+  w.part = (double*)ws_at(base, off);
+  off += round_up((size_t)B * T * Hq * ((N + 31) / 32) * 2 * sizeof(double), 256);
   w.ids = (int32_t*)ws_at(base, off);
   off += round_up((size_t)B * T * k * sizeof(int32_t), 256);
   w.cnt = (int32_t*)ws_at(base, off);
@@ -649,10 +706,12 @@ extern "C" lit_status lit_lookahead_golden(const void* q, lit_dtype q_dtype, int
   double* pb = pbar ? pbar : W.g.pbar;
   int32_t* ids = step_ids ? step_ids : W.ids;
   dim3 g1((unsigned)cdiv(N, LA_TILE), (unsigned)cdiv(M, LA_TILE), (unsigned)B);
-  lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, M, (int)kv->dtype, kvr, N, (double)scale, W.g.X);
+  lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, M, (int)kv->dtype, kvr, N, (double)scale, W.g.X,
+                                              W.part);
   LIT_CHECK_LAUNCH(who);
   // each (sequence, step) row is one a6 golden: softmax per head, head average, top-k
-  golden_stats_kernel<<<dim3((unsigned)(BT * Hq)), 1024, 0, st>>>(W.g.X, N, W.g.stats);
+  golden_stats_parts_kernel<<<dim3((unsigned)cdiv(BT * Hq, 4)), 256, 0, st>>>(W.part, (N + 31) / 32, BT * Hq,
+                                                                              W.g.stats);
   LIT_CHECK_LAUNCH(who);
   golden_pbar_kernel<<<dim3((unsigned)cdiv(N, 256), (unsigned)BT), 256, 0, st>>>(W.g.X, W.g.stats, Hq, N, pb);
   LIT_CHECK_LAUNCH(who);
