@@ -277,6 +277,10 @@ lit_status lit_sparse_attn_decode_noalloc(const void* q, lit_dtype q_dtype, int3
  *     G       = top-k of pbar, pbar descending then index ascending.
  * ids   : [B][k] ascending (tail -1); count: [B]; mask: [B][N] u8 or NULL;
  * pbar  : [B][N] fp64 output or NULL.
+ * q and the rows 16-byte aligned (FP8 row bytes 8-byte), else LIT_ERR_ALIGN. The
+ * logits are fp64 sums on the matrix cores, whose order is not sequential: pbar
+ * matches a sequential fp64 evaluation to a relative ~1e-15, and G can differ
+ * from it only where pbar ties the k-th value within that margin.
  * Workspace: lit_golden_workspace_bytes(B, Hq, N, k) bytes. */
 size_t lit_golden_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t k);
 lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t Hq, const lit_kv* kv,

@@ -23,89 +23,10 @@
 namespace lit {
 namespace {
 
-constexpr int GT = 16;      // rows and heads per logits tile
-constexpr int HALF = 256;   // dims staged per pass
-constexpr int LSTR = HALF + 1;
-
 // The KV arrays of a call (data, rope, scale rows), passed by value to kernels.
 struct KvRows {
   KvArr d, r, s;
 };
-
-__device__ __forceinline__ float kv_elem_f32(int dtype, const KvRows& kv, int b, int n, int d) {
-  if (dtype == LIT_F32) return ((const float*)kv.d.at(b, n))[d];
-  if (dtype == LIT_BF16) return bf16_to_f32(((const uint16_t*)kv.d.at(b, n))[d]);
-  if (d >= LIT_KV_FP8_DIMS) return bf16_to_f32(((const uint16_t*)kv.r.at(b, n))[d - LIT_KV_FP8_DIMS]);
-  const uint32_t byte = kv.d.at(b, n)[d];
-  const uint32_t sb = kv.s.at(b, n)[d / LIT_KV_FP8_GROUP];
-  const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
-  float v;
-  if (e == 15u && m == 7u)
-    v = __uint_as_float(0x7fc00000u);
-  else if (e == 0u)
-    v = (float)m * 0x1p-9f;
-  else
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  v = __uint_as_float(__float_as_uint(v) | ((byte & 0x80u) << 24));
-  const float sc = sb == 255u ? __uint_as_float(0x7fc00000u) : (sb == 0u ? 0x1p-127f : __uint_as_float(sb << 23));
-  return v * sc;
-}
-
-__device__ __forceinline__ float q_elem_f32(int dtype, const void* q, size_t off) {
-  return dtype == LIT_F32 ? ((const float*)q)[off] : bf16_to_f32(((const uint16_t*)q)[off]);
-}
-
-// X[b][h][n] = scale * sum_d q[b][h][d] kv[b][n][d], fp64, d ascending.
-__global__ __launch_bounds__(256) void golden_logits_kernel(const void* q, int q_dtype, int Hq, int kv_dtype, KvRows kv,
-                                                            int N, double sc, double* __restrict__ X) {
-  __shared__ float qs[GT][LSTR];
-  __shared__ float ks[GT][LSTR];
-  const int b = blockIdx.z, h0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
-  const int tid = threadIdx.x, r = tid >> 4, hh = tid & 15;
-  double acc = 0.0;
-  for (int half = 0; half < 2; half++) {
-    const int d0 = half * HALF;
-    for (int u = tid; u < GT * HALF; u += 256) {
-      const int rr = u / HALF, d = u % HALF;
-      const int h = h0 + rr, n = n0 + rr;
-      qs[rr][d] = h < Hq ? q_elem_f32(q_dtype, q, ((size_t)b * Hq + h) * LIT_KV_DIM + d0 + d) : 0.f;
-      ks[rr][d] = n < N ? kv_elem_f32(kv_dtype, kv, b, n, d0 + d) : 0.f;
-    }
-    __syncthreads();
-    for (int d = 0; d < HALF; d++) acc = fma((double)qs[hh][d], (double)ks[r][d], acc);
-    __syncthreads();
-  }
-  const int h = h0 + hh, n = n0 + r;
-  if (h < Hq && n < N) X[((size_t)b * Hq + h) * N + n] = sc * acc;
-}
-
-// Per (b, h): max and sum of exp(x - max) over n.
-__global__ __launch_bounds__(1024) void golden_stats_kernel(const double* __restrict__ X, int N,
-                                                            double* __restrict__ stats) {
-  __shared__ double red[16];
-  const double* x = X + (size_t)blockIdx.x * N;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  double m = -INFINITY;
-  for (int n = tid; n < N; n += 1024) m = fmax(m, x[n]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
-  if (lane == 0) red[wid] = m;
-  __syncthreads();
-  m = red[0];
-  for (int i = 1; i < 16; i++) m = fmax(m, red[i]);
-  __syncthreads();
-  double z = 0.0;
-  for (int n = tid; n < N; n += 1024) z += exp(x[n] - m);
-  z = wave_sum_f64(z);
-  if (lane == 0) red[wid] = z;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int i = 0; i < 16; i++) t += red[i];
-    stats[2 * blockIdx.x] = m;
-    stats[2 * blockIdx.x + 1] = t;
-  }
-}
 
 // pbar[b][n] = (sum_h exp(X - m_h) / Z_h) / Hq, h ascending.
 __global__ __launch_bounds__(256) void golden_pbar_kernel(const double* __restrict__ X, const double* __restrict__ stats,
@@ -333,7 +254,8 @@ __device__ __forceinline__ Raw8 load_kv8(int kv_dtype, const KvRows& kv, int b, 
   return r;
 }
 
-// OCP E4M3FN byte and E8M0 scale byte to fp32, as kv_elem_f32 decodes them.
+// OCP E4M3FN byte and E8M0 scale byte to fp32 (the format's definition: E4M3FN with
+// 0x7F / 0xFF NaN, E8M0 2^(byte-127) with 255 NaN).
 __device__ __forceinline__ float fp8_e4m3_f32(uint32_t byte) {
   const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
   float v;
@@ -514,6 +436,7 @@ __global__ __launch_bounds__(256) void count_u8_kernel(const uint8_t* __restrict
 
 struct GoldenWs {
   double* X;
+  double* part;  // per row and 32-entry block: maximum logit and its sum of exponentials
   double* stats;
   double* pbar;
   uint8_t* sel;
@@ -529,6 +452,8 @@ GoldenWs golden_ws(void* base, int B, int Hq, int N) {
   size_t off = 0;
   w.X = (double*)ws_at(base, off);
   off += round_up((size_t)B * Hq * N * sizeof(double), 256);
+  w.part = (double*)ws_at(base, off);
+  off += round_up((size_t)B * Hq * ((N + 31) / 32) * 2 * sizeof(double), 256);
   w.stats = (double*)ws_at(base, off);
   off += round_up((size_t)B * Hq * 2 * sizeof(double), 256);
   w.pbar = (double*)ws_at(base, off);
@@ -570,6 +495,9 @@ extern "C" lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t 
     return fail(LIT_ERR_DTYPE, "%s: kv dtype %d unsupported", who, (int)kv->dtype);
   if (kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 && (!kv->rope || !kv->scale))
     return fail(LIT_ERR_NULL, "%s: FP8 rows need rope and scale arrays", who);
+  if (!aligned(q, 16) || !aligned(kv->data, kv->dtype == LIT_FP8E4M3_G64_ROPE_BF16 ? 8 : 16) ||
+      (kv->rope && !aligned(kv->rope, 16)))
+    return fail(LIT_ERR_ALIGN, "%s: q and the rows must be 16-byte aligned (FP8 row bytes 8-byte)", who);
   KvRows kvr;
   const lit_status kst = kv_arrays(kv, &kvr.d, &kvr.r, &kvr.s, who);
   if (kst != LIT_OK) return kst;
@@ -581,10 +509,12 @@ extern "C" lit_status lit_golden_topk(const void* q, lit_dtype q_dtype, int32_t 
     return fail(LIT_ERR_ALIGN, "%s: workspace must be 256-byte aligned, pbar 8-byte aligned", who);
   hipStream_t st = (hipStream_t)stream;
   double* pb = pbar ? pbar : W.pbar;
-  dim3 g1((unsigned)cdiv(N, GT), (unsigned)cdiv(Hq, GT), (unsigned)B);
-  golden_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, Hq, (int)kv->dtype, kvr, N, (double)scale, W.X);
+  // the logits on the fp64 matrix cores (the one-step case of the lookahead's
+  // kernel: Hq query rows per sequence), the softmax statistics from its blocks
+  dim3 g1((unsigned)cdiv(N, LA_TILE), (unsigned)cdiv(Hq, LA_TILE), (unsigned)B);
+  lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, Hq, (int)kv->dtype, kvr, N, (double)scale, W.X, W.part);
   LIT_CHECK_LAUNCH(who);
-  golden_stats_kernel<<<dim3((unsigned)(B * Hq)), 1024, 0, st>>>(W.X, N, W.stats);
+  golden_stats_parts_kernel<<<dim3((unsigned)cdiv(B * Hq, 4)), 256, 0, st>>>(W.part, (N + 31) / 32, B * Hq, W.stats);
   LIT_CHECK_LAUNCH(who);
   golden_pbar_kernel<<<dim3((unsigned)cdiv(N, 256), (unsigned)B), 256, 0, st>>>(W.X, W.stats, Hq, N, pb);
   LIT_CHECK_LAUNCH(who);
@@ -638,8 +568,7 @@ extern "C" lit_status lit_golden_topp_vote(const double* x, int32_t is_logits, i
 
 namespace {
 struct LookaheadWs {
-  GoldenWs g;  // logits / stats / pbar / selection scratch of the B*T (sequence, step) rows
-  double* part;  // per row and 32-entry block: maximum logit and its sum of exponentials
+  GoldenWs g;  // logits / statistics / pbar / selection scratch of the B*T (sequence, step) rows
   int32_t* ids;
   int32_t* cnt;
   uint8_t* mask;
@@ -651,8 +580,6 @@ LookaheadWs lookahead_ws(void* base, int B, int T, int Hq, int N, int k) {
   LookaheadWs w;
   w.g = golden_ws(base, B * T, Hq, N);
   size_t off = w.g.bytes;
-  w.part = (double*)ws_at(base, off);
-  off += round_up((size_t)B * T * Hq * ((N + 31) / 32) * 2 * sizeof(double), 256);
   w.ids = (int32_t*)ws_at(base, off);
   off += round_up((size_t)B * T * k * sizeof(int32_t), 256);
   w.cnt = (int32_t*)ws_at(base, off);
@@ -707,10 +634,10 @@ extern "C" lit_status lit_lookahead_golden(const void* q, lit_dtype q_dtype, int
   int32_t* ids = step_ids ? step_ids : W.ids;
   dim3 g1((unsigned)cdiv(N, LA_TILE), (unsigned)cdiv(M, LA_TILE), (unsigned)B);
   lookahead_logits_kernel<<<g1, 256, 0, st>>>(q, (int)q_dtype, M, (int)kv->dtype, kvr, N, (double)scale, W.g.X,
-                                              W.part);
+                                              W.g.part);
   LIT_CHECK_LAUNCH(who);
   // each (sequence, step) row is one a6 golden: softmax per head, head average, top-k
-  golden_stats_parts_kernel<<<dim3((unsigned)cdiv(BT * Hq, 4)), 256, 0, st>>>(W.part, (N + 31) / 32, BT * Hq,
+  golden_stats_parts_kernel<<<dim3((unsigned)cdiv(BT * Hq, 4)), 256, 0, st>>>(W.g.part, (N + 31) / 32, BT * Hq,
                                                                               W.g.stats);
   LIT_CHECK_LAUNCH(who);
   golden_pbar_kernel<<<dim3((unsigned)cdiv(N, 256), (unsigned)BT), 256, 0, st>>>(W.g.X, W.g.stats, Hq, N, pb);

@@ -438,7 +438,21 @@ def test_golden_topk(name, wl, B, N, k):
     torch.cuda.synchronize()
     rids, rcnt, rmask, rp = oracle.golden(L.q, L.kv, SCALE, k)
     np.testing.assert_allclose(pbar.cpu().numpy(), rp, rtol=1e-11, atol=0)
-    check_selection(ids, cnt, mask, rids, rcnt, rmask, rp, f"golden {name}")
+    ids_np = ids.cpu().numpy()
+    if np.array_equal(ids_np, rids):
+        check_selection(ids, cnt, mask, rids, rcnt, rmask, rp, f"golden {name}")
+        return
+    # the logits are fp64 sums on the matrix cores, added in another order than
+    # the oracle's: a set may differ only at a tie with the k-th value within that
+    # rounding, and the count and mask follow the ids the GPU chose
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    for b in range(ids_np.shape[0]):
+        kth = np.sort(rp[b])[::-1][k - 1]
+        diff = set(ids_np[b].tolist()) ^ set(rids[b].tolist())
+        assert all(abs(rp[b][n] - kth) <= 1e-12 * kth for n in diff if n >= 0), (b, diff)
+        m = np.zeros(rp.shape[1], np.uint8)
+        m[ids_np[b][ids_np[b] >= 0]] = 1
+        assert np.array_equal(mask.cpu().numpy()[b], m)
 
 
 def test_recall_counts():
