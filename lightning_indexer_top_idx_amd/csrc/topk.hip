@@ -952,7 +952,7 @@ __device__ bool finish_rescored(const TopkParams& P, FastLds& L, int b, int M1, 
   if (tid == 0) L.sc.misc[5] = 0;
   for (int w = tid; w < CAND_CAP / 32; w += TK_THREADS) L.sel[w] = 0u;
   int tot;
-  int rpos = block_excl_scan((sure << 16) | resc, L.sc.scan, &tot);  // (its barriers order misc[5] = 0)
+  int rpos = block_excl_scan1<NWAVES>((sure << 16) | resc, L.sc.scan, &tot);  // (its barrier orders misc[5] = 0)
   rpos &= 0xffff;
   if (lane == 0) atomicAdd(&L.sc.misc[5], above2);
   const int A = tot >> 16, R = tot & 0xffff;
@@ -969,17 +969,17 @@ __device__ bool finish_rescored(const TopkParams& P, FastLds& L, int b, int M1, 
   lds_barrier();
   const int need = k - A;
   if (L.sc.misc[5] >= k || R > FBAND_CAP || need < 1 || need > R) return false;
-  // the best `need` rescored candidates by (exact score desc, index asc): the
-  // rank of entry i counted by ballots over 64 entries at a time, one wave per entry
-  for (int i = wid; i < R; i += NWAVES) {
-    const double si = L.band_s[i];
+  // the best `need` rescored candidates by (exact score desc, index asc): lane
+  // i of the block ranks entry i against every entry, each read by all lanes
+  // at once (one broadcast per entry; the list is in index order)
+  for (int i = tid; i - lane < R; i += TK_THREADS) {
+    const double si = i < R ? L.band_s[i] : 0.0;
     int rank = 0;
-    for (int j0 = 0; j0 < R; j0 += 64) {
-      const int j = j0 + lane;
-      const double sj = j < R ? L.band_s[j] : 0.0;
-      rank += __popcll(__ballot(j < R && (sj > si || (sj == si && j < i))));  // the list is in index order
+    for (int j = 0; j < R; j++) {
+      const double sj = L.band_s[j];
+      rank += sj > si || (sj == si && j < i);
     }
-    if (lane == 0 && rank < need) {
+    if (i < R && rank < need) {
       const int ps = L.binpos[i];
       atomicOr(&L.sel[ps >> 5], 1u << (ps & 31));
     }
@@ -991,7 +991,7 @@ __device__ bool finish_rescored(const TopkParams& P, FastLds& L, int b, int M1, 
   int c = 0;
   for (int i = ca; i < ce; i++) c += (L.sel[i >> 5] >> (i & 31)) & 1u;
   int total;
-  int opos = block_excl_scan(c, L.sc.scan, &total);
+  int opos = block_excl_scan1<NWAVES>(c, L.sc.scan, &total);
   for (int i = ca; i < ce; i++)
     if ((L.sel[i >> 5] >> (i & 31)) & 1u) {
       const int n = L.cidx[i];
@@ -1036,7 +1036,7 @@ __device__ bool wide_finish(const TopkParams& P, FastLds& L, int b) {
   }
   const int cnt = cword & ~(int)WIDE_OVERFLOW;
   int M1;
-  const int off = block_excl_scan(cnt, L.sc.scan, &M1);
+  const int off = block_excl_scan1<NWAVES>(cnt, L.sc.scan, &M1);
   const bool overflow = __syncthreads_or((cword & (int)WIDE_OVERFLOW) != 0);
   if (ns == 0) {  // nothing selectable (the mask is already clear)
     int32_t* ids = P.ids + (size_t)b * P.k;
