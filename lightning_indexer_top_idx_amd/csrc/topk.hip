@@ -641,7 +641,7 @@ __device__ void wide_candidates(const TopkParams& P, WideLds& L) {
     // cumulative counts from the top bin down: thread t owns bins 2047-2t, 2046-2t
     const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
     int tot;
-    const int ab = block_excl_scan(c0 + c1, L.sc.scan, &tot);
+    const int ab = block_excl_scan1<NWAVES>(c0 + c1, L.sc.scan, &tot);
     const int r1 = k, r2 = max(1, k - WIDE_MARGIN);
     if (ab < r1 && r1 <= ab + c0) L.sc.misc[0] = 2047 - 2 * tid;
     if (ab + c0 < r1 && r1 <= ab + c0 + c1) L.sc.misc[0] = 2046 - 2 * tid;
@@ -695,7 +695,7 @@ __device__ void wide_candidates(const TopkParams& P, WideLds& L) {
     }
   }
   int tot;
-  int pos = block_excl_scan((c << 16) | r, L.sc.scan, &tot);
+  int pos = block_excl_scan1<NWAVES>((c << 16) | r, L.sc.scan, &tot);
   int rpos = pos & 0xffff;
   pos >>= 16;
   const int ctot = tot >> 16, rtot = tot & 0xffff;
