@@ -415,8 +415,10 @@ __device__ __forceinline__ void band_scores_rounds(const TopkParams& P, int b, c
 // ---------------------------------------------------------------- fast path
 
 // Block-wide reduction of (sum, min, max) over all threads; uses sc->scan.
+// (fresh: nothing has read sc in this workgroup yet, so the barrier that keeps
+// its earlier readers from being overwritten is not needed.)
 __device__ __forceinline__ void block_sum_min_max(int& s, uint32_t& mn, uint32_t& mx, float& fm,
-                                                  SelectScratch* sc) {
+                                                  SelectScratch* sc, bool fresh = false) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -425,7 +427,7 @@ __device__ __forceinline__ void block_sum_min_max(int& s, uint32_t& mn, uint32_t
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
     fm = fmaxf(fm, __shfl_xor(fm, o));
   }
-  lds_barrier();
+  if (!fresh) lds_barrier();
   if (lane == 0) {
     sc->scan[wid] = s;
     sc->hist[wid] = mn;
@@ -608,20 +610,21 @@ __device__ void wide_candidates(const TopkParams& P, WideLds& L) {
   }
   int ns = 0;
   uint32_t kmin = 0xffffffffu, kmx = 0u;
+  uint32_t gk[GPT];  // this thread's group keys (0 past G), kept for the histogram
 #pragma unroll
   for (int j = 0; j < GPT; j++) {
     const int g = tid + TK_THREADS * j;
-    if (g < G) {
-      const uint32_t kk = score_key(gv[j]);
-      L.gkey[g] = kk;
-      if (kk) {
-        ns++;
-        kmin = min(kmin, kk);
-        kmx = max(kmx, kk);
-      }
+    gk[j] = g < G ? score_key(gv[j]) : 0u;
+    if (g < G) L.gkey[g] = gk[j];
+    if (gk[j]) {
+      ns++;
+      kmin = min(kmin, gk[j]);
+      kmx = max(kmx, gk[j]);
     }
   }
-  block_sum_min_max(ns, kmin, kmx, knorm, &L.sc);
+  // (cleared here: the reduction's barriers order it before the histogram)
+  for (int i = tid; i < 2048; i += TK_THREADS) L.hist2k[i] = 0u;
+  block_sum_min_max(ns, kmin, kmx, knorm, &L.sc, true);
 
   // 2. L and H from one histogram of the group keys (the bins span the bits
   //    below the common prefix of the smallest and largest)
@@ -631,12 +634,9 @@ __device__ void wide_candidates(const TopkParams& P, WideLds& L) {
     const int hbit = diff ? 31 - __clz((int)diff) : 0;
     const int shift = hbit > 10 ? hbit - 10 : 0;
     const uint32_t prefix = kmx & ~((2u << hbit) - 1u);
-    for (int i = tid; i < 2048; i += TK_THREADS) L.hist2k[i] = 0u;
-    lds_barrier();
-    for (int i = tid; i < G; i += TK_THREADS) {
-      const uint32_t kk = L.gkey[i];
-      if (kk != 0u) atomicAdd(&L.hist2k[(kk - prefix) >> shift], 1u);
-    }
+#pragma unroll
+    for (int j = 0; j < GPT; j++)
+      if (gk[j] != 0u) atomicAdd(&L.hist2k[(gk[j] - prefix) >> shift], 1u);
     lds_barrier();
     // cumulative counts from the top bin down: thread t owns bins 2047-2t, 2046-2t
     const int c0 = (int)L.hist2k[2047 - 2 * tid], c1 = (int)L.hist2k[2046 - 2 * tid];
