@@ -340,6 +340,41 @@ def test_attention_counts_below_cap_duplicates_and_empty():
         assert_attn_close(out, ref)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_attention_scores_rising_far_past_the_first_tile(kv_dtype):
+    # Sixteen sequences split into four slices of two tiles each. In every
+    # sequence one row in a slice's second tile is 120 x head 0's unit query, so
+    # head 0's score there exceeds its first tile's maximum by ~170 in log2
+    # units: the slice's running softmax reference has to move that far and
+    # rescale what it holds. The sparse list holds it at position 266 (slice
+    # 0's second tile), the dense layout at position 300; the other sequences
+    # plant it elsewhere.
+    B, N, Hq = 16, 2000, 64
+    print(f"case rising scores {kv_dtype}", flush=True)
+    g = torch.Generator().manual_seed(91)
+    x = torch.randn(B, N, 512, generator=g)
+    q = synth.make_q(B, Hq, "bf16", g, "cpu")
+    ids = np.stack([np.sort(np.random.default_rng(b).choice(N, 512, replace=False)) for b in range(B)]).astype(np.int32)
+    cnt = np.full(B, 512, np.int32)
+    for b in range(B):
+        unit = q[b, 0].float() / q[b, 0].float().norm()
+        for r in {int(ids[b, 266 - 7 * b]), 300 + 17 * b}:
+            x[b, r] = 120.0 * unit
+    if kv_dtype == "bf16":
+        kv = synth.KVRows("bf16", x.to(torch.bfloat16).contiguous())
+    else:
+        codes, sc = synth.fp8_encode(x[..., :synth.FP8_DIMS])
+        kv = synth.KVRows("fp8", codes, x[..., synth.FP8_DIMS:].to(torch.bfloat16).contiguous(), sc)
+    for sparse in (True, False):
+        a_ids, a_cnt = (dev(torch.from_numpy(ids)), dev(torch.from_numpy(cnt))) if sparse else (None, None)
+        out, lse = lit.sparse_attn_decode(q.cuda(), kv_dev(kv), a_ids, a_cnt, 0, SCALE)
+        torch.cuda.synchronize()
+        ref, rlse = oracle.attend(q, kv, ids if sparse else None, cnt if sparse else None, 0, SCALE)
+        assert np.isfinite(out.cpu().numpy()).all()
+        assert_attn_close(out, ref)
+        np.testing.assert_allclose(lse.double().cpu().numpy(), rlse, atol=2e-3, rtol=0)
+
+
 def test_failed_selection_gives_nan_for_its_sequence_only():
     # count[b] = -1 (the exact selection's failure sign): that sequence's out
     # and lse are NaN, the others match the oracle; on the split path (slices
