@@ -13,7 +13,8 @@
 // the arithmetic off the VALU (fp32 VALU alone would be ~3x slower than HBM).
 //
 // Mapping (v_mfma_f32_16x16x32_bf16, wave64): A = 16 heads x 32 dims of q (staged
-// in LDS once per workgroup, already in operand order), B = 32 dims x 16 entries
+// in LDS once per workgroup, already in operand order, and held in registers
+// when the workgroup scores one query), B = 32 dims x 16 entries
 // of keys loaded straight from HBM into registers (lane l holds entry l%16 and 8
 // consecutive dims), C = 16 heads x 16 entries. The dims are assigned to the 128
 // K positions so that each lane's four 16-byte key loads cover one contiguous
@@ -31,6 +32,7 @@ namespace {
 
 constexpr int CHUNK = LIT_KNORM_CHUNK;  // 256 entries: 4 waves x 64
 constexpr int KEY_RING = 3;             // key register buffers per wave (half-steps of 32 entries)
+constexpr int KEY_RING_1Q = 2;          // the same for one query per workgroup (its q operands take the registers)
 constexpr bool KEY_CONTIG = true;       // whole-line key loads, turned into operands through LDS
 static_assert(CHUNK == 256, "kernel tiling assumes 256-entry chunks");
 
@@ -152,8 +154,12 @@ __device__ __forceinline__ float store_score(float v, int e, int N, int nv, cons
 // A wave works through its 64 entries of each chunk in two half-steps of 32
 // (two column groups); its keys pass through a ring of NB register buffers, so
 // NB - 1 half-steps (NB - 1 times 8 KB per wave) are in flight while one is
-// multiplied (three buffers measured fastest: a fourth adds registers, not
-// bandwidth).
+// multiplied (several queries: three buffers measured fastest, a fourth adds
+// registers, not bandwidth). With one query per workgroup its A operands are
+// read from LDS once into registers instead of once per half-step, which
+// halves the LDS traffic of a half-step; the registers come from the ring,
+// which then holds two buffers (one query: 25.8 against 27.1-27.9 us per
+// 32 x 16384 launch).
 //
 // A workgroup scores QW queries of one sequence (a "unit"): every key operand
 // it loads is multiplied with each query's heads in turn, so a sequence with
@@ -249,6 +255,11 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
   float wr[QW][MT][4];
 #pragma unroll
   for (int qi = 0; qi < QW; qi++) load_lane_weights<MT>(wlds[qi], wr[qi]);
+  u32x4 qreg[QW == 1 ? MT * 4 : 1];  // one query's A operands, held for the whole launch
+  if (QW == 1) {
+#pragma unroll
+    for (int i = 0; i < MT * 4; i++) qreg[i] = qlds[0][i * 64 + lane];
+  }
   int nv[QW];  // entries visible to each query
 #pragma unroll
   for (int qi = 0; qi < QW; qi++) nv[qi] = lengths && qi < nq ? lengths[r0 + qi] : N;
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void idx_score_bf16_kernel(const uint16_t* 
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, qlds[qi][(mt * 4 + j) * 64 + lane]);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, QW == 1 ? qreg[mt * 4 + j] : qlds[qi][(mt * 4 + j) * 64 + lane]);
 #pragma unroll
           for (int G = 0; G < 2; G++)
             acc[G][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, kc[G][j]),
@@ -697,10 +708,11 @@ static void launch_bf16(int S, dim3 grid, hipStream_t st, const lit_idx_in* in, 
   // unit counts that fill the 8 XCDs evenly keep each unit on one XCD
   const int seq_xcd = grid.y % 8 == 0;
   const dim3 g = seq_xcd ? dim3(grid.x * grid.y) : grid;
+  constexpr int NB = QW == 1 ? KEY_RING_1Q : KEY_RING;
   if (S == 4)
-    idx_score_bf16_kernel<MT, 4, KEY_RING, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 4, NB, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
   else
-    idx_score_bf16_kernel<MT, 1, KEY_RING, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
+    idx_score_bf16_kernel<MT, 1, NB, KEY_CONTIG, QW><<<g, 256, 0, st>>>(q, in->w, k, allowed, lengths, in->H, N, Q, nqg, nchunks, scores, hints, hl, seq_xcd);
 }
 
 template <int MT>
