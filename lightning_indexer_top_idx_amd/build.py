@@ -29,6 +29,11 @@ FLAGS = [
     # packed fp32 arithmetic stays off: only scalar fp32 instructions are emitted
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source additions. The attention kernel's output accumulators take the
+# VGPR form of the matrix instructions: with the accumulator registers (AGPRs)
+# the compiler keeps O in VGPRs for the rare rescale and copies all of it to
+# the AGPRs and back on every tile.
+FILE_FLAGS = {"sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 # The host code checked by AddressSanitizer and UndefinedBehaviorSanitizer
@@ -41,7 +46,7 @@ LIB_SANITIZED = os.path.join(BUILD, "liblit_sanitized.so")
 
 def _compile(src: str, sanitize: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + (".san.o" if sanitize else ".o"))
-    cmd = [HIPCC, *FLAGS, *(SANITIZE if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *(SANITIZE if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
