@@ -29,11 +29,12 @@ FLAGS = [
     # packed fp32 arithmetic stays off: only scalar fp32 instructions are emitted
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# Per-source additions. The attention kernel's output accumulators take the
-# VGPR form of the matrix instructions: with the accumulator registers (AGPRs)
-# the compiler keeps O in VGPRs for the rare rescale and copies all of it to
-# the AGPRs and back on every tile.
-FILE_FLAGS = {"sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source additions. The attention and fp64 logits kernels take the VGPR
+# form of the matrix instructions: with the accumulation registers (AGPRs) the
+# compiler keeps their accumulators in VGPRs between uses and copies them to
+# the AGPRs and back around every batch of matrix instructions.
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+FILE_FLAGS = {"sparse_attn.hip": VGPR_MFMA, "golden.hip": VGPR_MFMA}
 
 
 # The host code checked by AddressSanitizer and UndefinedBehaviorSanitizer
