@@ -224,7 +224,7 @@ def test_topk_on_given_scores_with_heavy_ties():
 
 def test_topk_with_hints_on_fp32_order():
     # without `exact` the fp32 scores define the order; the hinted path must agree
-    for B, N, k in ((2, 16384, 512), (1, 5000, 4000), (1, 125000, 1024)):
+    for B, N, k in ((2, 16384, 512), (1, 5000, 4000), (1, 125000, 1024), (4, 125000, 512)):
         inp = W.layer_inputs(W.CTX64K, 3, "cpu", B=B, N=N).idx
         q, w, kk = dev(inp.q_idx), dev(inp.w), dev(inp.k_idx)
         scores, hints = lit.idx_score(q, w, kk)
@@ -238,8 +238,9 @@ def test_topk_with_hints_of_other_scores_falls_back():
     # hints computed for other scores: their group maxima may lie below or above
     # these scores' own; the selection detects that (a key above the hinted
     # largest, or fewer than k entries above the hinted bound) and takes the
-    # full scan, so the result is still the exact top-k of the scores given
-    for N, k in ((16384, 512), (4000, 256)):
+    # full scan, so the result is still the exact top-k of the scores given;
+    # above 16384 entries the two-kernel path's checks send it there
+    for N, k in ((16384, 512), (4000, 256), (40000, 512)):
         a = W.layer_inputs(W.CTX64K, 1, "cpu", B=2, N=N).idx
         o = W.layer_inputs(W.CTX64K, 2, "cpu", B=2, N=N).idx
         scores, _ = lit.idx_score(dev(a.q_idx), dev(a.w), dev(a.k_idx))
